@@ -1,0 +1,56 @@
+"""MXFP8 (E4M3 elements, E8M0 scale per 32) quantisation, mirrored for the
+prefill path (test infrastructure).
+
+Written from the OCP Microscaling Formats (MX) v1.0 conversion rule: for each
+block of 32 consecutive values, shared exponent X = floor(log2(max|V|)) - 8
+(8 = exponent of E4M3's largest normal, 448 = 1.75 * 2^8), clamped to the
+E8M0 range; each element is V / 2^X rounded to the nearest E4M3 value (ties to
+the even code), magnitudes beyond 448 saturate to 448.  A block of zeros gets
+the smallest scale.  The element rounding here searches the full table of
+E4M3 values instead of manipulating bits.
+"""
+import numpy as np
+
+from .formats import e4m3_to_f64
+
+# all finite non-negative E4M3 values, in code order (codes 0x00..0x7E)
+_E4M3_POS = e4m3_to_f64(np.arange(0x7F))
+_E4M3_MIDS = 0.5 * (_E4M3_POS[:-1] + _E4M3_POS[1:])
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 value (ties to even code), saturating at +-448; returns fp64."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    lo = np.searchsorted(_E4M3_MIDS, a, side="left")
+    hi = np.searchsorted(_E4M3_MIDS, a, side="right")
+    code = np.where(lo != hi, lo + (lo & 1), lo)      # tie -> even of (lo, lo+1)
+    code = np.minimum(code, 0x7E)
+    return np.copysign(_E4M3_POS[code], v)
+
+
+def mx_scale_exponent(block: np.ndarray) -> int:
+    amax = float(np.max(np.abs(block)))
+    if amax == 0.0:
+        return -127
+    m, e = np.frexp(amax)           # amax = m * 2^e, m in [0.5, 1)
+    return int(np.clip((e - 1) - 8, -127, 127))
+
+
+def mxfp8_quantize(v: np.ndarray) -> np.ndarray:
+    """Quantise a 1-D vector (length a multiple of 32) block by block and return
+    the dequantised fp64 values."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    for b in range(0, v.size, 32):
+        blk = v[b: b + 32]
+        X = mx_scale_exponent(blk)
+        out[b: b + 32] = e4m3_round(blk / np.ldexp(1.0, X)) * np.ldexp(1.0, X)
+    return out
+
+
+def mxfp8_quantize_f32(v: np.ndarray) -> np.ndarray:
+    """As mxfp8_quantize, applied to the fp32-rounded values: the kernels hold
+    h in fp32 when they quantise it, so the oracle takes the same decision on
+    the same precision."""
+    return mxfp8_quantize(np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64))

@@ -17,6 +17,11 @@ from .formats import bf16_bits_to_f64, e2m1_to_f64, e4m3_to_f64, e8m0_to_f64, un
 
 F32, BF16, MXFP4, NVFP4 = 0, 1, 2, 3
 
+# per-code values from the format decoders, looked up per element
+_E2M1 = e2m1_to_f64(np.arange(16))
+_E8M0 = e8m0_to_f64(np.arange(256))
+_E4M3 = e4m3_to_f64(np.arange(256))
+
 
 def _shapes(H, I):
     return ((I, H), (I, H), (H, I))
@@ -57,10 +62,10 @@ def decode_record(rec: np.ndarray, H: int, I: int, w_dtype: int):
         n = r * c
         codes = unpack_nibbles(rec[code_off[i]: code_off[i] + n // 2], n).reshape(r, c // blk, blk)
         sc = rec[scale_off[i]: scale_off[i] + n // blk].reshape(r, c // blk)
-        vals = e2m1_to_f64(codes)
+        vals = _E2M1[codes]
         if w_dtype == MXFP4:
-            s = e8m0_to_f64(sc)
+            s = _E8M0[sc]
         else:
-            s = e4m3_to_f64(sc) * tscale[i]
+            s = _E4M3[sc] * tscale[i]
         mats.append((vals * s[..., None]).reshape(r, c))
     return tuple(mats)

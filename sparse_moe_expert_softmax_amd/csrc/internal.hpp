@@ -1,0 +1,46 @@
+// Internal launchers shared by the C-ABI layer (api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ft_moe.h"
+
+namespace ft {
+
+// router
+hipError_t launch_route(const ft_moe_desc& d, const void* x, int T, const void* wr, const float* sel_bias,
+                        int32_t* ids, float* gates, double* logits, hipStream_t st);
+
+// slot table
+size_t slot_table_bytes(int L, int E, int S);
+hipError_t launch_slot_table_init(void* table, int L, int E, int S, hipStream_t st);
+hipError_t launch_slot_lookup(void* table, int layer, const int32_t* ids, int n_pairs, int32_t* slot_ids,
+                              uint8_t* miss_flags, int32_t* miss_list, int32_t* n_miss, hipStream_t st);
+int slot_max_slots();
+int slot_max_experts();
+
+// forward workspace: every region 256-byte aligned
+struct FwdPlan {
+  int T, P, E, H, I, nb;       // tokens, pairs, experts, hidden, inter, permute blocks
+  bool mfma;                   // large-batch MXFP4 path on scaled MFMA
+  size_t off_hist, off_offsets, off_active, off_perm, off_pos, off_h, off_y, off_xq, off_xs, off_hs;
+  size_t bytes;
+};
+FwdPlan plan_forward(const ft_moe_desc& d, int T);
+
+// permutation (grouping pairs by expert, stable in pair order)
+hipError_t launch_permute(const FwdPlan& pl, const int32_t* ids, const uint32_t* mask, char* ws,
+                          hipStream_t st);
+
+// decode-sized grouped GEMV: gate/up + SwiGLU, then down, then combine
+hipError_t launch_gemv_forward(const ft_moe_desc& d, const FwdPlan& pl, const void* x, const int32_t* slot_ids,
+                               const void* pool, const float* gates, float* out, char* ws, hipStream_t st);
+
+// large-batch MXFP4 path on gfx950 scaled MFMA
+hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const void* x, const int32_t* slot_ids,
+                               const void* pool, const float* gates, float* out, char* ws, hipStream_t st);
+
+constexpr int PERM_CHUNK = 4096;  // pairs per permute block
+
+}  // namespace ft

@@ -1,0 +1,214 @@
+// Global LRU expert-slot table, resident in HBM and updated on the device.
+//
+// The pages keep every expert in host memory and use free device memory as
+// one least-recently-used expert cache shared by all MoE layers (FreeToken
+// explainer page, "how" section; LRU per its glossary: at capacity the entry
+// unreferenced for longest goes).  Key = (layer, expert).  One lookup call
+// takes the ids one layer selected for a batch:
+//   distinct ids ascending; hits stamped with the new tick; if the misses
+//   outnumber the slots this call did not stamp -> no change, FT_EPOOL;
+//   else the i-th miss (ascending id) takes the i-th slot in (last_use asc,
+//   slot asc) order among the unstamped slots, evicting its key.
+// One workgroup does the whole call: the state is small
+// and the call is a strict sequence of dependent steps.  Limits: S <= 8192
+// slots, E <= 4096 experts per layer, <= 1024 ids per call.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace ft {
+
+constexpr int SLOT_THREADS = 1024;
+constexpr int SLOT_MAX_S = 8192;
+constexpr int SLOT_MAX_E = 4096;
+
+struct TableView {
+  uint32_t* tick;
+  int32_t* status;
+  int32_t* key_slot;   // [L*E]
+  int32_t* slot_key;   // [S]
+  uint32_t* last_use;  // [S]
+  int L, E, S;
+};
+
+__host__ __device__ inline TableView table_view(void* base) {
+  int32_t* h = reinterpret_cast<int32_t*>(base);
+  TableView v;
+  v.tick = reinterpret_cast<uint32_t*>(h);
+  v.status = h + 1;
+  v.L = h[2];
+  v.E = h[3];
+  v.S = h[4];
+  int32_t* p = h + 16;  // 64-byte header
+  v.key_slot = p;
+  v.slot_key = p + (int64_t)v.L * v.E;
+  v.last_use = reinterpret_cast<uint32_t*>(v.slot_key + v.S);
+  return v;
+}
+
+size_t slot_table_bytes(int L, int E, int S) {
+  return 64 + sizeof(int32_t) * ((size_t)L * E + S) + sizeof(uint32_t) * (size_t)S;
+}
+
+__global__ void slot_table_init_kernel(int32_t* base, int L, int E, int S) {
+  const int64_t n_keys = (int64_t)L * E;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid == 0) {
+    base[0] = 0;  // tick
+    base[1] = FT_OK;
+    base[2] = L;
+    base[3] = E;
+    base[4] = S;
+    for (int i = 5; i < 16; ++i) base[i] = 0;
+  }
+  int32_t* key_slot = base + 16;
+  int32_t* slot_key = key_slot + n_keys;
+  uint32_t* last_use = reinterpret_cast<uint32_t*>(slot_key + S);
+  for (int64_t i = tid; i < n_keys; i += (int64_t)gridDim.x * blockDim.x) key_slot[i] = -1;
+  for (int64_t i = tid; i < S; i += (int64_t)gridDim.x * blockDim.x) {
+    slot_key[i] = -1;
+    last_use[i] = 0u;
+  }
+}
+
+hipError_t launch_slot_table_init(void* table, int L, int E, int S, hipStream_t st) {
+  const int64_t n = (int64_t)L * E + S;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  slot_table_init_kernel<<<blocks, 256, 0, st>>>(reinterpret_cast<int32_t*>(table), L, E, S);
+  return hipGetLastError();
+}
+
+// 64-bit victim key: (last_use, slot); ~0 = not eligible.
+__device__ __forceinline__ uint64_t vkey(uint32_t lu, int s) { return ((uint64_t)lu << 32) | (uint32_t)s; }
+
+__global__ void __launch_bounds__(SLOT_THREADS) slot_lookup_kernel(
+    void* table, int layer, const int32_t* __restrict__ ids, int n_pairs, int32_t* __restrict__ slot_ids,
+    uint8_t* __restrict__ miss_flags, int32_t* __restrict__ miss_list, int32_t* __restrict__ n_miss_out) {
+  __shared__ uint32_t lu_s[SLOT_MAX_S];          // last_use copy
+  __shared__ uint8_t present[SLOT_MAX_E];        // per expert of this layer: 1 if selected
+  __shared__ uint8_t umiss[SLOT_MAX_E];          // 1 if missed
+  __shared__ int32_t uslot[SLOT_MAX_E];          // slot after the call (for selected experts)
+  __shared__ int32_t ulist[SLOT_THREADS];        // distinct ids ascending
+  __shared__ int32_t n_u, n_hit, n_mis;
+  __shared__ uint64_t wave_best[SLOT_THREADS / 64];
+  __shared__ int32_t victims[SLOT_THREADS];
+
+  TableView tv = table_view(table);
+  const int tid = threadIdx.x;
+  const int E = tv.E, S = tv.S;
+  if (layer >= tv.L || S > SLOT_MAX_S || E > SLOT_MAX_E) {  // bad call: report, touch nothing
+    if (tid == 0) { *tv.status = FT_EINVAL; *n_miss_out = -1; }
+    for (int p = tid; p < n_pairs; p += SLOT_THREADS) { slot_ids[p] = -1; miss_flags[p] = 0; }
+    return;
+  }
+  const int32_t* ks_layer = tv.key_slot + (int64_t)layer * E;
+
+  for (int e = tid; e < E; e += SLOT_THREADS) { present[e] = 0; umiss[e] = 0; }
+  if (tid == 0) { n_u = 0; n_hit = 0; n_mis = 0; }
+  __syncthreads();
+  for (int p = tid; p < n_pairs; p += SLOT_THREADS) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) present[e] = 1;
+  }
+  __syncthreads();
+  // distinct ids in ascending order (serial compaction by one wave is plenty
+  // for E <= 4096; done by thread 0 to keep the order trivially right)
+  if (tid == 0) {
+    int n = 0, h = 0;
+    for (int e = 0; e < E; ++e) {
+      if (present[e]) {
+        ulist[n++] = e;
+        if (ks_layer[e] >= 0) ++h;
+      }
+    }
+    n_u = n;
+    n_hit = h;
+    n_mis = n - h;
+  }
+  __syncthreads();
+  const int nu = n_u, nm = n_mis, nh = n_hit;
+  if (nm > S - nh) {  // exhaustion: report, change nothing
+    if (tid == 0) { *tv.status = FT_EPOOL; *n_miss_out = -1; }
+    for (int p = tid; p < n_pairs; p += SLOT_THREADS) { slot_ids[p] = -1; miss_flags[p] = 0; }
+    return;
+  }
+  const uint32_t tick = *tv.tick + 1u;
+  for (int s = tid; s < S; s += SLOT_THREADS) lu_s[s] = tv.last_use[s];
+  __syncthreads();
+  // stamp hits (in the LDS copy and in the table)
+  for (int i = tid; i < nu; i += SLOT_THREADS) {
+    const int e = ulist[i];
+    const int s = ks_layer[e];
+    if (s >= 0) { tv.last_use[s] = tick; lu_s[s] = tick; uslot[e] = s; }
+  }
+  __syncthreads();
+  // pick nm victims, smallest (last_use, slot) among slots with last_use < tick
+  const int lane = tid & 63, wv = tid >> 6;
+  for (int r = 0; r < nm; ++r) {
+    uint64_t best = ~0ull;
+    for (int s = tid; s < S; s += SLOT_THREADS) {
+      const uint32_t lu = lu_s[s];
+      if (lu < tick) {
+        const uint64_t kk = vkey(lu, s);
+        best = kk < best ? kk : best;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t ob = __shfl_xor(best, o, 64);
+      best = ob < best ? ob : best;
+    }
+    if (lane == 0) wave_best[wv] = best;
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t b = ~0ull;
+      for (int w = 0; w < SLOT_THREADS / 64; ++w) b = wave_best[w] < b ? wave_best[w] : b;
+      const int s = (int)(uint32_t)(b & 0xFFFFFFFFu);
+      victims[r] = s;
+      lu_s[s] = tick;  // now stamped by this call
+    }
+    __syncthreads();
+  }
+  // assign misses (ascending id) to victims in order; sequential by thread 0
+  // because an eviction may clear a key of this same layer
+  if (tid == 0) {
+    int r = 0;
+    for (int i = 0; i < nu; ++i) {
+      const int e = ulist[i];
+      if (ks_layer[e] >= 0) continue;
+      const int s = victims[r];
+      const int old = tv.slot_key[s];
+      if (old >= 0) tv.key_slot[old] = -1;
+      tv.slot_key[s] = layer * E + e;
+      tv.key_slot[(int64_t)layer * E + e] = s;
+      tv.last_use[s] = tick;
+      uslot[e] = s;
+      umiss[e] = 1;
+      miss_list[2 * r] = e;
+      miss_list[2 * r + 1] = s;
+      ++r;
+    }
+    *tv.tick = tick;
+    *tv.status = FT_OK;
+    *n_miss_out = nm;
+  }
+  __syncthreads();
+  for (int p = tid; p < n_pairs; p += SLOT_THREADS) {
+    const int e = ids[p];
+    const bool ok = e >= 0 && e < E;
+    slot_ids[p] = ok ? uslot[e] : -1;
+    miss_flags[p] = ok ? umiss[e] : (uint8_t)0;
+  }
+}
+
+hipError_t launch_slot_lookup(void* table, int layer, const int32_t* ids, int n_pairs, int32_t* slot_ids,
+                              uint8_t* miss_flags, int32_t* miss_list, int32_t* n_miss, hipStream_t st) {
+  slot_lookup_kernel<<<1, SLOT_THREADS, 0, st>>>(table, layer, ids, n_pairs, slot_ids, miss_flags, miss_list,
+                                                 n_miss);
+  return hipGetLastError();
+}
+
+int slot_max_slots() { return SLOT_MAX_S; }
+int slot_max_experts() { return SLOT_MAX_E; }
+
+}  // namespace ft

@@ -1,0 +1,143 @@
+"""Thin ctypes binding of ``libftmoe.so`` (declared in ``include/ft_moe.h``).
+
+Argument marshalling only: the functions take torch tensors (device memory,
+pinned host memory) and torch streams, pass raw pointers to the C ABI and
+raise on a non-OK status.  Every step of the layer runs in the HIP library;
+there is no fallback.  The names follow the C entry points.
+"""
+import ctypes
+import os
+
+import torch
+
+from .configs import MoEConfig
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libftmoe.so")
+
+FT_OK, FT_EINVAL, FT_EUNSUPPORTED, FT_EPOOL, FT_EHIP, FT_EWORKSPACE = 0, -1, -2, -3, -4, -5
+STATUS_NAMES = {0: "FT_OK", -1: "FT_EINVAL", -2: "FT_EUNSUPPORTED", -3: "FT_EPOOL", -4: "FT_EHIP",
+                -5: "FT_EWORKSPACE"}
+
+
+class FtError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+                ("router_dtype", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("expert_stride", ctypes.c_int64)]
+
+
+_lib = None
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "ft_record_bytes": (_sz, [_i32, _i32, _i32]),
+    "ft_route_workspace_bytes": (_sz, [ctypes.POINTER(Desc), _i32]),
+    "ft_moe_route": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ft_slot_table_bytes": (_sz, [_i32, _i32, _i32]),
+    "ft_slot_table_init": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp]),
+    "ft_slot_lookup": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "ft_expert_upload": (ctypes.c_int, [_vp, _i64, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_vp), _i32, _vp, _vp]),
+    "ft_moe_workspace_bytes": (_sz, [ctypes.POINTER(Desc), _i32]),
+    "ft_moe_forward": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ft_last_error": (ctypes.c_char_p, []),
+}
+EXPORTED = tuple(_SIGS)
+
+
+def lib():
+    """Load the built library; raise if it is missing (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_moe_expert_softmax_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != FT_OK:
+        raise FtError(rc, lib().ft_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_desc(cfg: MoEConfig, expert_stride: int = None) -> Desc:
+    from .synth import record_stride
+    stride = record_stride(cfg.hidden, cfg.inter, cfg.w_dtype) if expert_stride is None else expert_stride
+    return Desc(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.act_dtype, cfg.w_dtype, cfg.router_dtype,
+                1 if cfg.renormalize else 0, stride)
+
+
+def ft_record_bytes(hidden: int, inter: int, w_dtype: int) -> int:
+    return int(lib().ft_record_bytes(hidden, inter, w_dtype))
+
+
+def ft_route_workspace_bytes(desc: Desc, n_tokens: int) -> int:
+    return int(lib().ft_route_workspace_bytes(ctypes.byref(desc), n_tokens))
+
+
+def ft_moe_route(desc: Desc, x, w_router, topk_ids, topk_gates, sel_bias=None, logits=None, workspace=None,
+                 stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ft_moe_route(ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(w_router), _ptr(sel_bias),
+                              _ptr(topk_ids), _ptr(topk_gates), _ptr(logits), _ptr(workspace), ws_bytes,
+                              _stream(stream)))
+
+
+def ft_slot_table_bytes(n_layers: int, n_experts: int, n_slots: int) -> int:
+    return int(lib().ft_slot_table_bytes(n_layers, n_experts, n_slots))
+
+
+def ft_slot_table_init(table, n_layers: int, n_experts: int, n_slots: int, stream=None):
+    _check(lib().ft_slot_table_init(_ptr(table), n_layers, n_experts, n_slots, _stream(stream)))
+
+
+def ft_slot_lookup(table, layer: int, topk_ids, slot_ids, miss_flags, miss_list, n_miss, stream=None):
+    _check(lib().ft_slot_lookup(_ptr(table), layer, _ptr(topk_ids), topk_ids.numel(), _ptr(slot_ids),
+                                _ptr(miss_flags), _ptr(miss_list), _ptr(n_miss), _stream(stream)))
+
+
+def ft_expert_upload(pool, expert_stride: int, record_bytes: int, slots, host_ptrs, stream=None, done_event=None):
+    """slots: list of ints; host_ptrs: list of integer host addresses (pinned)."""
+    n = len(slots)
+    arr_s = (_i32 * max(n, 1))(*slots)
+    arr_p = (_vp * max(n, 1))(*host_ptrs)
+    ev = None if done_event is None else ctypes.c_void_p(done_event.cuda_event)
+    _check(lib().ft_expert_upload(_ptr(pool), expert_stride, record_bytes, arr_s, arr_p, n, _stream(stream), ev))
+
+
+def ft_moe_workspace_bytes(desc: Desc, n_tokens: int) -> int:
+    return int(lib().ft_moe_workspace_bytes(ctypes.byref(desc), n_tokens))
+
+
+def ft_moe_forward(desc: Desc, x, topk_ids, topk_gates, pool, out, workspace, slot_ids=None, expert_mask=None,
+                   stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().ft_moe_forward(ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(topk_ids), _ptr(topk_gates),
+                                _ptr(slot_ids), _ptr(pool), _ptr(expert_mask), _ptr(out), _ptr(workspace),
+                                ws_bytes, _stream(stream)))
+
+
+def ft_last_error() -> str:
+    return lib().ft_last_error().decode()

@@ -39,17 +39,20 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return ((b + rounding) >> 16).astype(np.uint16)
 
 
-_E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
-
-
 def _e2m1_encode_mag(m: np.ndarray) -> np.ndarray:
     """Magnitude (already divided by the block scale) -> 3-bit E2M1 magnitude code,
-    nearest with ties to the even code, saturating at 6."""
-    lo = np.searchsorted(_E2M1_MIDS, m, side="left")
-    hi = np.searchsorted(_E2M1_MIDS, m, side="right")
-    tie = lo != hi
-    code = np.where(tie, lo + (lo & 1), lo)  # at a tie pick the even one of (lo, lo+1)
-    return code.astype(np.uint8)
+    nearest with ties to the even code, saturating at 6.  The midpoints between
+    neighbouring values are 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; a value exactly
+    on a midpoint goes to the even code, hence the alternating > / >=."""
+    m = np.asarray(m, dtype=np.float32)
+    code = (m > 0.25).astype(np.uint8)
+    code += m >= 0.75
+    code += m > 1.25
+    code += m >= 1.75
+    code += m > 2.5
+    code += m >= 3.5
+    code += m > 5.0
+    return code
 
 
 def e2m1_encode(v: np.ndarray) -> np.ndarray:
@@ -86,12 +89,12 @@ def mxfp4_encode_matrix(w: np.ndarray):
     """[rows, K] fp32 -> (codes [rows, K/2] u8, scales [rows, K/32] u8 E8M0),
     shared exponent floor(log2(amax)) - 2 per 32-element block along K."""
     rows, K = w.shape
-    blk = w.reshape(rows, K // 32, 32).astype(np.float64)
-    amax = np.abs(blk).max(axis=2)
+    blk = np.asarray(w, dtype=np.float32).reshape(rows, K // 32, 32)
+    amax = np.abs(blk).max(axis=2).astype(np.float64)
     _, e = np.frexp(np.where(amax > 0, amax, 1.0))
     X = np.where(amax > 0, (e - 1) - 2, -127)
     X = np.clip(X, -127, 127)
-    q = blk / np.ldexp(1.0, X)[..., None]
+    q = blk * np.ldexp(1.0, -X).astype(np.float32)[..., None]   # exact: power-of-two scaling
     codes = e2m1_encode(q).reshape(rows, K)
     return _pack_nibbles(codes), (X + 127).astype(np.uint8)
 
@@ -99,17 +102,17 @@ def mxfp4_encode_matrix(w: np.ndarray):
 def nvfp4_encode_matrix(w: np.ndarray):
     """[rows, K] fp32 -> (codes [rows, K/2], E4M3 block scales [rows, K/16], fp32 tensor scale)."""
     rows, K = w.shape
-    w64 = w.astype(np.float64)
-    amax_t = float(np.abs(w64).max())
+    w32 = np.asarray(w, dtype=np.float32)
+    amax_t = float(np.abs(w32).max())
     ts = np.float32(amax_t / (6.0 * 448.0)) if amax_t > 0 else np.float32(1.0)
-    blk = w64.reshape(rows, K // 16, 16)
-    amax_b = np.abs(blk).max(axis=2)
+    blk = w32.reshape(rows, K // 16, 16)
+    amax_b = np.abs(blk).max(axis=2).astype(np.float64)
     sc = e4m3_encode(amax_b / 6.0 / float(ts))
     # decoded block-scale values are needed to place elements; E4M3 decoding here is
     # part of encoding (choosing codes), not of reading the record back
-    sc_val = _e4m3_value_for_encoding(sc) * float(ts)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        q = np.where(sc_val[..., None] > 0, blk / sc_val[..., None], 0.0)
+    sc_val = (_e4m3_value_for_encoding(sc) * float(ts)).astype(np.float32)
+    inv = np.where(sc_val > 0, 1.0 / np.where(sc_val > 0, sc_val, 1.0), 0.0).astype(np.float32)
+    q = blk * inv[..., None]
     codes = e2m1_encode(q).reshape(rows, K)
     return _pack_nibbles(codes), sc, ts
 

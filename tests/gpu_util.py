@@ -1,0 +1,97 @@
+"""Helpers shared by the GPU parity tests: build device inputs from the seeded
+generator, run the C-ABI path, run the oracle on the same bytes, compare."""
+import numpy as np
+import torch
+
+from oracle.moe import moe_layer, route, to_f64
+from oracle.record import decode_record
+from sparse_moe_expert_softmax_amd import ftmoe, synth
+from sparse_moe_expert_softmax_amd.configs import MoEConfig
+
+POISON = 0xFF  # bytes of never-selected records: NaN in bf16/f32, NaN scale in MXFP4/NVFP4
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).cuda()
+
+
+def max_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / max |ref| over the tensor."""
+    den = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(got - ref))) / (den if den > 0 else 1.0)
+
+
+class LayerData:
+    """One layer's inputs for a config: router, activations, and a lazily
+    filled expert pool (only the experts that are needed get real records;
+    the rest are poison bytes that turn any stray read into NaNs)."""
+
+    def __init__(self, cfg: MoEConfig, layer: int, step: int, T: int, x=None, wr=None):
+        self.cfg, self.layer, self.T = cfg, layer, T
+        self.x = synth.activations(cfg, step, layer, T) if x is None else x
+        self.wr = synth.router_weights(cfg, layer) if wr is None else wr
+        self.stride = synth.record_stride(cfg.hidden, cfg.inter, cfg.w_dtype)
+        self.desc = ftmoe.make_desc(cfg, self.stride)
+        self._records = {}
+        self.pool = None
+
+    def record(self, e: int) -> np.ndarray:
+        if e not in self._records:
+            self._records[e] = synth.expert_record(self.cfg, self.layer, e)
+        return self._records[e]
+
+    def experts_f64(self, e: int):
+        return decode_record(self.record(e), self.cfg.hidden, self.cfg.inter, self.cfg.w_dtype)
+
+    def build_pool(self, experts) -> torch.Tensor:
+        """Device pool [E, stride] u8 with real records for `experts`, poison elsewhere."""
+        if self.pool is None:
+            self.pool = torch.full((self.cfg.n_experts, self.stride), POISON, dtype=torch.uint8, device="cuda")
+        for e in sorted(set(int(v) for v in experts)):
+            self.pool[e].copy_(torch.from_numpy(self.record(e)))
+        return self.pool
+
+    # ---------------------------------------------------------- GPU side --
+    def gpu_route(self, bias=None):
+        cfg, T = self.cfg, self.T
+        x, wr = dev(self.x), dev(self.wr)
+        ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+        gates = torch.empty((T, cfg.top_k), dtype=torch.float32, device="cuda")
+        logits = torch.empty((T, cfg.n_experts), dtype=torch.float64, device="cuda")
+        b = None if bias is None else dev(bias.astype(np.float32))
+        ftmoe.ft_moe_route(self.desc, x, wr, ids, gates, sel_bias=b, logits=logits)
+        return ids, gates, logits
+
+    def gpu_forward(self, ids, gates, mask=None, slot_ids=None, pool=None):
+        cfg, T = self.cfg, self.T
+        x = dev(self.x)
+        out = torch.full((T, cfg.hidden), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(ftmoe.ft_moe_workspace_bytes(self.desc, T), 256), dtype=torch.uint8, device="cuda")
+        m = None if mask is None else dev(np.asarray(mask, dtype=np.uint32))
+        ftmoe.ft_moe_forward(self.desc, x, ids, gates, self.pool if pool is None else pool, out, ws,
+                             slot_ids=slot_ids, expert_mask=m)
+        return out
+
+    # ------------------------------------------------------- oracle side --
+    def oracle_route(self, bias=None):
+        x64 = to_f64(self.x, self.cfg.act_dtype)
+        w64 = to_f64(self.wr, self.cfg.router_dtype)
+        return route(x64, w64, self.cfg.top_k, bias=bias, renormalize=self.cfg.renormalize)
+
+    def oracle_layer(self, mask=None, bias=None, tokens=None, x_quant=None, h_quant=None):
+        x64 = to_f64(self.x, self.cfg.act_dtype)
+        w64 = to_f64(self.wr, self.cfg.router_dtype)
+        cache = {}
+
+        def expert(e):
+            if e not in cache:
+                cache[e] = self.experts_f64(e)
+            return cache[e]
+
+        return moe_layer(x64, w64, expert, self.cfg.top_k, bias=bias, mask=mask,
+                         renormalize=self.cfg.renormalize, tokens=tokens, x_quant=x_quant, h_quant=h_quant)

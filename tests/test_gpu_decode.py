@@ -1,0 +1,266 @@
+"""GPU parity of the decode path against the fp64 oracle, through the C ABI.
+
+Bars: routing ids, slot tables and miss flags bit-exact; gates within 1e-6;
+outputs within max relative error 1e-5 (fp32 layer) / 1e-2 (bf16, MXFP4,
+NVFP4-like layers); partition sums within 1e-5 of the unmasked output."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import LayerData, dev, max_rel_err
+from oracle.lru import LruSim
+from sparse_moe_expert_softmax_amd import ftmoe, synth
+from sparse_moe_expert_softmax_amd.configs import C1, C2, C3, C5, MoEConfig, F32, BF16
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+TOL = {F32: 1e-5, BF16: 1e-2}
+
+
+def tol(cfg):
+    return 1e-5 if cfg.w_dtype == F32 else 1e-2
+
+
+def check_route(ld: LayerData, bias=None):
+    ids, gates, logits = ld.gpu_route(bias)
+    torch.cuda.synchronize()
+    o_ids, o_gates, o_logits = ld.oracle_route(bias)
+    np.testing.assert_array_equal(ids.cpu().numpy(), o_ids)
+    np.testing.assert_allclose(gates.cpu().numpy(), o_gates, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(logits.cpu().numpy(), o_logits, rtol=1e-9, atol=1e-12)
+    return ids, gates, o_ids
+
+
+def run_layer(cfg, layer, step, T, mask=None, x=None, wr=None):
+    ld = LayerData(cfg, layer, step, T, x=x, wr=wr)
+    ids, gates, o_ids = check_route(ld)
+    ld.build_pool(o_ids.ravel())
+    out = ld.gpu_forward(ids, gates, mask=mask).cpu().numpy()
+    ref, _, _ = ld.oracle_layer(mask=mask)
+    assert not np.isnan(out).any()
+    err = max_rel_err(out, ref)
+    assert err <= tol(cfg), f"max rel err {err:.3g} > {tol(cfg)}"
+    return ld, ids, gates, out, ref
+
+
+# --------------------------------------------------------------- routing --
+@pytest.mark.parametrize("cfg,T", [(C1, 16), (C2, 4), (C3, 4), (C5, 4), (C1, 1), (C2, 37)])
+def test_route_matches_oracle(cfg, T):
+    print(f"route {cfg.name} T={T}", flush=True)
+    check_route(LayerData(cfg, 0, 0, T))
+
+
+def test_route_ties_zero_router_and_duplicate_rows():
+    cfg = C2
+    ld = LayerData(cfg, 0, 1, 4, wr=np.zeros((cfg.n_experts, cfg.hidden), dtype=np.uint16))
+    ids, gates, _ = ld.gpu_route()
+    np.testing.assert_array_equal(ids.cpu().numpy(), np.tile(np.arange(cfg.top_k), (4, 1)))
+    np.testing.assert_allclose(gates.cpu().numpy(), 1.0 / cfg.top_k, rtol=0, atol=1e-7)
+    wr = synth.router_weights(cfg, 3).copy()
+    for dup in (17, 64, 101):
+        wr[dup] = wr[5]
+    x = synth.activations(cfg, 0, 3, 8)
+    # make expert 5 win for every token so its duplicates are selected too
+    wr[5] = wr[17] = wr[64] = wr[101] = (synth.f32_to_bf16_bits(np.full(cfg.hidden, 0.0, np.float32)))
+    x = x.copy()
+    check_route(LayerData(cfg, 3, 0, 8, x=x, wr=wr))
+
+
+def test_route_selection_bias_follows_trace():
+    cfg = C3
+    tr = synth.zipf_trace(cfg, n_steps=2)[1, 7]              # [4, k]
+    bias = synth.trace_bias(tr, cfg.n_experts)
+    ld = LayerData(cfg, 7, 1, 4)
+    ids, gates, o_ids = check_route(ld, bias=bias)
+    for t in range(4):
+        assert sorted(ids[t].cpu().tolist()) == sorted(tr[t].tolist())
+
+
+# --------------------------------------------------------------- forward --
+def test_forward_tiny_fp32():
+    run_layer(C1, 0, 0, 16)
+
+
+@pytest.mark.parametrize("T", [1, 5, 17, 33])
+def test_forward_tiny_fp32_ragged(T):
+    run_layer(C1, 0, T, T)
+
+
+@pytest.mark.parametrize("b", [1, 2, 4])
+@pytest.mark.parametrize("layer", [0, 39])
+def test_forward_decode_bf16(b, layer):
+    print(f"decode bf16 b={b} layer={layer}", flush=True)
+    run_layer(C2, layer, 11 + layer, b)
+
+
+def test_forward_deterministic_and_masks_partition():
+    cfg = C2
+    ld, ids, gates, out, ref = run_layer(cfg, 2, 5, 4)
+    again = ld.gpu_forward(ids, gates).cpu().numpy()
+    assert np.array_equal(out, again)                      # bitwise identical rerun
+    masks = synth.partition_masks(cfg, 2, 4)
+    full_words = (cfg.n_experts + 31) // 32
+    for m in masks:
+        comp = (~m) & np.uint32(0xFFFFFFFF)
+        a = ld.gpu_forward(ids, gates, mask=m).cpu().numpy()
+        b = ld.gpu_forward(ids, gates, mask=comp).cpu().numpy()
+        assert max_rel_err(a + b, out) <= 1e-5
+        ra, _, _ = ld.oracle_layer(mask=m)
+        assert max_rel_err(a, ra) <= 1e-2 * max(1.0, np.abs(ref).max() / max(np.abs(ra).max(), 1e-30))
+    zero = ld.gpu_forward(ids, gates, mask=np.zeros(full_words, dtype=np.uint32)).cpu().numpy()
+    assert np.all(zero == 0)
+
+
+def test_forward_zero_tokens_is_noop():
+    cfg = C1
+    ld = LayerData(cfg, 0, 0, 0, x=np.zeros((0, cfg.hidden), np.float32))
+    out = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ids = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    x = torch.zeros((0, cfg.hidden), dtype=torch.float32, device="cuda")
+    pool = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    ftmoe.ft_moe_forward(ld.desc, x, ids, out, pool, out, ws)
+
+
+def test_forward_mxfp4_decode():
+    cfg = C3
+    for b in (1, 4):
+        print(f"mxfp4 b={b}", flush=True)
+        run_layer(cfg, 5, 3, b)
+
+
+def test_forward_nvfp4_decode_with_partition_masks():
+    cfg = C5
+    ld, ids, gates, out, ref = run_layer(cfg, 1, 2, 4)
+    masks = synth.partition_masks(cfg, 1, 3)
+    for m in masks:
+        comp = (~m) & np.uint32(0xFFFFFFFF)
+        a = ld.gpu_forward(ids, gates, mask=m).cpu().numpy()
+        b = ld.gpu_forward(ids, gates, mask=comp).cpu().numpy()
+        assert max_rel_err(a + b, out) <= 1e-5
+
+
+def test_forward_rejects_bad_arguments():
+    cfg = C2
+    ld = LayerData(cfg, 0, 0, 2)
+    ids, gates, _ = ld.gpu_route()
+    ld.build_pool([])
+    x = dev(ld.x)
+    out = torch.empty((2, cfg.hidden), dtype=torch.float32, device="cuda")
+    small = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ftmoe.FtError) as ei:
+        ftmoe.ft_moe_forward(ld.desc, x, ids, gates, ld.pool, out, small)
+    assert ei.value.status == ftmoe.FT_EWORKSPACE
+    bad = ftmoe.make_desc(cfg)
+    bad.top_k = cfg.n_experts + 1
+    with pytest.raises(ftmoe.FtError) as ei:
+        ftmoe.ft_moe_forward(bad, x, ids, gates, ld.pool, out, small)
+    assert ei.value.status == ftmoe.FT_EINVAL
+
+
+# ------------------------------------------------------------ slot table --
+def _gpu_table(L, E, S):
+    tb = torch.zeros(ftmoe.ft_slot_table_bytes(L, E, S), dtype=torch.uint8, device="cuda")
+    ftmoe.ft_slot_table_init(tb, L, E, S)
+    return tb
+
+
+def _table_arrays(tb, L, E, S):
+    a = tb.cpu().numpy().view(np.int32)
+    tick = int(a[0])
+    ks = a[16:16 + L * E].reshape(L, E)
+    sk = a[16 + L * E:16 + L * E + S]
+    lu = a[16 + L * E + S:16 + L * E + 2 * S].view(np.uint32)
+    return tick, ks, sk, lu
+
+
+def _lookup(tb, layer, ids_np):
+    n = ids_np.size
+    ids = dev(ids_np.astype(np.int32))
+    slot = torch.empty(n, dtype=torch.int32, device="cuda")
+    flags = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ml = torch.empty(2 * n, dtype=torch.int32, device="cuda")
+    nm = torch.empty(1, dtype=torch.int32, device="cuda")
+    ftmoe.ft_slot_lookup(tb, layer, ids, slot, flags, ml, nm)
+    nmv = int(nm.item())
+    return slot.cpu().numpy(), flags.cpu().numpy(), ml.cpu().numpy(), nmv
+
+
+def test_slot_table_replays_lru_oracle_bit_exact():
+    g = np.random.default_rng(60)
+    for (L, E, S) in [(3, 16, 10), (2, 64, 24), (5, 8, 40)]:
+        tb = _gpu_table(L, E, S)
+        sim = LruSim(L, E, S)
+        for call in range(300):
+            layer = int(g.integers(0, L))
+            ids = g.integers(0, E, int(g.integers(1, 9))).astype(np.int32)
+            ref = sim.lookup(layer, ids)
+            slot, flags, ml, nm = _lookup(tb, layer, ids)
+            if ref is None:
+                assert nm == -1
+                continue
+            np.testing.assert_array_equal(slot, ref[0])
+            np.testing.assert_array_equal(flags, ref[1])
+            assert nm == len(ref[2])
+            assert [tuple(ml[2 * i:2 * i + 2]) for i in range(nm)] == [tuple(p) for p in ref[2]]
+        tick, ks, sk, lu = _table_arrays(tb, L, E, S)
+        assert tick == sim.tick
+        np.testing.assert_array_equal(ks, sim.key_slot)
+        np.testing.assert_array_equal(sk, sim.slot_key)
+        np.testing.assert_array_equal(lu, sim.last_use)
+
+
+def test_slot_table_exhaustion_changes_nothing():
+    tb = _gpu_table(2, 16, 4)
+    _lookup(tb, 0, np.array([1, 2], np.int32))
+    before = [np.copy(v) if isinstance(v, np.ndarray) else v for v in _table_arrays(tb, 2, 16, 4)]
+    slot, flags, ml, nm = _lookup(tb, 1, np.array([0, 1, 2, 3, 4], np.int32))
+    assert nm == -1 and np.all(slot == -1)
+    after = _table_arrays(tb, 2, 16, 4)
+    assert before[0] == after[0]
+    for u, v in zip(before[1:], after[1:]):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_slot_table_zipf_trace_matches_oracle():
+    cfg = C3
+    L, E, S = cfg.n_layers, cfg.n_experts, cfg.n_slots
+    tr = synth.zipf_trace(cfg, n_steps=48)
+    for b in (1, 4):
+        tb = _gpu_table(L, E, S)
+        sim = LruSim(L, E, S)
+        misses = 0
+        for step in range(tr.shape[0]):
+            for layer in range(L):
+                ids = tr[step, layer, :b].ravel()
+                ref = sim.lookup(layer, ids)
+                slot, flags, ml, nm = _lookup(tb, layer, ids)
+                np.testing.assert_array_equal(slot, ref[0])
+                np.testing.assert_array_equal(flags, ref[1])
+                assert nm == len(ref[2])
+                misses += nm
+        tick, ks, sk, lu = _table_arrays(tb, L, E, S)
+        np.testing.assert_array_equal(ks, sim.key_slot)
+        np.testing.assert_array_equal(lu, sim.last_use)
+        assert misses > 0
+
+
+# ----------------------------------------------------------------- upload --
+def test_upload_copies_records_and_rejects_pageable():
+    cfg = C3
+    stride = synth.record_stride(cfg.hidden, cfg.inter, cfg.w_dtype)
+    rb = synth.record_bytes(cfg.hidden, cfg.inter, cfg.w_dtype)
+    recs = [synth.expert_record(cfg, 2, e) for e in (3, 9)]
+    host = [torch.from_numpy(r).pin_memory() for r in recs]
+    pool = torch.zeros((8, stride), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    ftmoe.ft_expert_upload(pool, stride, rb, [5, 1], [h.data_ptr() for h in host], stream=side, done_event=ev)
+    torch.cuda.current_stream().wait_event(ev)
+    got = pool.cpu().numpy()
+    assert np.array_equal(got[5, :rb], recs[0][:rb]) and np.array_equal(got[1, :rb], recs[1][:rb])
+    assert not got[0].any()
+    pageable = torch.from_numpy(recs[0].copy())
+    with pytest.raises(ftmoe.FtError) as ei:
+        ftmoe.ft_expert_upload(pool, stride, rb, [2], [pageable.data_ptr()])
+    assert ei.value.status == ftmoe.FT_EINVAL

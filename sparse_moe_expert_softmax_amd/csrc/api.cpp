@@ -59,13 +59,15 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T) {
   p.nb = (p.P + PERM_CHUNK - 1) / PERM_CHUNK;
   if (p.nb < 1) p.nb = 1;
   p.mfma = false;
+  p.path = dec_supported(d, T) ? PATH_DEC : PATH_GEMV;
   size_t o = 0;
   p.off_hist = o;    o = align256(o + sizeof(int32_t) * (size_t)p.nb * p.E);
   p.off_offsets = o; o = align256(o + sizeof(int32_t) * (size_t)(p.E + 2));
   p.off_active = o;  o = align256(o + sizeof(int32_t) * (size_t)p.E);
   p.off_perm = o;    o = align256(o + sizeof(int32_t) * (size_t)p.P);
   p.off_pos = o;     o = align256(o + sizeof(int32_t) * (size_t)p.P);
-  p.off_h = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.I);
+  p.off_cnt = o;     o = align256(o + sizeof(uint32_t) * (size_t)(p.H / 16 + 1));
+  p.off_h = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.I);   // fp32 h, or bf16 hi/lo pairs
   p.off_y = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.H);
   p.off_xq = p.off_xs = p.off_hs = o;
   p.bytes = o;
@@ -85,7 +87,7 @@ size_t ft_record_bytes(int32_t hidden, int32_t inter, int32_t w_dtype) {
 
 size_t ft_route_workspace_bytes(const ft_moe_desc* desc, int32_t n_tokens) {
   if (!desc || n_tokens < 0) return 0;
-  return align256(sizeof(double) * (size_t)n_tokens * desc->n_experts);
+  return 256 + align256(sizeof(double) * (size_t)n_tokens * desc->n_experts);
 }
 
 int ft_moe_route(const ft_moe_desc* desc, const void* x, int32_t n_tokens, const void* w_router,
@@ -98,15 +100,16 @@ int ft_moe_route(const ft_moe_desc* desc, const void* x, int32_t n_tokens, const
   if (!x || !w_router || !topk_ids || !topk_gates) return fail(FT_EINVAL, "NULL x / w_router / output");
   if (!aligned(x, 16) || !aligned(w_router, 16)) return fail(FT_EINVAL, "x and w_router must be 16-byte aligned");
   if (desc->hidden % 8) return fail(FT_EINVAL, "hidden must be a multiple of 8");
-  double* lg = logits;
-  if (!lg) {
-    if (!workspace || ws_bytes < ft_route_workspace_bytes(desc, n_tokens))
-      return fail(FT_EWORKSPACE, "route needs %zu workspace bytes when logits is NULL",
-                  ft_route_workspace_bytes(desc, n_tokens));
-    lg = reinterpret_cast<double*>(workspace);
-  }
-  hipError_t e = ft::launch_route(*desc, x, n_tokens, w_router, sel_bias, topk_ids, topk_gates, lg,
-                                  reinterpret_cast<hipStream_t>(stream));
+  if (!workspace || ws_bytes < ft_route_workspace_bytes(desc, n_tokens))
+    return fail(FT_EWORKSPACE, "route needs %zu workspace bytes", ft_route_workspace_bytes(desc, n_tokens));
+  if (!aligned(workspace, 256)) return fail(FT_EINVAL, "workspace must be 256-byte aligned");
+  uint32_t* counter = reinterpret_cast<uint32_t*>(workspace);
+  double* lg = logits ? logits : reinterpret_cast<double*>(reinterpret_cast<char*>(workspace) + 256);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = (n_tokens <= ft::ROUTE_DECODE_MAX_T)
+                     ? ft::launch_route_decode(*desc, x, n_tokens, w_router, sel_bias, topk_ids, topk_gates, lg,
+                                               counter, st)
+                     : ft::launch_route(*desc, x, n_tokens, w_router, sel_bias, topk_ids, topk_gates, lg, st);
   if (e != hipSuccess) return hip_fail(e, "ft_moe_route launch");
   return FT_OK;
 }
@@ -195,7 +198,13 @@ int ft_moe_forward(const ft_moe_desc* desc, const void* x, int32_t n_tokens, con
   if (!aligned(workspace, 256)) return fail(FT_EINVAL, "workspace must be 256-byte aligned");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
-  hipError_t e = ft::launch_permute(pl, topk_ids, expert_mask, ws, st);
+  hipError_t e;
+  if (pl.path == ft::PATH_DEC) {
+    e = ft::launch_dec_forward(*desc, pl, x, topk_ids, expert_mask, slot_ids, pool_base, topk_gates, out, ws, st);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    return FT_OK;
+  }
+  e = ft::launch_permute(pl, topk_ids, expert_mask, ws, st);
   if (e != hipSuccess) return hip_fail(e, "permute launch");
   if (pl.mfma)
     e = ft::launch_mfma_forward(*desc, pl, x, slot_ids, pool_base, topk_gates, out, ws, st);

@@ -1,0 +1,436 @@
+// Decode-batch grouped expert GEMV on gfx950 matrix cores.
+//
+// At decode (a handful of tokens) the expert FFN is a bandwidth-bound
+// matrix-vector product: every byte of each routed expert is read once.
+// The reduction along K is done by v_mfma_f32_16x16x32_bf16 with the 16
+// weight rows of a tile as the A operand and up to 16 routed tokens as the
+// B columns, so no cross-lane reduction is needed and the VALU only decodes
+// weights.  Weights stay in their stored format in HBM and are expanded to
+// bf16 in registers: bf16 as is, MXFP4 with the hardware fp4 conversion
+// (the E8M0 scale is a power of two, so the bf16 values are exact), the
+// NVFP4-like format through fp32 (e2m1 * e4m3 has at most 6 significant
+// bits, exact in bf16) with the fp32 tensor scale applied to the
+// accumulators.  Activations are bf16 inputs (exact).  The down projection
+// reads h as two bf16 terms h = hi + lo (|h - hi - lo| <= 2^-18 |h|).
+//
+// Two kernels per layer:
+//  1. gate/up: grid = (distinct expert d) x (16-row tile of I).  Each
+//     workgroup derives the expert grouping of the <= 64 (token, rank) pairs
+//     itself (no separate permutation launch), splits K over its 4 waves,
+//     sums the wave partials in LDS in a fixed order, applies SwiGLU and
+//     stores h.  Workgroup 0 also clears the combine tile counters.
+//  2. down + combine: grid = (d) x (16-row tile of H).  Each workgroup
+//     stores y for its tile, then bumps the tile's counter; the last
+//     arriving workgroup of a tile sums the gate-weighted y of every token
+//     over j in order (deterministic, no floating-point atomics) and resets
+//     the counter.
+// The combine is the weighted sum of partial expert outputs that the pages
+// rely on for exactness (FreeToken explainer page, "how" section).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace ft {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int DM_WAVES = 4;
+constexpr int DM_THREADS = DM_WAVES * 64;
+
+// Pairs routed to this workgroup's expert, derived from the ids in LDS.
+struct PairInfo {
+  int n_distinct;   // distinct (kept) experts among the pairs
+  int expert;       // expert handled by this workgroup (valid if d < n_distinct)
+  int npairs;       // pairs routed to it
+  int pair[DEC_MAX_PAIRS];  // their pair indices t*k + j, ascending
+};
+
+__device__ __forceinline__ bool dm_in_mask(const uint32_t* mask, int e) {
+  return mask == nullptr || ((mask[e >> 5] >> (e & 31)) & 1u);
+}
+
+// Wave 0: group the P <= 64 pairs by expert; the d-th group in order of first
+// appearance goes to this workgroup.  Any fixed order works: d only chooses
+// which workgroup computes which expert.
+__device__ __forceinline__ void dm_group_pairs(const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask,
+                                               int P, int E, int d, PairInfo* pi) {
+  const int lane = threadIdx.x & 63;
+  int e = -1;
+  bool valid = false;
+  if (lane < P) {
+    e = ids[lane];
+    valid = e >= 0 && e < E && dm_in_mask(mask, e);
+  }
+  uint64_t todo = __ballot(valid);
+  int n = 0;
+  uint64_t mine = 0;
+  int my_e = -1;
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const int el = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t m = __ballot(valid && e == el);
+    if (n == d) { mine = m; my_e = el; }
+    todo &= ~m;
+    ++n;
+  }
+  if ((mine >> lane) & 1ull) {
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    pi->pair[__popcll(mine & below)] = lane;
+  }
+  if (lane == 0) {
+    pi->n_distinct = n;
+    pi->expert = my_e;
+    pi->npairs = __popcll(mine);
+  }
+}
+
+// ------------------------------------------------------------ weight tiles --
+// Chunk = the K extent one lane group covers per step: 64 for bf16 (two
+// MFMAs, 8 contiguous K each), 128 for the fp4 formats (one 32-element block
+// per lane group, four MFMAs).  Actual k of MFMA j, lane group g, element e:
+//   bf16: c*64  + 32*j + 8*g + e        fp4: c*128 + 32*g + 8*j + e
+template <int WD> struct Chunk { static constexpr int K = (WD == FT_BF16) ? 64 : 128; static constexpr int NM = (WD == FT_BF16) ? 2 : 4; };
+
+template <int WD>
+__device__ __forceinline__ int kofs(int c, int j, int g) {
+  if constexpr (WD == FT_BF16) return c * 64 + 32 * j + 8 * g;
+  else return c * 128 + 32 * g + 8 * j;
+}
+
+// Raw bytes of one lane's share of a chunk, loaded before any decode so that
+// the loads of several chunks can be in flight together.
+template <int WD> struct RawW;
+template <> struct RawW<FT_BF16> { uint4 q[2]; };
+template <> struct RawW<FT_MXFP4> { uint4 q; uint32_t s; };
+template <> struct RawW<FT_NVFP4> { uint4 q; uint32_t s; };
+
+struct WMat {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  float tscale;
+  int K;
+};
+
+template <int WD>
+__device__ __forceinline__ WMat wmat(const uint8_t* rec, const RecordLayout& L, int m, int K) {
+  WMat w;
+  w.codes = rec + L.code_off[m];
+  w.scales = rec + L.scale_off[m];
+  w.K = K;
+  w.tscale = 1.0f;
+  if constexpr (WD == FT_NVFP4) w.tscale = reinterpret_cast<const float*>(rec + L.tscale_off)[m];
+  return w;
+}
+
+template <int WD>
+__device__ __forceinline__ void load_raw(const WMat& w, int row, int c, int g, RawW<WD>& r) {
+  if constexpr (WD == FT_BF16) {
+    const uint16_t* base = reinterpret_cast<const uint16_t*>(w.codes) + (int64_t)row * w.K;
+    r.q[0] = *reinterpret_cast<const uint4*>(base + kofs<WD>(c, 0, g));
+    r.q[1] = *reinterpret_cast<const uint4*>(base + kofs<WD>(c, 1, g));
+  } else {
+    const int k0 = c * 128 + 32 * g;  // 32 elements = 16 bytes of codes
+    r.q = *reinterpret_cast<const uint4*>(w.codes + ((int64_t)row * w.K + k0) / 2);
+    if constexpr (WD == FT_MXFP4) {
+      r.s = w.scales[(int64_t)row * (w.K / 32) + k0 / 32];
+    } else {  // two E4M3 block scales, blocks of 16
+      const uint8_t* sp = w.scales + (int64_t)row * (w.K / 16) + k0 / 16;
+      r.s = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16_trunc(float a, float b) {
+  // exact values only (the low 16 bits are zero): take the upper halves
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+}
+
+// 8 E2M1 codes (one dword) -> 8 bf16, each times `scale` (a power of two).
+__device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t q, float scale) {
+  union { bf16x2_t h[4]; bf16x8_t v; } u;
+  u.h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 0);
+  u.h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q >> 8, scale, 0);
+  u.h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q >> 16, scale, 0);
+  u.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q >> 24, scale, 0);
+  return u.v;
+}
+
+// 8 E2M1 codes times an arbitrary fp32 block scale (exact products) -> bf16.
+__device__ __forceinline__ bf16x8_t fp4x8_bf16_mul(uint32_t q, float s) {
+  uint4 o;
+  uint32_t* op = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q >> (8 * b), 1.0f, 0);
+    op[b] = pack_bf16_trunc(v[0] * s, v[1] * s);
+  }
+  return as_bf16x8(o);
+}
+
+// A operand (weights) of MFMA j of a chunk.
+template <int WD>
+__device__ __forceinline__ bf16x8_t decode_a(const RawW<WD>& r, int j) {
+  if constexpr (WD == FT_BF16) {
+    return as_bf16x8(r.q[j]);
+  } else if constexpr (WD == FT_MXFP4) {
+    const uint32_t q = (j == 0) ? r.q.x : (j == 1) ? r.q.y : (j == 2) ? r.q.z : r.q.w;
+    return fp4x8_bf16(q, e8m0_to_f32(r.s));
+  } else {
+    const uint32_t q = (j == 0) ? r.q.x : (j == 1) ? r.q.y : (j == 2) ? r.q.z : r.q.w;
+    const float s = e4m3_to_f32((j < 2) ? (r.s & 0xFFu) : (r.s >> 8));
+    return fp4x8_bf16_mul(q, s);
+  }
+}
+
+__device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// bf16 round-to-nearest-even of a finite fp32 value
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// -------------------------------------------------------------- gate / up --
+template <int WD, int UNROLL>
+__global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P,
+    int k, const void* __restrict__ pool, int64_t stride, const int32_t* __restrict__ slot_ids,
+    uint16_t* __restrict__ hbuf, uint32_t* __restrict__ tile_cnt, int n_tiles_h, int H, int I, int E) {
+  __shared__ PairInfo pi;
+  __shared__ f32x4_t red[DM_WAVES][2][64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
+  const int n_rt = I / 16;
+  const int d = blockIdx.x / n_rt, rt = blockIdx.x % n_rt;
+  if (blockIdx.x == 0)
+    for (int i = tid; i < n_tiles_h; i += DM_THREADS) tile_cnt[i] = 0u;
+  if (wv == 0) dm_group_pairs(ids, mask, P, E, d, &pi);
+  __syncthreads();
+  if (d >= pi.n_distinct) return;
+  const int e = pi.expert, np = pi.npairs;
+  const int slot = slot_ids ? slot_ids[pi.pair[0]] : e;
+  const int row = rt * 16 + col;  // A-operand row of this lane
+  if (slot < 0) {  // failed lookup: poison this expert's h, never read out of bounds
+    if (wv == 0)
+      for (int q = lane; q < np * 16; q += 64) {
+        const int p = pi.pair[q / 16];
+        hbuf[(int64_t)p * 2 * I + rt * 16 + (q % 16)] = 0x7FC0u;
+        hbuf[(int64_t)p * 2 * I + I + rt * 16 + (q % 16)] = 0u;
+      }
+    return;
+  }
+  const uint8_t* rec = reinterpret_cast<const uint8_t*>(pool) + (int64_t)slot * stride;
+  const RecordLayout L = record_layout(H, I, WD);
+  const WMat Gm = wmat<WD>(rec, L, 0, H), Um = wmat<WD>(rec, L, 1, H);
+  constexpr int CK = Chunk<WD>::K, NM = Chunk<WD>::NM;
+  const int nchunk = H / CK;
+
+  for (int tg = 0; tg < np; tg += 16) {
+    const bool tok_ok = tg + col < np;
+    const int t = tok_ok ? pi.pair[tg + col] / k : 0;
+    const uint16_t* xr = x + (int64_t)t * H;
+    f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = wv; c0 < nchunk; c0 += DM_WAVES * UNROLL) {
+      RawW<WD> rg[UNROLL], ru[UNROLL];
+      uint4 xb[UNROLL][NM];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int c = c0 + u * DM_WAVES;
+        if (c < nchunk) {
+          load_raw<WD>(Gm, row, c, g, rg[u]);
+          load_raw<WD>(Um, row, c, g, ru[u]);
+#pragma unroll
+          for (int j = 0; j < NM; ++j)
+            xb[u][j] = tok_ok ? *reinterpret_cast<const uint4*>(xr + kofs<WD>(c, j, g)) : make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int c = c0 + u * DM_WAVES;
+        if (c < nchunk) {
+#pragma unroll
+          for (int j = 0; j < NM; ++j) {
+            const bf16x8_t b = as_bf16x8(xb[u][j]);
+            ag = mfma(decode_a<WD>(rg[u], j), b, ag);
+            au = mfma(decode_a<WD>(ru[u], j), b, au);
+          }
+        }
+      }
+    }
+    red[wv][0][lane] = ag;
+    red[wv][1][lane] = au;
+    __syncthreads();
+    if (wv == 0) {
+      f32x4_t sg = red[0][0][lane], su = red[0][1][lane];
+#pragma unroll
+      for (int w = 1; w < DM_WAVES; ++w) { sg += red[w][0][lane]; su += red[w][1][lane]; }
+      if (tok_ok) {
+        const int p = pi.pair[tg + col];
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gv = sg[i] * Gm.tscale, uv = su[i] * Um.tscale;
+          const float h = gv / (1.0f + expf(-gv)) * uv;
+          const uint32_t hb = bf16_rne_bits(h);
+          hi[i] = (uint16_t)hb;
+          lo[i] = (uint16_t)bf16_rne_bits(h - __uint_as_float(hb << 16));
+        }
+        // output rows of this lane: rt*16 + 4*g + i
+        uint16_t* hp = hbuf + (int64_t)p * 2 * I + rt * 16 + 4 * g;
+        *reinterpret_cast<uint2*>(hp) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+        *reinterpret_cast<uint2*>(hp + I) =
+            make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------- down + combine --
+template <int WD, int UNROLL>
+__global__ void __launch_bounds__(DM_THREADS) dec_down_kernel(
+    const uint16_t* __restrict__ hbuf, const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P,
+    int k, const void* __restrict__ pool, int64_t stride, const int32_t* __restrict__ slot_ids,
+    const float* __restrict__ gates, float* __restrict__ ybuf, float* __restrict__ out,
+    uint32_t* __restrict__ tile_cnt, int T, int H, int I, int E) {
+  __shared__ PairInfo pi;
+  __shared__ f32x4_t red[DM_WAVES][64];
+  __shared__ int last;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
+  const int n_rt = H / 16;
+  const int d = blockIdx.x / n_rt, rt = blockIdx.x % n_rt;
+  if (wv == 0) dm_group_pairs(ids, mask, P, E, d, &pi);
+  __syncthreads();
+  const int nd = pi.n_distinct;
+  if (nd == 0) {  // every pair masked out: the output is zero
+    if (d == 0)
+      for (int q = tid; q < T * 16; q += DM_THREADS) out[(int64_t)(q / 16) * H + rt * 16 + (q % 16)] = 0.f;
+    return;
+  }
+  if (d >= nd) return;
+  const int e = pi.expert, np = pi.npairs;
+  const int slot = slot_ids ? slot_ids[pi.pair[0]] : e;
+  const int row = rt * 16 + col;
+  constexpr int CK = Chunk<WD>::K, NM = Chunk<WD>::NM;
+  const int nchunk = I / CK;
+  if (slot >= 0) {
+    const uint8_t* rec = reinterpret_cast<const uint8_t*>(pool) + (int64_t)slot * stride;
+    const RecordLayout L = record_layout(H, I, WD);
+    const WMat Dm = wmat<WD>(rec, L, 2, I);
+    for (int tg = 0; tg < np; tg += 16) {
+      const bool tok_ok = tg + col < np;
+      const int p = tok_ok ? pi.pair[tg + col] : 0;
+      const uint16_t* hh = hbuf + (int64_t)p * 2 * I;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = wv; c0 < nchunk; c0 += DM_WAVES * UNROLL) {
+        RawW<WD> rw[UNROLL];
+        uint4 bh[UNROLL][NM], bl[UNROLL][NM];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int c = c0 + u * DM_WAVES;
+          if (c < nchunk) {
+            load_raw<WD>(Dm, row, c, g, rw[u]);
+#pragma unroll
+            for (int j = 0; j < NM; ++j) {
+              const int ko = kofs<WD>(c, j, g);
+              bh[u][j] = tok_ok ? *reinterpret_cast<const uint4*>(hh + ko) : make_uint4(0, 0, 0, 0);
+              bl[u][j] = tok_ok ? *reinterpret_cast<const uint4*>(hh + I + ko) : make_uint4(0, 0, 0, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int c = c0 + u * DM_WAVES;
+          if (c < nchunk) {
+#pragma unroll
+            for (int j = 0; j < NM; ++j) {
+              const bf16x8_t a = decode_a<WD>(rw[u], j);
+              acc = mfma(a, as_bf16x8(bh[u][j]), acc);
+              acc = mfma(a, as_bf16x8(bl[u][j]), acc);
+            }
+          }
+        }
+      }
+      red[wv][lane] = acc;
+      __syncthreads();
+      if (wv == 0 && tok_ok) {
+        f32x4_t s = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < DM_WAVES; ++w) s += red[w][lane];
+        s *= Dm.tscale;
+        *reinterpret_cast<f32x4_t*>(ybuf + (int64_t)p * H + rt * 16 + 4 * g) = s;
+      }
+      __syncthreads();
+    }
+  } else if (wv == 0) {  // failed lookup: poison this expert's y
+    for (int q = lane; q < np * 16; q += 64) ybuf[(int64_t)pi.pair[q / 16] * H + rt * 16 + (q % 16)] = __builtin_nanf("");
+  }
+  // last workgroup to finish this row tile combines every token's outputs
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last = (atomicAdd(&tile_cnt[rt], 1u) == (uint32_t)(nd - 1));
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  for (int q = tid; q < T * 16; q += DM_THREADS) {
+    const int t = q / 16, r = rt * 16 + (q % 16);
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int pj = t * k + j;
+      const int ej = ids[pj];
+      if (ej < 0 || ej >= E || !dm_in_mask(mask, ej)) continue;
+      acc = fmaf(gates[pj], ybuf[(int64_t)pj * H + r], acc);
+    }
+    out[(int64_t)t * H + r] = acc;
+  }
+  if (tid == 0) tile_cnt[rt] = 0u;
+}
+
+template <int WD>
+static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const void* x, const int32_t* ids,
+                                const uint32_t* mask, const int32_t* slot_ids, const void* pool, const float* gates,
+                                float* out, char* ws, hipStream_t st) {
+  const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k;
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + pl.off_h);
+  float* ybuf = reinterpret_cast<float*>(ws + pl.off_y);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + pl.off_cnt);
+  const int nd_max = pl.P < E ? pl.P : E;
+  dec_gateup_kernel<WD, 2><<<nd_max * (I / 16), DM_THREADS, 0, st>>>(
+      reinterpret_cast<const uint16_t*>(x), ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, hbuf, cnt, H / 16,
+      H, I, E);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dec_down_kernel<WD, 2><<<nd_max * (H / 16), DM_THREADS, 0, st>>>(hbuf, ids, mask, pl.P, k, pool, d.expert_stride,
+                                                                   slot_ids, gates, ybuf, out, cnt, pl.T, H, I, E);
+  return hipGetLastError();
+}
+
+bool dec_supported(const ft_moe_desc& d, int T) {
+  if (d.act_dtype != FT_BF16) return false;
+  if (d.w_dtype != FT_BF16 && d.w_dtype != FT_MXFP4 && d.w_dtype != FT_NVFP4) return false;
+  const int64_t P = (int64_t)T * d.top_k;
+  if (P < 1 || P > DEC_MAX_PAIRS) return false;
+  const int ck = (d.w_dtype == FT_BF16) ? 64 : 128;
+  return d.hidden % ck == 0 && d.inter % ck == 0 && d.hidden % 16 == 0 && d.inter % 16 == 0;
+}
+
+hipError_t launch_dec_forward(const ft_moe_desc& d, const DecPlan& pl, const void* x, const int32_t* ids,
+                              const uint32_t* mask, const int32_t* slot_ids, const void* pool, const float* gates,
+                              float* out, char* ws, hipStream_t st) {
+  switch (d.w_dtype) {
+    case FT_BF16: return dec_forward_t<FT_BF16>(d, pl, x, ids, mask, slot_ids, pool, gates, out, ws, st);
+    case FT_MXFP4: return dec_forward_t<FT_MXFP4>(d, pl, x, ids, mask, slot_ids, pool, gates, out, ws, st);
+    default: return dec_forward_t<FT_NVFP4>(d, pl, x, ids, mask, slot_ids, pool, gates, out, ws, st);
+  }
+}
+
+}  // namespace ft

@@ -11,6 +11,9 @@ namespace ft {
 // router
 hipError_t launch_route(const ft_moe_desc& d, const void* x, int T, const void* wr, const float* sel_bias,
                         int32_t* ids, float* gates, double* logits, hipStream_t st);
+constexpr int ROUTE_DECODE_MAX_T = 16;
+hipError_t launch_route_decode(const ft_moe_desc& d, const void* x, int T, const void* wr, const float* sel_bias,
+                               int32_t* ids, float* gates, double* logits, uint32_t* counter, hipStream_t st);
 
 // slot table
 size_t slot_table_bytes(int L, int E, int S);
@@ -20,14 +23,26 @@ hipError_t launch_slot_lookup(void* table, int layer, const int32_t* ids, int n_
 int slot_max_slots();
 int slot_max_experts();
 
+// forward paths
+enum FwdPath { PATH_DEC = 0, PATH_GEMV = 1, PATH_MFMA = 2 };
+constexpr int DEC_MAX_PAIRS = 64;  // decode path: T*k pairs grouped inside the kernels
+
 // forward workspace: every region 256-byte aligned
 struct FwdPlan {
   int T, P, E, H, I, nb;       // tokens, pairs, experts, hidden, inter, permute blocks
+  int path;                    // FwdPath
   bool mfma;                   // large-batch MXFP4 path on scaled MFMA
-  size_t off_hist, off_offsets, off_active, off_perm, off_pos, off_h, off_y, off_xq, off_xs, off_hs;
+  size_t off_hist, off_offsets, off_active, off_perm, off_pos, off_h, off_y, off_xq, off_xs, off_hs, off_cnt;
   size_t bytes;
 };
+typedef FwdPlan DecPlan;
 FwdPlan plan_forward(const ft_moe_desc& d, int T);
+
+// decode path (matrix-core GEMV, in-kernel grouping, fused combine)
+bool dec_supported(const ft_moe_desc& d, int T);
+hipError_t launch_dec_forward(const ft_moe_desc& d, const DecPlan& pl, const void* x, const int32_t* ids,
+                              const uint32_t* mask, const int32_t* slot_ids, const void* pool, const float* gates,
+                              float* out, char* ws, hipStream_t st);
 
 // permutation (grouping pairs by expert, stable in pair order)
 hipError_t launch_permute(const FwdPlan& pl, const int32_t* ids, const uint32_t* mask, char* ws,

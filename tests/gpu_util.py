@@ -64,7 +64,8 @@ class LayerData:
         gates = torch.empty((T, cfg.top_k), dtype=torch.float32, device="cuda")
         logits = torch.empty((T, cfg.n_experts), dtype=torch.float64, device="cuda")
         b = None if bias is None else dev(bias.astype(np.float32))
-        ftmoe.ft_moe_route(self.desc, x, wr, ids, gates, sel_bias=b, logits=logits)
+        ws = torch.zeros(ftmoe.ft_route_workspace_bytes(self.desc, T), dtype=torch.uint8, device="cuda")
+        ftmoe.ft_moe_route(self.desc, x, wr, ids, gates, sel_bias=b, logits=logits, workspace=ws)
         return ids, gates, logits
 
     def gpu_forward(self, ids, gates, mask=None, slot_ids=None, pool=None):

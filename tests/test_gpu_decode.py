@@ -264,3 +264,33 @@ def test_upload_copies_records_and_rejects_pageable():
     with pytest.raises(ftmoe.FtError) as ei:
         ftmoe.ft_expert_upload(pool, stride, rb, [2], [pageable.data_ptr()])
     assert ei.value.status == ftmoe.FT_EINVAL
+
+
+@pytest.mark.parametrize("cfg,T", [(C2, 9), (C3, 11)])
+def test_forward_general_path_above_decode_pairs(cfg, T):
+    """More than 64 (token, rank) pairs: the permute + grouped GEMV path."""
+    print(f"general path {cfg.name} T={T}", flush=True)
+    run_layer(cfg, 3, 7, T)
+
+
+def test_forward_decode_path_slot_indirection_and_poison():
+    """Records placed at arbitrary pool slots through slot_ids; a negative slot
+    (failed lookup) turns that expert's outputs into NaN instead of a fault."""
+    cfg = C2
+    ld = LayerData(cfg, 4, 9, 2)
+    ids, gates, o_ids = check_route(ld)
+    uniq = sorted(set(o_ids.ravel().tolist()))
+    slot_of = {e: 3 + 2 * i for i, e in enumerate(uniq)}
+    pool = torch.full((3 + 2 * len(uniq), ld.stride), 0xFF, dtype=torch.uint8, device="cuda")
+    for e, s in slot_of.items():
+        pool[s].copy_(torch.from_numpy(ld.record(e)))
+    slots = torch.from_numpy(np.vectorize(slot_of.get)(o_ids).astype(np.int32)).cuda()
+    out = ld.gpu_forward(ids, gates, slot_ids=slots, pool=pool).cpu().numpy()
+    ref, _, _ = ld.oracle_layer()
+    assert max_rel_err(out, ref) <= 1e-2
+    bad = slots.clone()
+    bad[0, 0] = -1
+    e0 = int(o_ids[0, 0])
+    bad[torch.from_numpy(o_ids == e0).cuda()] = -1
+    out2 = ld.gpu_forward(ids, gates, slot_ids=bad, pool=pool).cpu().numpy()
+    assert np.isnan(out2[0]).any()

@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--workload", default="decode_bf16_h2048_e128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of HIP-graph replay")
+    ap.add_argument("--graphs", type=int, default=16, help="distinct captured steps (distinct inputs) replayed in turn")
     return ap.parse_args()
 
 
@@ -149,20 +151,50 @@ def main():
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
+    graphs = []
+    if not args.eager:
+        # one captured graph per distinct input set; replayed in turn
+        n_g = min(args.graphs, args.steps)
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for gi in range(n_g):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    step_stream = torch.cuda.current_stream()
+                    for l in range(L):
+                        s_ = args.warmup + gi
+                        ftmoe.ft_moe_route(desc, xs[s_, l], routers[l], ids_all[s_, l], gates_all[s_, l],
+                                           workspace=rws, stream=step_stream)
+                        ftmoe.ft_moe_forward(desc, xs[s_, l], ids_all[s_, l], gates_all[s_, l], pools[l], out, ws,
+                                             stream=step_stream)
+                graphs.append(g)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for s in range(args.warmup, n_steps):
-        step(s)
+    for i, s in enumerate(range(args.warmup, n_steps)):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(s)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+    print(f"[bench] timed {args.steps} steps ({'graph' if graphs else 'eager'}): {ms_per_step:.4f} ms/step",
+          file=sys.stderr, flush=True)
 
-    # per-call forward durations (HIP events on the launch stream), a second pass
+    # per-call forward durations: HIP events on the launch stream around every
+    # forward, with the queue filled ahead (a device-side sleep) so that host
+    # launch latency does not fall inside the measured intervals
     n_meas = min(args.steps, 50)
     fwd_ms = []
     for s in range(args.warmup, args.warmup + n_meas):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+        torch.cuda._sleep(2_000_000)
         step(s, ev)
         torch.cuda.synchronize()
         fwd_ms.extend(a.elapsed_time(b) for a, b in ev)
@@ -172,10 +204,11 @@ def main():
     ids_np = ids_all.cpu().numpy()
     distinct = np.array([[len(np.unique(ids_np[s, l])) for l in range(L)] for s in range(n_steps)])
     d_meas = distinct[args.warmup:args.warmup + n_meas].ravel()
+    d_timed = np.array([distinct[args.warmup + (i % len(graphs) if graphs else i)].sum() for i in range(args.steps)])
     fwd_bytes = d_meas * rec_bytes + B * H * 2 + B * H * 4
     achieved_gbs = float(np.mean(fwd_bytes) / (np.mean(fwd_ms) * 1e-3) / 1e9)
     route_bytes = E * H * 2 + B * H * 2
-    step_bytes = float(np.mean(distinct[args.warmup:].sum(axis=1))) * rec_bytes + L * (route_bytes + B * H * 4)
+    step_bytes = float(np.mean(d_timed)) * rec_bytes + L * (route_bytes + B * H * 4)
     layer_tok_s = B * L / (ms_per_step * 1e-3)
 
     res = {
@@ -192,7 +225,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": B, "layers": L, "hidden": H, "experts": E, "top_k": k,
-                   "inter": I, "weights": "bf16", "resident_gb": round(L * E * stride / 1e9, 1)},
+                   "inter": I, "weights": "bf16", "resident_gb": round(L * E * stride / 1e9, 1),
+                   "launch": "eager" if not graphs else f"hip graphs ({len(graphs)} captured steps)"},
         "stack_tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
         "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "ft_moe_forward (expert GEMV)",

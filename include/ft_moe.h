@@ -85,11 +85,8 @@ size_t ft_record_bytes(int32_t hidden, int32_t inter, int32_t w_dtype);
  * topk_gates[t,j] = softmax of the selected l (renormalize=1) or the full
  * softmax probability (renormalize=0), computed in fp64, stored fp32.
  * logits (nullable): l as fp64 [T, E].
- * workspace: ft_route_workspace_bytes(desc, T) bytes, 256-byte aligned and
- * zero-filled before its first use; its first word is a device counter that
- * every call leaves at zero (calls sharing a workspace must not overlap).
- * Up to 16 tokens run as one launch (the last workgroup to finish the
- * logits does the top-k); more tokens run logits and top-k as two launches.
+ * workspace: ft_route_workspace_bytes(desc, T) bytes, 256-byte aligned
+ * (holds the logits when `logits` is NULL; calls sharing it must not overlap).
  * Errors: FT_EINVAL on null x/w_router/outputs, n_tokens < 0, k > E,
  * E > 1024, k > 32; FT_EUNSUPPORTED on other dtypes.  n_tokens = 0 is a no-op. */
 size_t ft_route_workspace_bytes(const ft_moe_desc* desc, int32_t n_tokens);

@@ -103,12 +103,10 @@ int ft_moe_route(const ft_moe_desc* desc, const void* x, int32_t n_tokens, const
   if (!workspace || ws_bytes < ft_route_workspace_bytes(desc, n_tokens))
     return fail(FT_EWORKSPACE, "route needs %zu workspace bytes", ft_route_workspace_bytes(desc, n_tokens));
   if (!aligned(workspace, 256)) return fail(FT_EINVAL, "workspace must be 256-byte aligned");
-  uint32_t* counter = reinterpret_cast<uint32_t*>(workspace);
   double* lg = logits ? logits : reinterpret_cast<double*>(reinterpret_cast<char*>(workspace) + 256);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = (n_tokens <= ft::ROUTE_DECODE_MAX_T)
-                     ? ft::launch_route_decode(*desc, x, n_tokens, w_router, sel_bias, topk_ids, topk_gates, lg,
-                                               counter, st)
+                     ? ft::launch_route_decode(*desc, x, n_tokens, w_router, sel_bias, topk_ids, topk_gates, lg, st)
                      : ft::launch_route(*desc, x, n_tokens, w_router, sel_bias, topk_ids, topk_gates, lg, st);
   if (e != hipSuccess) return hip_fail(e, "ft_moe_route launch");
   return FT_OK;

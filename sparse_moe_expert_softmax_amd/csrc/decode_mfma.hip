@@ -18,12 +18,14 @@
 //     workgroup derives the expert grouping of the <= 64 (token, rank) pairs
 //     itself (no separate permutation launch), splits K over its 4 waves,
 //     sums the wave partials in LDS in a fixed order, applies SwiGLU and
-//     stores h.  Workgroup 0 also clears the combine tile counters.
-//  2. down + combine: grid = (d) x (16-row tile of H).  Each workgroup
-//     stores y for its tile, then bumps the tile's counter; the last
-//     arriving workgroup of a tile sums the gate-weighted y of every token
-//     over j in order (deterministic, no floating-point atomics) and resets
-//     the counter.
+//     stores g * h (gate of the pair folded in).
+//  2. down + combine: grid = 16-row tiles of H.  The gate is folded into h
+//     (h' = g_tj * h_tj), so out[t] = sum over routed experts of D_e h'_t is
+//     one accumulation: every (expert, K chunk) job of the tile adds into the
+//     same 16 x 16 (rows x tokens) accumulator.  Jobs are dealt to the 16
+//     waves round-robin and the wave partials are summed in LDS in a fixed
+//     order, so the result is deterministic without any cross-workgroup
+//     synchronisation or floating-point atomics.
 // The combine is the weighted sum of partial expert outputs that the pages
 // rely on for exactness (FreeToken explainer page, "how" section).
 #include "common.hpp"
@@ -205,14 +207,12 @@ template <int WD, int UNROLL>
 __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P,
     int k, const void* __restrict__ pool, int64_t stride, const int32_t* __restrict__ slot_ids,
-    uint16_t* __restrict__ hbuf, uint32_t* __restrict__ tile_cnt, int n_tiles_h, int H, int I, int E) {
+    const float* __restrict__ gates, uint16_t* __restrict__ hbuf, int H, int I, int E) {
   __shared__ PairInfo pi;
   __shared__ f32x4_t red[DM_WAVES][2][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
   const int n_rt = I / 16;
   const int d = blockIdx.x / n_rt, rt = blockIdx.x % n_rt;
-  if (blockIdx.x == 0)
-    for (int i = tid; i < n_tiles_h; i += DM_THREADS) tile_cnt[i] = 0u;
   if (wv == 0) dm_group_pairs(ids, mask, P, E, d, &pi);
   __syncthreads();
   if (d >= pi.n_distinct) return;
@@ -237,6 +237,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
   for (int tg = 0; tg < np; tg += 16) {
     const bool tok_ok = tg + col < np;
     const int t = tok_ok ? pi.pair[tg + col] / k : 0;
+    const float gate = (tok_ok && wv == 0) ? gates[pi.pair[tg + col]] : 0.f;  // issued before the stream
     const uint16_t* xr = x + (int64_t)t * H;
     f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = wv; c0 < nchunk; c0 += DM_WAVES * UNROLL) {
@@ -279,7 +280,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float gv = sg[i] * Gm.tscale, uv = su[i] * Um.tscale;
-          const float h = gv / (1.0f + expf(-gv)) * uv;
+          const float h = gate * (gv / (1.0f + expf(-gv)) * uv);
           const uint32_t hb = bf16_rne_bits(h);
           hi[i] = (uint16_t)hb;
           lo[i] = (uint16_t)bf16_rne_bits(h - __uint_as_float(hb << 16));
@@ -296,103 +297,119 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
 }
 
 // ---------------------------------------------------------- down + combine --
+constexpr int DD_WAVES = 16;
+constexpr int DD_THREADS = DD_WAVES * 64;
+constexpr int DD_MAXT = 16;  // token columns of the accumulator
+
+struct DownInfo {
+  int n_distinct;
+  int slot[DEC_MAX_PAIRS];                 // record slot of each distinct expert (-1: failed lookup)
+  int pair[DEC_MAX_PAIRS][DD_MAXT];        // pair index of (expert d, token t), -1 if t not routed to d
+};
+
+// Wave 0: every kept (expert, token) pair, grouped by expert in order of first appearance.
+__device__ __forceinline__ void dd_group_all(const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask,
+                                             const int32_t* __restrict__ slot_ids, int P, int k, int E,
+                                             DownInfo* di) {
+  const int lane = threadIdx.x & 63;
+  int e = -1;
+  bool valid = false;
+  if (lane < P) {
+    e = ids[lane];
+    valid = e >= 0 && e < E && dm_in_mask(mask, e);
+  }
+  for (int q = lane; q < DEC_MAX_PAIRS * DD_MAXT; q += 64) (&di->pair[0][0])[q] = -1;
+  uint64_t todo = __ballot(valid);
+  int n = 0;
+  int my_d = -1;
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const int el = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t m = __ballot(valid && e == el);
+    if ((m >> lane) & 1ull) my_d = n;
+    if (lane == leader) di->slot[n] = slot_ids ? slot_ids[leader] : el;
+    todo &= ~m;
+    ++n;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  if (valid) di->pair[my_d][lane / k] = lane;
+  if (lane == 0) di->n_distinct = n;
+}
+
 template <int WD, int UNROLL>
-__global__ void __launch_bounds__(DM_THREADS) dec_down_kernel(
+__global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
     const uint16_t* __restrict__ hbuf, const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P,
     int k, const void* __restrict__ pool, int64_t stride, const int32_t* __restrict__ slot_ids,
-    const float* __restrict__ gates, float* __restrict__ ybuf, float* __restrict__ out,
-    uint32_t* __restrict__ tile_cnt, int T, int H, int I, int E) {
-  __shared__ PairInfo pi;
-  __shared__ f32x4_t red[DM_WAVES][64];
-  __shared__ int last;
+    float* __restrict__ out, int T, int H, int I, int E) {
+  __shared__ DownInfo di;
+  __shared__ f32x4_t red[DD_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
-  const int n_rt = H / 16;
-  const int d = blockIdx.x / n_rt, rt = blockIdx.x % n_rt;
-  if (wv == 0) dm_group_pairs(ids, mask, P, E, d, &pi);
+  const int rt = blockIdx.x;
+  if (wv == 0) dd_group_all(ids, mask, slot_ids, P, k, E, &di);
   __syncthreads();
-  const int nd = pi.n_distinct;
-  if (nd == 0) {  // every pair masked out: the output is zero
-    if (d == 0)
-      for (int q = tid; q < T * 16; q += DM_THREADS) out[(int64_t)(q / 16) * H + rt * 16 + (q % 16)] = 0.f;
-    return;
-  }
-  if (d >= nd) return;
-  const int e = pi.expert, np = pi.npairs;
-  const int slot = slot_ids ? slot_ids[pi.pair[0]] : e;
+  const int nd = di.n_distinct;
   const int row = rt * 16 + col;
   constexpr int CK = Chunk<WD>::K, NM = Chunk<WD>::NM;
   const int nchunk = I / CK;
-  if (slot >= 0) {
-    const uint8_t* rec = reinterpret_cast<const uint8_t*>(pool) + (int64_t)slot * stride;
-    const RecordLayout L = record_layout(H, I, WD);
-    const WMat Dm = wmat<WD>(rec, L, 2, I);
-    for (int tg = 0; tg < np; tg += 16) {
-      const bool tok_ok = tg + col < np;
-      const int p = tok_ok ? pi.pair[tg + col] : 0;
-      const uint16_t* hh = hbuf + (int64_t)p * 2 * I;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      for (int c0 = wv; c0 < nchunk; c0 += DM_WAVES * UNROLL) {
-        RawW<WD> rw[UNROLL];
-        uint4 bh[UNROLL][NM], bl[UNROLL][NM];
+  const int njobs = nd * nchunk;
+  const RecordLayout L = record_layout(H, I, WD);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  bool poisoned = false;
+  for (int j0 = wv; j0 < njobs; j0 += DD_WAVES * UNROLL) {
+    RawW<WD> rw[UNROLL];
+    uint4 bh[UNROLL][NM], bl[UNROLL][NM];
+    float ts[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          const int c = c0 + u * DM_WAVES;
-          if (c < nchunk) {
-            load_raw<WD>(Dm, row, c, g, rw[u]);
-#pragma unroll
-            for (int j = 0; j < NM; ++j) {
-              const int ko = kofs<WD>(c, j, g);
-              bh[u][j] = tok_ok ? *reinterpret_cast<const uint4*>(hh + ko) : make_uint4(0, 0, 0, 0);
-              bl[u][j] = tok_ok ? *reinterpret_cast<const uint4*>(hh + I + ko) : make_uint4(0, 0, 0, 0);
-            }
-          }
+    for (int u = 0; u < UNROLL; ++u) {
+      const int job = j0 + u * DD_WAVES;
+      ts[u] = 0.f;
+      if (job < njobs) {
+        const int d = job / nchunk, c = job % nchunk;
+        const int slot = di.slot[d];
+        const int p = (col < T) ? di.pair[d][col] : -1;
+        if (slot < 0) {
+          poisoned = true;
+        } else {
+          const uint8_t* rec = reinterpret_cast<const uint8_t*>(pool) + (int64_t)slot * stride;
+          const WMat Dm = wmat<WD>(rec, L, 2, I);
+          ts[u] = Dm.tscale;
+          load_raw<WD>(Dm, row, c, g, rw[u]);
         }
+        const uint16_t* hh = hbuf + (int64_t)(p < 0 ? 0 : p) * 2 * I;
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          const int c = c0 + u * DM_WAVES;
-          if (c < nchunk) {
-#pragma unroll
-            for (int j = 0; j < NM; ++j) {
-              const bf16x8_t a = decode_a<WD>(rw[u], j);
-              acc = mfma(a, as_bf16x8(bh[u][j]), acc);
-              acc = mfma(a, as_bf16x8(bl[u][j]), acc);
-            }
-          }
+        for (int jj = 0; jj < NM; ++jj) {
+          const int ko = kofs<WD>(c, jj, g);
+          bh[u][jj] = p >= 0 ? *reinterpret_cast<const uint4*>(hh + ko) : make_uint4(0, 0, 0, 0);
+          bl[u][jj] = p >= 0 ? *reinterpret_cast<const uint4*>(hh + I + ko) : make_uint4(0, 0, 0, 0);
         }
       }
-      red[wv][lane] = acc;
-      __syncthreads();
-      if (wv == 0 && tok_ok) {
-        f32x4_t s = red[0][lane];
+    }
 #pragma unroll
-        for (int w = 1; w < DM_WAVES; ++w) s += red[w][lane];
-        s *= Dm.tscale;
-        *reinterpret_cast<f32x4_t*>(ybuf + (int64_t)p * H + rt * 16 + 4 * g) = s;
+    for (int u = 0; u < UNROLL; ++u) {
+      if (ts[u] != 0.f) {
+        f32x4_t part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < NM; ++jj) {
+          const bf16x8_t a = decode_a<WD>(rw[u], jj);
+          part = mfma(a, as_bf16x8(bh[u][jj]), part);
+          part = mfma(a, as_bf16x8(bl[u][jj]), part);
+        }
+        if constexpr (WD == FT_NVFP4) acc += part * ts[u];
+        else acc += part;
       }
-      __syncthreads();
     }
-  } else if (wv == 0) {  // failed lookup: poison this expert's y
-    for (int q = lane; q < np * 16; q += 64) ybuf[(int64_t)pi.pair[q / 16] * H + rt * 16 + (q % 16)] = __builtin_nanf("");
   }
-  // last workgroup to finish this row tile combines every token's outputs
-  __threadfence();
+  if (poisoned) acc = acc * __builtin_nanf("");
+  red[wv][lane] = acc;
   __syncthreads();
-  if (tid == 0) last = (atomicAdd(&tile_cnt[rt], 1u) == (uint32_t)(nd - 1));
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  for (int q = tid; q < T * 16; q += DM_THREADS) {
-    const int t = q / 16, r = rt * 16 + (q % 16);
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int pj = t * k + j;
-      const int ej = ids[pj];
-      if (ej < 0 || ej >= E || !dm_in_mask(mask, ej)) continue;
-      acc = fmaf(gates[pj], ybuf[(int64_t)pj * H + r], acc);
-    }
-    out[(int64_t)t * H + r] = acc;
+  if (wv == 0 && col < T) {
+    f32x4_t s = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < DD_WAVES; ++w) s += red[w][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[(int64_t)col * H + rt * 16 + 4 * g + i] = s[i];
   }
-  if (tid == 0) tile_cnt[rt] = 0u;
 }
 
 template <int WD>
@@ -401,16 +418,14 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
                                 float* out, char* ws, hipStream_t st) {
   const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k;
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + pl.off_h);
-  float* ybuf = reinterpret_cast<float*>(ws + pl.off_y);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + pl.off_cnt);
   const int nd_max = pl.P < E ? pl.P : E;
-  dec_gateup_kernel<WD, 2><<<nd_max * (I / 16), DM_THREADS, 0, st>>>(
-      reinterpret_cast<const uint16_t*>(x), ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, hbuf, cnt, H / 16,
-      H, I, E);
+  dec_gateup_kernel<WD, 4><<<nd_max * (I / 16), DM_THREADS, 0, st>>>(
+      reinterpret_cast<const uint16_t*>(x), ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, H, I,
+      E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  dec_down_kernel<WD, 2><<<nd_max * (H / 16), DM_THREADS, 0, st>>>(hbuf, ids, mask, pl.P, k, pool, d.expert_stride,
-                                                                   slot_ids, gates, ybuf, out, cnt, pl.T, H, I, E);
+  dec_down_kernel<WD, (WD == FT_BF16) ? 4 : 2><<<H / 16, DD_THREADS, 0, st>>>(hbuf, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids,
+                                                        out, pl.T, H, I, E);
   return hipGetLastError();
 }
 
@@ -418,7 +433,7 @@ bool dec_supported(const ft_moe_desc& d, int T) {
   if (d.act_dtype != FT_BF16) return false;
   if (d.w_dtype != FT_BF16 && d.w_dtype != FT_MXFP4 && d.w_dtype != FT_NVFP4) return false;
   const int64_t P = (int64_t)T * d.top_k;
-  if (P < 1 || P > DEC_MAX_PAIRS) return false;
+  if (P < 1 || P > DEC_MAX_PAIRS || T > DD_MAXT) return false;
   const int ck = (d.w_dtype == FT_BF16) ? 64 : 128;
   return d.hidden % ck == 0 && d.inter % ck == 0 && d.hidden % 16 == 0 && d.inter % 16 == 0;
 }

@@ -13,7 +13,7 @@ hipError_t launch_route(const ft_moe_desc& d, const void* x, int T, const void* 
                         int32_t* ids, float* gates, double* logits, hipStream_t st);
 constexpr int ROUTE_DECODE_MAX_T = 16;
 hipError_t launch_route_decode(const ft_moe_desc& d, const void* x, int T, const void* wr, const float* sel_bias,
-                               int32_t* ids, float* gates, double* logits, uint32_t* counter, hipStream_t st);
+                               int32_t* ids, float* gates, double* logits, hipStream_t st);
 
 // slot table
 size_t slot_table_bytes(int L, int E, int S);

@@ -66,98 +66,13 @@ __global__ void __launch_bounds__(256) route_logits_kernel(const void* __restric
   }
 }
 
-// Candidate order: a beats b if a's score is larger, or equal with lower id;
-// NaN ranks below every number.
-__device__ __forceinline__ bool beats(double a, int ea, double b, int eb) {
-  const bool na = a != a, nb = b != b;
-  if (na || nb) {
-    if (!na) return true;
-    if (!nb) return false;
-    return ea < eb;
-  }
-  return a > b || (a == b && ea < eb);
-}
-
-constexpr int MAX_E_PER_LANE = 16;  // E <= 1024
-
-// One wave per token.
-__global__ void __launch_bounds__(256) route_topk_kernel(const double* __restrict__ logits,
-                                                         const float* __restrict__ sel_bias,
-                                                         int32_t* __restrict__ ids,
-                                                         float* __restrict__ gates, int T, int E,
-                                                         int k, int renormalize) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const double* lt = logits + (int64_t)t * E;
-  double s[MAX_E_PER_LANE];
-  uint32_t taken = 0;
-  const int per = (E + 63) / 64;
-#pragma unroll
-  for (int i = 0; i < MAX_E_PER_LANE; ++i) {
-    const int e = lane + 64 * i;
-    double v = __longlong_as_double(0x7FF8000000000000LL);  // NaN = empty
-    if (i < per && e < E) {
-      v = lt[e];
-      if (sel_bias) v += (double)sel_bias[(int64_t)t * E + e];
-    } else {
-      taken |= 1u << i;
-    }
-    s[i] = v;
-  }
-  int my_id = -1;  // lane j < k ends up holding the j-th selected id
-  for (int j = 0; j < k; ++j) {
-    double best = __longlong_as_double(0x7FF8000000000000LL);
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < MAX_E_PER_LANE; ++i) {
-      if (!(taken >> i & 1u) && beats(s[i], lane + 64 * i, best, be)) {
-        best = s[i];
-        be = lane + 64 * i;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const double ob = __shfl_xor(best, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      if (beats(ob, oe, best, be)) { best = ob; be = oe; }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) my_id = be;
-  }
-  // gates in fp64
-  const bool sel = lane < k;
-  const double l = sel ? lt[my_id] : 0.0;
-  double g;
-  if (renormalize) {
-    double m = sel ? l : -__builtin_inf();
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
-    const double ex = sel ? exp(l - m) : 0.0;
-    const double den = wave_sum(ex);
-    g = ex / den;
-  } else {
-    double m = -__builtin_inf();
-    for (int e = lane; e < E; e += 64) m = fmax(m, lt[e]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
-    double part = 0.0;
-    for (int e = lane; e < E; e += 64) part += exp(lt[e] - m);
-    const double den = wave_sum(part);
-    g = sel ? exp(l - m) / den : 0.0;
-  }
-  if (sel) {
-    ids[(int64_t)t * k + lane] = my_id;
-    gates[(int64_t)t * k + lane] = (float)g;
-  }
-}
-
 // ---------------------------------------------------------------- decode --
-// One launch for few tokens: workgroup e computes the logits of expert e for
-// all T <= 16 tokens (its 4 waves split H; fp64 partial sums reduced across
-// the wave with a multi-value butterfly, then across waves in LDS, in a fixed
-// order identical for every expert).  The workgroup that finishes last (a
-// device-scope counter in the workspace, reset after use) runs the top-k.
+// Few tokens: workgroup e computes the logits of expert e for all T <= 16
+// tokens (its 4 waves split H; fp64 partial sums reduced across the wave with
+// a multi-value butterfly, then across waves in LDS, in a fixed order that is
+// the same for every expert).  A second launch of one workgroup (one wave per
+// token) runs the top-k.  Two launches rather than a last-workgroup handoff:
+// a device-scope release per workgroup costs an L2 write-back on this chip.
 constexpr int RD_MAXT = 16;
 
 // Reduce v[N] (N a power of two <= 16) over the 64 lanes; afterwards lane l
@@ -194,77 +109,137 @@ __device__ __forceinline__ uint64_t dkey(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
+// Top-k of one token's E <= 64*PER scores by one wave, without a serial
+// chain of cross-lane shuffles: a radix select over the orderable 64-bit
+// keys (one ballot per held value and bit, most significant bit first,
+// stopping as soon as the candidate set is exactly the number still needed),
+// then the k winners are ranked by (score desc, id asc) through LDS.
+// Equal scores at the boundary go to the lowest ids.  Scratch: 32 entries
+// per wave in LDS.
+struct TopkScratch {
+  uint64_t key[32];
+  double l[32];
+  double ex[32];
+  int id[32];
+};
+
 template <int PER>
 __device__ void topk_one_token(const double* __restrict__ lt, const float* __restrict__ bias_t, int E, int k,
-                               int renormalize, int32_t* __restrict__ ids_t, float* __restrict__ gates_t) {
+                               int renormalize, int32_t* __restrict__ ids_t, float* __restrict__ gates_t,
+                               TopkScratch* sc) {
   const int lane = threadIdx.x & 63;
   uint64_t key[PER];
+  double lv[PER];
+  bool cand[PER], sel[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
-    if (e < E) {
-      double v = lt[e];
-      if (bias_t) v += (double)bias_t[e];
-      key[i] = dkey(v) | 0ull;
-    } else {
-      key[i] = 0ull;
-    }
+    const bool ok = e < E;
+    lv[i] = ok ? lt[e] : 0.0;
+    double s = lv[i];
+    if (ok && bias_t) s += (double)bias_t[e];
+    key[i] = ok ? dkey(s) : 0ull;
+    cand[i] = ok;
+    sel[i] = false;
   }
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (lane + 64 * i >= E) taken |= 1u << i;
-  int my_id = -1;
-  for (int j = 0; j < k; ++j) {
-    uint64_t bk = 0ull;
-    int be = 0x7FFFFFFF;
+  int need = k;
+  for (int b = 63; b >= 0 && need > 0; --b) {
+    int n_cand = 0, c1 = 0;
+    uint64_t m1[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int e = lane + 64 * i;
-      if (!((taken >> i) & 1u) && (key[i] > bk || (key[i] == bk && e < be))) { bk = key[i]; be = e; }
+      const bool one = cand[i] && ((key[i] >> b) & 1ull);
+      m1[i] = __ballot(one);
+      c1 += __popcll(m1[i]);
+      n_cand += __popcll(__ballot(cand[i]));
     }
+    if (n_cand == need) break;  // every candidate is selected
+    const bool take_ones = c1 >= need;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const uint64_t ok = __shfl_xor(bk, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      if (ok > bk || (ok == bk && oe < be)) { bk = ok; be = oe; }
+    for (int i = 0; i < PER; ++i) {
+      const bool one = (m1[i] >> lane) & 1ull;
+      if (take_ones) {
+        cand[i] = cand[i] && one;
+      } else {
+        if (cand[i] && one) sel[i] = true;  // strictly above the threshold
+        cand[i] = cand[i] && !one;
+      }
     }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) my_id = be;
+    if (!take_ones) need -= c1;
   }
-  const bool sel = lane < k;
-  const double l = sel ? lt[my_id] : 0.0;
-  double gsel;
+  // remaining candidates share the threshold key (or fit exactly): take the
+  // `need` lowest ids, i.e. first in (i, lane) order
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint64_t m = __ballot(cand[i]);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int before = __popcll(m & below);
+    if (cand[i] && before < need) sel[i] = true;
+    need -= __popcll(m);
+    if (need < 0) need = 0;
+  }
+  // compact the winners into LDS in (i, lane) = ascending id order
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint64_t m = __ballot(sel[i]);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (sel[i]) {
+      const int pos = base + __popcll(m & below);
+      sc->key[pos] = key[i];
+      sc->l[pos] = lv[i];
+      sc->id[pos] = lane + 64 * i;
+    }
+    base += __popcll(m);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  const bool mine = lane < k;
+  uint64_t kk = 0ull;
+  int id = 0;
+  double l = 0.0;
+  int rank = 0;
+  if (mine) {
+    kk = sc->key[lane];
+    id = sc->id[lane];
+    l = sc->l[lane];
+    for (int m = 0; m < k; ++m) {
+      const uint64_t km = sc->key[m];
+      rank += (km > kk || (km == kk && sc->id[m] < id)) ? 1 : 0;
+    }
+  }
+  double g = 0.0;
   if (renormalize) {
-    double m = sel ? l : -__builtin_inf();
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
-    const double ex = sel ? exp(l - m) : 0.0;
-    gsel = ex / wave_sum(ex);
+    double mx = -__builtin_inf();
+    for (int m = 0; m < k; ++m) mx = fmax(mx, sc->l[m]);
+    const double ex = mine ? exp(l - mx) : 0.0;
+    if (mine) sc->ex[lane] = ex;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    double den = 0.0;
+    for (int m = 0; m < k; ++m) den += sc->ex[m];
+    g = ex / den;
   } else {
-    double m = -__builtin_inf();
-    for (int e = lane; e < E; e += 64) m = fmax(m, lt[e]);
+    double mx = -__builtin_inf();
+    for (int e = lane; e < E; e += 64) mx = fmax(mx, lt[e]);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
+    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
     double part = 0.0;
-    for (int e = lane; e < E; e += 64) part += exp(lt[e] - m);
+    for (int e = lane; e < E; e += 64) part += exp(lt[e] - mx);
     const double den = wave_sum(part);
-    gsel = sel ? exp(l - m) / den : 0.0;
+    g = mine ? exp(l - mx) / den : 0.0;
   }
-  if (sel) {
-    ids_t[lane] = my_id;
-    gates_t[lane] = (float)gsel;
+  if (mine) {
+    ids_t[rank] = id;
+    gates_t[rank] = (float)g;
   }
 }
 
 template <int XDT, int WDT, int NT>
 __global__ void __launch_bounds__(256) route_decode_kernel(const void* __restrict__ x, const void* __restrict__ wr,
                                                            const float* __restrict__ sel_bias,
-                                                           double* __restrict__ logits, int32_t* __restrict__ ids,
-                                                           float* __restrict__ gates, uint32_t* __restrict__ counter,
-                                                           int T, int H, int E, int k, int renormalize) {
+                                                           double* __restrict__ logits, int T, int H, int E) {
   __shared__ double part[4][RD_MAXT];
-  __shared__ int last;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int e = blockIdx.x;
   double acc[NT];
@@ -292,47 +267,46 @@ __global__ void __launch_bounds__(256) route_decode_kernel(const void* __restric
     const int t = threadIdx.x;
     logits[(int64_t)t * E + e] = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) last = (atomicAdd(counter, 1u) == (uint32_t)(gridDim.x - 1));
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  for (int t = wv; t < T; t += 4) {
-    const double* lt = logits + (int64_t)t * E;
-    const float* bt = sel_bias ? sel_bias + (int64_t)t * E : nullptr;
-    if (E <= 64) topk_one_token<1>(lt, bt, E, k, renormalize, ids + (int64_t)t * k, gates + (int64_t)t * k);
-    else if (E <= 128) topk_one_token<2>(lt, bt, E, k, renormalize, ids + (int64_t)t * k, gates + (int64_t)t * k);
-    else if (E <= 256) topk_one_token<4>(lt, bt, E, k, renormalize, ids + (int64_t)t * k, gates + (int64_t)t * k);
-    else if (E <= 512) topk_one_token<8>(lt, bt, E, k, renormalize, ids + (int64_t)t * k, gates + (int64_t)t * k);
-    else topk_one_token<16>(lt, bt, E, k, renormalize, ids + (int64_t)t * k, gates + (int64_t)t * k);
-  }
-  if (threadIdx.x == 0) *counter = 0u;
+}
+
+// One wave per token, PER = ceil(E / 64) logits per lane.
+template <int PER>
+__global__ void __launch_bounds__(1024) route_topk_decode_kernel(const double* __restrict__ logits,
+                                                                 const float* __restrict__ sel_bias,
+                                                                 int32_t* __restrict__ ids, float* __restrict__ gates,
+                                                                 int T, int E, int k, int renormalize) {
+  __shared__ TopkScratch sc[16];
+  const int w = threadIdx.x >> 6;
+  const int t = blockIdx.x * (blockDim.x >> 6) + w;
+  if (t >= T) return;
+  topk_one_token<PER>(logits + (int64_t)t * E, sel_bias ? sel_bias + (int64_t)t * E : nullptr, E, k, renormalize,
+                      ids + (int64_t)t * k, gates + (int64_t)t * k, &sc[w]);
 }
 
 template <int XDT, int WDT>
 static void launch_route_decode_t(const ft_moe_desc& d, const void* x, int T, const void* wr, const float* sel_bias,
-                                  int32_t* ids, float* gates, double* logits, uint32_t* counter, hipStream_t st) {
+                                  int32_t* ids, float* gates, double* logits, hipStream_t st) {
   const int H = d.hidden, E = d.n_experts, k = d.top_k, rn = d.renormalize;
-  if (T <= 1)
-    route_decode_kernel<XDT, WDT, 1><<<E, 256, 0, st>>>(x, wr, sel_bias, logits, ids, gates, counter, T, H, E, k, rn);
-  else if (T <= 2)
-    route_decode_kernel<XDT, WDT, 2><<<E, 256, 0, st>>>(x, wr, sel_bias, logits, ids, gates, counter, T, H, E, k, rn);
-  else if (T <= 4)
-    route_decode_kernel<XDT, WDT, 4><<<E, 256, 0, st>>>(x, wr, sel_bias, logits, ids, gates, counter, T, H, E, k, rn);
-  else if (T <= 8)
-    route_decode_kernel<XDT, WDT, 8><<<E, 256, 0, st>>>(x, wr, sel_bias, logits, ids, gates, counter, T, H, E, k, rn);
-  else
-    route_decode_kernel<XDT, WDT, 16><<<E, 256, 0, st>>>(x, wr, sel_bias, logits, ids, gates, counter, T, H, E, k, rn);
+  if (T <= 1) route_decode_kernel<XDT, WDT, 1><<<E, 256, 0, st>>>(x, wr, sel_bias, logits, T, H, E);
+  else if (T <= 2) route_decode_kernel<XDT, WDT, 2><<<E, 256, 0, st>>>(x, wr, sel_bias, logits, T, H, E);
+  else if (T <= 4) route_decode_kernel<XDT, WDT, 4><<<E, 256, 0, st>>>(x, wr, sel_bias, logits, T, H, E);
+  else if (T <= 8) route_decode_kernel<XDT, WDT, 8><<<E, 256, 0, st>>>(x, wr, sel_bias, logits, T, H, E);
+  else route_decode_kernel<XDT, WDT, 16><<<E, 256, 0, st>>>(x, wr, sel_bias, logits, T, H, E);
+  const int threads = 64 * T;
+  if (E <= 64) route_topk_decode_kernel<1><<<1, threads, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);
+  else if (E <= 128) route_topk_decode_kernel<2><<<1, threads, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);
+  else if (E <= 256) route_topk_decode_kernel<4><<<1, threads, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);
+  else if (E <= 512) route_topk_decode_kernel<8><<<1, threads, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);
+  else route_topk_decode_kernel<16><<<1, threads, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);
 }
 
 hipError_t launch_route_decode(const ft_moe_desc& d, const void* x, int T, const void* wr, const float* sel_bias,
-                               int32_t* ids, float* gates, double* logits, uint32_t* counter, hipStream_t st) {
+                               int32_t* ids, float* gates, double* logits, hipStream_t st) {
   const int xd = d.act_dtype, wd = d.router_dtype;
-  if (xd == FT_BF16 && wd == FT_BF16) launch_route_decode_t<FT_BF16, FT_BF16>(d, x, T, wr, sel_bias, ids, gates, logits, counter, st);
-  else if (xd == FT_F32 && wd == FT_F32) launch_route_decode_t<FT_F32, FT_F32>(d, x, T, wr, sel_bias, ids, gates, logits, counter, st);
-  else if (xd == FT_BF16 && wd == FT_F32) launch_route_decode_t<FT_BF16, FT_F32>(d, x, T, wr, sel_bias, ids, gates, logits, counter, st);
-  else launch_route_decode_t<FT_F32, FT_BF16>(d, x, T, wr, sel_bias, ids, gates, logits, counter, st);
+  if (xd == FT_BF16 && wd == FT_BF16) launch_route_decode_t<FT_BF16, FT_BF16>(d, x, T, wr, sel_bias, ids, gates, logits, st);
+  else if (xd == FT_F32 && wd == FT_F32) launch_route_decode_t<FT_F32, FT_F32>(d, x, T, wr, sel_bias, ids, gates, logits, st);
+  else if (xd == FT_BF16 && wd == FT_F32) launch_route_decode_t<FT_BF16, FT_F32>(d, x, T, wr, sel_bias, ids, gates, logits, st);
+  else launch_route_decode_t<FT_F32, FT_BF16>(d, x, T, wr, sel_bias, ids, gates, logits, st);
   return hipGetLastError();
 }
 
@@ -352,8 +326,13 @@ hipError_t launch_route(const ft_moe_desc& d, const void* x, int T, const void* 
     route_logits_kernel<FT_F32, FT_BF16, RT><<<grid, 256, 0, st>>>(x, wr, logits, T, d.hidden, d.n_experts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  route_topk_kernel<<<(T + 3) / 4, 256, 0, st>>>(logits, sel_bias, ids, gates, T, d.n_experts,
-                                                 d.top_k, d.renormalize);
+  const int E = d.n_experts, k = d.top_k, rn = d.renormalize;
+  const int nb = (T + 3) / 4;
+  if (E <= 64) route_topk_decode_kernel<1><<<nb, 256, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);
+  else if (E <= 128) route_topk_decode_kernel<2><<<nb, 256, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);
+  else if (E <= 256) route_topk_decode_kernel<4><<<nb, 256, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);
+  else if (E <= 512) route_topk_decode_kernel<8><<<nb, 256, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);
+  else route_topk_decode_kernel<16><<<nb, 256, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);
   return hipGetLastError();
 }
 

@@ -58,8 +58,9 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T) {
   p.I = d.inter;
   p.nb = (p.P + PERM_CHUNK - 1) / PERM_CHUNK;
   if (p.nb < 1) p.nb = 1;
-  p.mfma = false;
-  p.path = dec_supported(d, T) ? PATH_DEC : PATH_GEMV;
+  p.mfma = mfma_supported(d, T);
+  p.path = p.mfma ? PATH_MFMA : (dec_supported(d, T) ? PATH_DEC : PATH_GEMV);
+  p.max_tiles = p.P / 64 + p.E + 1;
   size_t o = 0;
   p.off_hist = o;    o = align256(o + sizeof(int32_t) * (size_t)p.nb * p.E);
   p.off_offsets = o; o = align256(o + sizeof(int32_t) * (size_t)(p.E + 2));
@@ -67,9 +68,16 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T) {
   p.off_perm = o;    o = align256(o + sizeof(int32_t) * (size_t)p.P);
   p.off_pos = o;     o = align256(o + sizeof(int32_t) * (size_t)p.P);
   p.off_cnt = o;     o = align256(o + sizeof(uint32_t) * (size_t)(p.H / 16 + 1));
-  p.off_h = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.I);   // fp32 h, or bf16 hi/lo pairs
+  p.off_h = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.I);   // fp32 h, bf16 hi/lo, or MXFP8 codes
   p.off_y = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.H);
-  p.off_xq = p.off_xs = p.off_hs = o;
+  if (p.mfma) {
+    p.off_xq = o;    o = align256(o + (size_t)T * p.H);                     // MXFP8 x codes
+    p.off_xs = o;    o = align256(o + (size_t)T * p.H / 32);                // and scales
+    p.off_hs = o;    o = align256(o + (size_t)p.P * p.I / 32);              // h scales
+    p.off_tiles = o; o = align256(o + sizeof(int32_t) * (size_t)(2 * p.max_tiles + 1));
+  } else {
+    p.off_xq = p.off_xs = p.off_hs = p.off_tiles = o;
+  }
   p.bytes = o;
   return p;
 }

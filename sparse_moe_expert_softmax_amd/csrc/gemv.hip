@@ -246,6 +246,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   *reinterpret_cast<float4*>(out + (int64_t)t * H + h) = acc;
 }
 
+hipError_t launch_combine(const FwdPlan& pl, const int32_t* pos, const float* gates, float* out, char* ws,
+                          hipStream_t st) {
+  const float* ybuf = reinterpret_cast<const float*>(ws + pl.off_y);
+  dim3 cg((pl.H / 4 + 255) / 256, pl.T);
+  combine_kernel<<<cg, 256, 0, st>>>(ybuf, pos, gates, out, pl.T, pl.H, pl.P / pl.T);
+  return hipGetLastError();
+}
+
 template <int WD>
 static hipError_t gemv_forward_t(const ft_moe_desc& d, const FwdPlan& pl, const void* x, const int32_t* slot_ids,
                                  const void* pool, const float* gates, float* out, char* ws, hipStream_t st) {

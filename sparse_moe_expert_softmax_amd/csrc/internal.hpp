@@ -33,6 +33,8 @@ struct FwdPlan {
   int path;                    // FwdPath
   bool mfma;                   // large-batch MXFP4 path on scaled MFMA
   size_t off_hist, off_offsets, off_active, off_perm, off_pos, off_h, off_y, off_xq, off_xs, off_hs, off_cnt;
+  size_t off_tiles;            // MFMA path: tile list (2 ints per tile) + count
+  int max_tiles;               // upper bound of (expert, 64-row) tiles: P/64 + E
   size_t bytes;
 };
 typedef FwdPlan DecPlan;
@@ -53,6 +55,10 @@ hipError_t launch_gemv_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
                                const void* pool, const float* gates, float* out, char* ws, hipStream_t st);
 
 // large-batch MXFP4 path on gfx950 scaled MFMA
+constexpr int MFMA_MIN_TOKENS = 256;
+bool mfma_supported(const ft_moe_desc& d, int T);
+hipError_t launch_combine(const FwdPlan& pl, const int32_t* pos, const float* gates, float* out, char* ws,
+                          hipStream_t st);
 hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const void* x, const int32_t* slot_ids,
                                const void* pool, const float* gates, float* out, char* ws, hipStream_t st);
 

@@ -33,39 +33,6 @@ __device__ __forceinline__ void load8_f64(const void* base, int64_t i, double (&
   }
 }
 
-// One wave per (expert, tile of RT tokens); lanes stride over H, 8 elements each.
-template <int XDT, int WDT, int RT>
-__global__ void __launch_bounds__(256) route_logits_kernel(const void* __restrict__ x,
-                                                           const void* __restrict__ wr,
-                                                           double* __restrict__ logits, int T, int H,
-                                                           int E) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int t0 = blockIdx.y * RT;
-  if (e >= E) return;
-  double acc[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) acc[r] = 0.0;
-  for (int h = lane * 8; h < H; h += 64 * 8) {
-    double w[8];
-    load8_f64<WDT>(wr, (int64_t)e * H + h, w);
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      if (t0 + r < T) {
-        double xv[8];
-        load8_f64<XDT>(x, (int64_t)(t0 + r) * H + h, xv);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[r] = fma(xv[j], w[j], acc[r]);
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const double s = wave_sum(acc[r]);
-    if (lane == 0 && t0 + r < T) logits[(int64_t)(t0 + r) * E + e] = s;
-  }
-}
-
 // ---------------------------------------------------------------- decode --
 // Few tokens: workgroup e computes the logits of expert e for all T <= 16
 // tokens (its 4 waves split H; fp64 partial sums reduced across the wave with
@@ -310,23 +277,96 @@ hipError_t launch_route_decode(const ft_moe_desc& d, const void* x, int T, const
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- prefill --
+// Many tokens: logits as a tiled fp64 GEMM.  A workgroup computes 128 tokens
+// x 64 experts; each thread holds 8 x 4 fp64 accumulators; K advances 16 per
+// step through double-buffered LDS holding the operands already widened to
+// fp64 (exact).  Each accumulator adds its products in ascending h order, the
+// same order for every expert.
+constexpr int RL_TT = 128, RL_TE = 64, RL_KB = 16;
+
+template <int XDT, int WDT>
+__global__ void __launch_bounds__(256) route_logits_tiled_kernel(const void* __restrict__ x, const void* __restrict__ wr,
+                                                                 double* __restrict__ logits, int T, int H, int E) {
+  __shared__ double xs[2][RL_KB][RL_TT];
+  __shared__ double wsm[2][RL_KB][RL_TE];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * RL_TT, e0 = blockIdx.y * RL_TE;
+  const int ty = tid / 16, tx = tid % 16;  // thread owns tokens ty*8.. and experts tx*4..
+  double acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  // loaders: x: token tid/2, 8 consecutive k at (tid%2)*8; w: threads < 128: expert tid/2, same k split
+  const int xt = t0 + tid / 2, xk = (tid % 2) * 8;
+  const int we = e0 + tid / 2;
+  double lx[8], lw[8];
+  auto gload = [&](int kb) {
+    if (xt < T) load8_f64<XDT>(x, (int64_t)xt * H + kb + xk, lx);
+    else for (int j = 0; j < 8; ++j) lx[j] = 0.0;
+    if (tid < 128) {
+      if (we < E) load8_f64<WDT>(wr, (int64_t)we * H + kb + xk, lw);
+      else for (int j = 0; j < 8; ++j) lw[j] = 0.0;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xs[buf][xk + j][tid / 2] = lx[j];
+    if (tid < 128)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wsm[buf][xk + j][tid / 2] = lw[j];
+  };
+  const int nk = H / RL_KB;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nk) gload((s + 1) * RL_KB);
+#pragma unroll 2
+    for (int kk = 0; kk < RL_KB; ++kk) {
+      double a[8], b[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = xs[cur][kk][ty * 8 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = wsm[cur][kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+    }
+    if (s + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = t0 + ty * 8 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) logits[(int64_t)t * E + e] = acc[i][j];
+    }
+  }
+}
+
 hipError_t launch_route(const ft_moe_desc& d, const void* x, int T, const void* wr,
                         const float* sel_bias, int32_t* ids, float* gates, double* logits,
                         hipStream_t st) {
-  constexpr int RT = 4;
-  dim3 grid((d.n_experts + 3) / 4, (T + RT - 1) / RT);
-  const int xd = d.act_dtype, wd = d.router_dtype;
+  dim3 grid((T + RL_TT - 1) / RL_TT, (d.n_experts + RL_TE - 1) / RL_TE);
+  const int xd = d.act_dtype, wd = d.router_dtype, H = d.hidden, E = d.n_experts;
   if (xd == FT_BF16 && wd == FT_BF16)
-    route_logits_kernel<FT_BF16, FT_BF16, RT><<<grid, 256, 0, st>>>(x, wr, logits, T, d.hidden, d.n_experts);
+    route_logits_tiled_kernel<FT_BF16, FT_BF16><<<grid, 256, 0, st>>>(x, wr, logits, T, H, E);
   else if (xd == FT_F32 && wd == FT_F32)
-    route_logits_kernel<FT_F32, FT_F32, RT><<<grid, 256, 0, st>>>(x, wr, logits, T, d.hidden, d.n_experts);
+    route_logits_tiled_kernel<FT_F32, FT_F32><<<grid, 256, 0, st>>>(x, wr, logits, T, H, E);
   else if (xd == FT_BF16 && wd == FT_F32)
-    route_logits_kernel<FT_BF16, FT_F32, RT><<<grid, 256, 0, st>>>(x, wr, logits, T, d.hidden, d.n_experts);
+    route_logits_tiled_kernel<FT_BF16, FT_F32><<<grid, 256, 0, st>>>(x, wr, logits, T, H, E);
   else
-    route_logits_kernel<FT_F32, FT_BF16, RT><<<grid, 256, 0, st>>>(x, wr, logits, T, d.hidden, d.n_experts);
+    route_logits_tiled_kernel<FT_F32, FT_BF16><<<grid, 256, 0, st>>>(x, wr, logits, T, H, E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int E = d.n_experts, k = d.top_k, rn = d.renormalize;
+  const int k = d.top_k, rn = d.renormalize;
   const int nb = (T + 3) / 4;
   if (E <= 64) route_topk_decode_kernel<1><<<nb, 256, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);
   else if (E <= 128) route_topk_decode_kernel<2><<<nb, 256, 0, st>>>(logits, sel_bias, ids, gates, T, E, k, rn);

@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of HIP-graph replay")
     ap.add_argument("--graphs", type=int, default=16, help="distinct captured steps (distinct inputs) replayed in turn")
+    ap.add_argument("--tokens", type=int, default=8192, help="prefill: prompt tokens (multiples of 8192 run as chunks)")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
+    ap.add_argument("--host-layers", type=int, default=2, help="distinct pinned host layer images (aliased)")
     return ap.parse_args()
 
 
@@ -112,10 +115,16 @@ def main():
     from sparse_moe_expert_softmax_amd.configs import CONFIGS
 
     cfg = CONFIGS[args.workload]
-    if cfg.name != "decode_bf16_h2048_e128":
-        print(json.dumps({"error": f"workload {cfg.name} is run by bench_workloads.py"}))
-        sys.exit(2)
     torch.cuda.set_device(0)
+    if cfg.name == "prefill_mxfp4_h4096_e256":
+        return run_prefill(args, cfg, torch)
+    if cfg.name == "decode_mxfp4_h4096_e256_lru":
+        return run_decode_lru(args, cfg, torch)
+    if cfg.name == "decode_nvfp4_h6144_e256":
+        return run_decode_resident_fp4(args, cfg, torch)
+    if cfg.name != "decode_bf16_h2048_e128":
+        print(json.dumps({"error": f"no benchmark for workload {cfg.name}"}))
+        sys.exit(2)
     B, L, E, H, I, k = args.batch, cfg.n_layers, cfg.n_experts, cfg.hidden, cfg.inter, cfg.top_k
     stride = synth.record_stride(H, I, cfg.w_dtype)
     rec_bytes = synth.record_bytes(H, I, cfg.w_dtype)
@@ -238,6 +247,369 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, B, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+MFMA_PEAK_TFLOPS = 5000.0   # dense fp8 rate; the f8 x f4 instruction issues at the fp8 rate
+
+
+def _base_result(args, metric_value, unit, ms_per_step, config, dtype):
+    return {"metric": "moe_layer_tokens_per_s", "value": round(metric_value, 1), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic", "config": config}
+
+
+def _fp4_layer_pool(cfg, layer, torch, stride):
+    from sparse_moe_expert_softmax_amd import synth
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.ENTROPY * 1000 + cfg.cid * 100 + layer)
+    pool = torch.empty((cfg.n_experts, stride), dtype=torch.uint8, device="cuda")
+    for e in range(cfg.n_experts):
+        pool[e].copy_(synth.device_record_fp4(torch, g, cfg.hidden, cfg.inter, cfg.weight_std, cfg.w_dtype, stride))
+    return pool
+
+
+def run_prefill(args, cfg, torch):
+    """8,192-token chunks through the MXFP4 layers: compute with weights
+    resident, then the full pipeline where the next layer's whole expert set
+    is copied from pinned host memory on a side stream while the current
+    layer computes (two HBM layer buffers)."""
+    from sparse_moe_expert_softmax_amd import ftmoe, synth
+    CH = 8192
+    T = CH
+    chunks = max(1, args.tokens // CH)
+    L = args.layers or cfg.n_layers
+    H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
+    stride = synth.record_stride(H, I, cfg.w_dtype)
+    rec = synth.record_bytes(H, I, cfg.w_dtype)
+    layer_bytes = E * stride
+    desc = ftmoe.make_desc(cfg, stride)
+    NH = max(1, min(args.host_layers, L))
+    print(f"[bench] prefill: {L} layers, {chunks} chunk(s) of {CH}; {NH} pinned host layer images "
+          f"of {layer_bytes / 1e9:.2f} GB", file=sys.stderr, flush=True)
+    host = []
+    for h in range(NH):
+        dev = _fp4_layer_pool(cfg, h, torch, stride)
+        hb = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
+        hb.copy_(dev)
+        host.append(hb)
+        del dev
+    torch.cuda.synchronize()
+    bufs = [torch.empty((E, stride), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for b in range(2):
+        bufs[b].copy_(host[b % NH])
+    routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(L)]
+    xs = [torch.from_numpy(synth.activations(cfg, c, 0, CH).view(np.int16)).cuda() for c in range(chunks)]
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ftmoe.ft_moe_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+    rws = torch.zeros(ftmoe.ft_route_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+    comp = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    EV = lambda: torch.cuda.Event(enable_timing=True)
+
+    # ---- compute only, weights resident (alternating the two layer buffers)
+    route_ms, fwd_ms = [], []
+    n_warm, n_meas = max(2, args.warmup // 10), max(4, min(args.steps, L))
+    for it in range(n_warm + n_meas):
+        l = it % L
+        e0, e1, e2 = EV(), EV(), EV()
+        e0.record(comp)
+        ftmoe.ft_moe_route(desc, xs[0], routers[l], ids, gates, workspace=rws, stream=comp)
+        e1.record(comp)
+        ftmoe.ft_moe_forward(desc, xs[0], ids, gates, bufs[it % 2], out, ws, stream=comp)
+        e2.record(comp)
+        if it >= n_warm:
+            torch.cuda.synchronize()
+            route_ms.append(e0.elapsed_time(e1))
+            fwd_ms.append(e1.elapsed_time(e2))
+    route_ms, fwd_ms = np.array(route_ms), np.array(fwd_ms)
+    t_layer = float(np.mean(route_ms + fwd_ms))
+    print(f"[bench] resident: route {route_ms.mean():.3f} ms, forward {fwd_ms.mean():.3f} ms per layer",
+          file=sys.stderr, flush=True)
+
+    # ---- full pipeline: next layer's experts uploaded while this layer computes
+    recs_ptr = [[host[h][e].data_ptr() for e in range(E)] for h in range(NH)]
+    ready = [EV() for _ in range(L * chunks + 1)]
+    free = [EV() for _ in range(2)]
+    copy_ev = []
+    torch.cuda.synchronize()
+    w0, w1 = EV(), EV()
+    w0.record(comp)
+    # layer 0 of chunk 0 is uploaded before the clock as part of the pipeline fill
+    side.wait_stream(comp)
+    c0 = EV(); c0.record(side)
+    ftmoe.ft_expert_upload(bufs[0], stride, rec, list(range(E)), recs_ptr[0], stream=side, done_event=ready[0])
+    c1 = EV(); c1.record(side)
+    copy_ev.append((c0, c1))
+    n = 0
+    for c in range(chunks):
+        for l in range(L):
+            cur = n % 2
+            if n + 1 < L * chunks:  # start the next layer's upload into the other buffer
+                nl = (n + 1) % L
+                if n >= 1:
+                    side.wait_event(free[(n + 1) % 2])
+                a, b = EV(), EV()
+                a.record(side)
+                ftmoe.ft_expert_upload(bufs[(n + 1) % 2], stride, rec, list(range(E)), recs_ptr[nl % NH],
+                                       stream=side, done_event=ready[n + 1])
+                b.record(side)
+                copy_ev.append((a, b))
+            comp.wait_event(ready[n])
+            ftmoe.ft_moe_route(desc, xs[c], routers[l], ids, gates, workspace=rws, stream=comp)
+            ftmoe.ft_moe_forward(desc, xs[c], ids, gates, bufs[cur], out, ws, stream=comp)
+            free[cur].record(comp)
+            n += 1
+    w1.record(comp)
+    torch.cuda.synchronize()
+    wall_ms = w0.elapsed_time(w1)
+    copy_ms = float(sum(a.elapsed_time(b) for a, b in copy_ev))
+    comp_ms = t_layer * L * chunks
+    upload_gbs = len(copy_ev) * E * rec / (copy_ms * 1e-3) / 1e9
+
+    useful = 6.0 * T * k * H * I  # gate/up 4*P*H*I + down 2*P*H*I
+    tflops = useful / (float(np.mean(fwd_ms)) * 1e-3) / 1e12
+    res = _base_result(args, T / (t_layer * 1e-3), "tokens/s", t_layer * L,
+                       {"workload": cfg.name, "tokens_per_chunk": CH, "chunks": chunks, "layers": L, "hidden": H,
+                        "experts": E, "top_k": k, "inter": I, "weights": "mxfp4",
+                        "activations": "bf16, quantised to mxfp8 for the matrix cores"}, "f8xf4 (f32 accumulate)")
+    res["note"] = "value = tokens/s through one MoE layer with its experts resident (route + forward)"
+    res["per_layer_ms"] = {"route": round(float(route_ms.mean()), 4), "forward": round(float(fwd_ms.mean()), 4)}
+    res["pipeline"] = {"wall_ms": round(wall_ms, 2), "upload_ms_sum": round(copy_ms, 2),
+                       "compute_ms_sum": round(comp_ms, 2),
+                       "overlap_efficiency": round(max(copy_ms, comp_ms) / wall_ms, 4),
+                       "host_link_gbs": round(upload_gbs, 2),
+                       "tokens_per_s_end_to_end": round(T * chunks / (wall_ms * 1e-3), 1),
+                       "host_layer_images": NH}
+    res["roofline"] = {"bound": "mfma", "kernel": "ft_moe_forward (grouped scaled-MFMA expert GEMM)",
+                       "achieved": round(tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                       "flops_per_launch": useful, "avg_launch_us": round(float(np.mean(fwd_ms)) * 1e3, 1)}
+    print(json.dumps(res), flush=True)
+
+
+def run_decode_resident_fp4(args, cfg, torch):
+    """NVFP4-like decode, layers resident, batch 4, with the partition masks:
+    every layer call also runs the forward on a random half of the experts and
+    on the other half, and the two partial outputs must sum to the full one."""
+    from sparse_moe_expert_softmax_amd import ftmoe, synth
+    L = args.layers or cfg.n_layers
+    B = cfg.batches[0] if args.batch == 1 else args.batch
+    H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
+    stride = synth.record_stride(H, I, cfg.w_dtype)
+    rec = synth.record_bytes(H, I, cfg.w_dtype)
+    desc = ftmoe.make_desc(cfg, stride)
+    print(f"[bench] generating {L} NVFP4 layers ({L * E * stride / 1e9:.1f} GB) on the device", file=sys.stderr,
+          flush=True)
+    pools = [_fp4_layer_pool(cfg, l, torch, stride) for l in range(L)]
+    routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(L)]
+    n_steps = args.warmup + args.steps
+    xs = torch.stack([torch.stack([torch.from_numpy(synth.activations(cfg, s, l, B).view(np.int16))
+                                   for l in range(L)]) for s in range(n_steps)]).cuda()
+    masks = [torch.from_numpy(synth.partition_masks(cfg, l).view(np.int32)).cuda() for l in range(L)]
+    ids = torch.empty((n_steps, L, B, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((n_steps, L, B, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((L, B, H), dtype=torch.float32, device="cuda")
+    pa = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    pb = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ftmoe.ft_moe_workspace_bytes(desc, B), dtype=torch.uint8, device="cuda")
+    rws = torch.zeros(ftmoe.ft_route_workspace_bytes(desc, B), dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def step(s, ev=None):
+        for l in range(L):
+            ftmoe.ft_moe_route(desc, xs[s, l], routers[l], ids[s, l], gates[s, l], workspace=rws, stream=st)
+            if ev is not None:
+                ev[l][0].record(st)
+            ftmoe.ft_moe_forward(desc, xs[s, l], ids[s, l], gates[s, l], pools[l], out[l], ws, stream=st)
+            if ev is not None:
+                ev[l][1].record(st)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(2_000_000)
+    t0.record(st)
+    for s in range(args.warmup, n_steps):
+        step(s)
+    t1.record(st)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    fwd_ms = []
+    for s in range(args.warmup, min(n_steps, args.warmup + 20)):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+        torch.cuda._sleep(2_000_000)
+        step(s, ev)
+        torch.cuda.synchronize()
+        fwd_ms.extend(a.elapsed_time(b) for a, b in ev)
+    # partition masks: part(mask) + part(~mask) == full, on the last step
+    worst = 0.0
+    s = n_steps - 1
+    for l in range(L):
+        ftmoe.ft_moe_forward(desc, xs[s, l], ids[s, l], gates[s, l], pools[l], out[l], ws, stream=st)
+        full = out[l].clone()
+        for m in masks[l]:
+            comp_m = (~m).contiguous()
+            ftmoe.ft_moe_forward(desc, xs[s, l], ids[s, l], gates[s, l], pools[l], pa, ws, expert_mask=m, stream=st)
+            ftmoe.ft_moe_forward(desc, xs[s, l], ids[s, l], gates[s, l], pools[l], pb, ws, expert_mask=comp_m,
+                                 stream=st)
+            worst = max(worst, float(((pa + pb) - full).abs().max() / full.abs().max()))
+    ids_np = ids.cpu().numpy()
+    distinct = np.array([[len(np.unique(ids_np[s_, l])) for l in range(L)]
+                         for s_ in range(args.warmup, min(n_steps, args.warmup + 20))]).ravel()
+    fwd_bytes = distinct * rec + B * H * 2 + B * H * 4
+    gbs = float(np.mean(fwd_bytes) / (np.mean(fwd_ms) * 1e-3) / 1e9)
+    res = _base_result(args, B * L / (ms_per_step * 1e-3), "tokens/s", ms_per_step,
+                       {"workload": cfg.name, "batch": B, "layers": L, "hidden": H, "experts": E, "top_k": k,
+                        "inter": I, "weights": "nvfp4-like (e2m1, e4m3 per 16, fp32 per tensor)",
+                        "resident_gb": round(L * E * stride / 1e9, 1), "launch": "eager"}, "bf16")
+    res["partition_masks"] = {"masks_per_layer": int(masks[0].shape[0]), "max_rel_err_sum_vs_full": worst}
+    res["roofline"] = {"bound": "hbm", "kernel": "ft_moe_forward (expert GEMV)", "achieved": round(gbs, 1),
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                       "bytes_per_launch": round(float(np.mean(fwd_bytes))),
+                       "avg_launch_us": round(float(np.mean(fwd_ms)) * 1e3, 2),
+                       "distinct_experts_per_call": round(float(np.mean(distinct)), 2)}
+    print(json.dumps(res), flush=True)
+
+
+def run_decode_lru(args, cfg, torch):
+    """MXFP4 decode through the global LRU slot pool, routing driven by the
+    seeded Zipf trace (selection bias), cold start; misses are uploaded from
+    pinned host memory on a side stream before the layer's forward."""
+    from sparse_moe_expert_softmax_amd import ftmoe, synth
+    L = args.layers or cfg.n_layers
+    B = args.batch
+    H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
+    S = int(cfg.pool_fraction * E * L)
+    stride = synth.record_stride(H, I, cfg.w_dtype)
+    rec = synth.record_bytes(H, I, cfg.w_dtype)
+    desc = ftmoe.make_desc(cfg, stride)
+    NH = max(1, min(args.host_layers, L))
+    n_steps = min(cfg.trace_steps, args.warmup + args.steps)
+    print(f"[bench] LRU decode: {L} layers, pool {S} slots ({S * stride / 1e9:.1f} GB), {NH} pinned host layer "
+          f"images, {n_steps} trace steps at batch {B}", file=sys.stderr, flush=True)
+    host = []
+    for h in range(NH):
+        dev = _fp4_layer_pool(cfg, h, torch, stride)
+        hb = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
+        hb.copy_(dev)
+        host.append(hb)
+        del dev
+    host_ptr = [[host[h][e].data_ptr() for e in range(E)] for h in range(NH)]
+    pool = torch.empty((S, stride), dtype=torch.uint8, device="cuda")
+    table = torch.zeros(ftmoe.ft_slot_table_bytes(L, E, S), dtype=torch.uint8, device="cuda")
+    ftmoe.ft_slot_table_init(table, L, E, S)
+    trace = synth.zipf_trace(cfg, n_steps=n_steps)
+    routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(L)]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.ENTROPY + 3)
+    ids = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((B, k), dtype=torch.float32, device="cuda")
+    slots = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    flags = torch.empty((B, k), dtype=torch.uint8, device="cuda")
+    mlist = torch.empty(2 * B * k + 1, dtype=torch.int32, device="cuda")  # [n_miss, (e, slot)...]
+    h_mlist = torch.empty(2 * B * k + 1, dtype=torch.int32, pin_memory=True)
+    bias = torch.zeros((B, E), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ftmoe.ft_moe_workspace_bytes(desc, B), dtype=torch.uint8, device="cuda")
+    rws = torch.zeros(ftmoe.ft_route_workspace_bytes(desc, B), dtype=torch.uint8, device="cuda")
+    comp = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    trace_dev = torch.from_numpy(trace[:, :, :B, :].astype(np.int64)).cuda()
+    EV = lambda: torch.cuda.Event(enable_timing=True)
+    misses, step_ms, fwd_ms, up_ev = [], [], [], []
+    import time as _t
+    xs = torch.randn((64, B, H), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    for s_ in range(n_steps):
+        t_s = _t.perf_counter()
+        for l in range(L):
+            x = xs[(s_ * L + l) % 64]
+            bias.zero_()
+            bias.scatter_(1, trace_dev[s_, l], 30.0)
+            ftmoe.ft_moe_route(desc, x, routers[l], ids, gates, sel_bias=bias, workspace=rws, stream=comp)
+            ftmoe.ft_slot_lookup(table, l, ids, slots, flags, mlist[1:], mlist[:1], stream=comp)
+            h_mlist.copy_(mlist, non_blocking=True)
+            comp.synchronize()
+            nm = int(h_mlist[0])
+            if nm < 0:
+                raise RuntimeError("slot pool exhausted")
+            if nm:
+                pairs = h_mlist[1:1 + 2 * nm].tolist()
+                es, ss = pairs[0::2], pairs[1::2]
+                a, b, done = EV(), EV(), torch.cuda.Event()
+                a.record(side)
+                ftmoe.ft_expert_upload(pool, stride, rec, ss, [host_ptr[l % NH][e] for e in es], stream=side,
+                                       done_event=done)
+                b.record(side)
+                comp.wait_event(done)
+                if s_ >= args.warmup:
+                    up_ev.append((a, b, nm))
+            e0, e1 = EV(), EV()
+            e0.record(comp)
+            ftmoe.ft_moe_forward(desc, x, ids, gates, pool, out, ws, slot_ids=slots, stream=comp)
+            e1.record(comp)
+            if s_ >= args.warmup:
+                fwd_ms.append((e0, e1))
+            misses.append(nm)
+        comp.synchronize()
+        if s_ >= args.warmup:
+            step_ms.append((_t.perf_counter() - t_s) * 1e3)
+    torch.cuda.synchronize()
+    # kernel-level forward time without host gaps: replay recorded calls with the queue filled ahead
+    rec_calls = []
+    for s_ in range(max(args.warmup, n_steps - 4), n_steps):
+        for l in range(L):
+            bias.zero_()
+            bias.scatter_(1, trace_dev[s_, l], 30.0)
+            i_ = torch.empty_like(ids); g_ = torch.empty_like(gates)
+            ftmoe.ft_moe_route(desc, xs[(s_ * L + l) % 64], routers[l], i_, g_, sel_bias=bias, workspace=rws,
+                               stream=comp)
+            ftmoe.ft_slot_lookup(table, l, i_, slots, flags, mlist[1:], mlist[:1], stream=comp)
+            rec_calls.append((xs[(s_ * L + l) % 64], i_, g_, slots.clone()))
+    torch.cuda.synchronize()
+    f_res = []
+    torch.cuda._sleep(2_000_000)
+    for x_, i_, g_, sl_ in rec_calls:
+        e0, e1 = EV(), EV()
+        e0.record(comp)
+        ftmoe.ft_moe_forward(desc, x_, i_, g_, pool, out, ws, slot_ids=sl_, stream=comp)
+        e1.record(comp)
+        f_res.append((e0, e1))
+    torch.cuda.synchronize()
+    f_res_ms = np.array([a.elapsed_time(b) for a, b in f_res])
+    d_res = np.array([len(np.unique(i_.cpu().numpy())) for _, i_, _, _ in rec_calls])
+    n_up = sum(n for _, _, n in up_ev)
+    up_ms = sum(a.elapsed_time(b) for a, b, _ in up_ev)
+    f_ms = np.array([a.elapsed_time(b) for a, b in fwd_ms])
+    miss_arr = np.array(misses).reshape(n_steps, L)
+    # distinct experts per call = the trace's distinct ids (routing follows the trace)
+    distinct = np.array([[len(np.unique(trace[s_, l, :B])) for l in range(L)] for s_ in range(args.warmup, n_steps)])
+    fwd_bytes = d_res * rec + B * H * 2 + B * H * 4
+    gbs = float(np.mean(fwd_bytes) / (np.mean(f_res_ms) * 1e-3) / 1e9)
+    t_step = float(np.mean(step_ms))
+    res = _base_result(args, B * L / (t_step * 1e-3), "tokens/s", t_step,
+                       {"workload": cfg.name, "batch": B, "layers": L, "hidden": H, "experts": E, "top_k": k,
+                        "inter": I, "weights": "mxfp4", "pool_slots": S, "pool_gb": round(S * stride / 1e9, 1),
+                        "trace": f"zipf s={cfg.zipf_s}, {n_steps} steps, cold start", "host_layer_images": NH,
+                        "launch": "eager, host-synchronous per layer (miss list read back before uploads)"}, "bf16")
+    res["steps"] = n_steps - args.warmup
+    res["lru"] = {"miss_rate_per_selected_expert": round(float(miss_arr[args.warmup:].sum() / distinct.sum()), 4),
+                  "misses_per_layer_call": round(float(miss_arr[args.warmup:].mean()), 3),
+                  "cold_start_misses_first_step": int(miss_arr[0].sum()),
+                  "upload_gb_per_step": round(float(n_up * rec / max(1, len(step_ms)) / 1e9), 3),
+                  "host_link_gbs": round(n_up * rec / (up_ms * 1e-3) / 1e9, 2) if up_ms > 0 else None}
+    res["roofline"] = {"bound": "hbm", "kernel": "ft_moe_forward (expert GEMV, slot-indirected)",
+                       "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                       "bytes_per_launch": round(float(np.mean(fwd_bytes))),
+                       "avg_launch_us": round(float(np.mean(f_res_ms)) * 1e3, 2),
+                       "note": "forward calls of the last trace steps replayed with the queue filled ahead; "
+                               "in the host-synchronous loop the forward averaged "
+                               f"{float(np.mean(f_ms)) * 1e3:.1f} us"}
     print(json.dumps(res), flush=True)
 
 

@@ -182,77 +182,43 @@ __global__ void __launch_bounds__(256) grouped_mx_gemm_kernel(GemmArgs ga) {
   const uint8_t* rec = ga.pool + (int64_t)slot * ga.stride;
   const RecordLayout L = record_layout(ga.H, ga.I, FT_MXFP4);
 
-  // ---- per-thread global source rows for the loads of one K step
-  // A: 2 x 16 B per thread: rows (tid/8) and (tid/8 + 32), column chunk tid%8
-  int64_t a_row[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    int m = m0 + tid / 8 + 32 * r;
-    if (m >= m_end) m = m_end - 1;  // padding rows repeat the last row (results discarded)
-    a_row[r] = (MODE == GM_GATEUP) ? (int64_t)(ga.perm[m] / ga.k) : (int64_t)m;
-  }
-  // B: 2 x 16 B per thread: tile rows (tid/4) and (tid/4 + 64), chunk tid%4
-  const uint8_t* b_row[2];
-  const uint8_t* bs_row[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int br = tid / 4 + 64 * r;  // 0..127
-    int mat, row;
-    if (MODE == GM_GATEUP) {
-      mat = br < 64 ? 0 : 1;
-      row = ntile * 64 + (br & 63);
-    } else {
-      mat = 2;
-      row = ntile * 128 + br;
-    }
-    b_row[r] = rec + L.code_off[mat] + (int64_t)row * (K / 2);
-    bs_row[r] = rec + L.scale_off[mat] + (int64_t)row * (K / 32);
-  }
-  // scales: thread t < 64 -> A row t; 64 <= t < 192 -> B row t-64
-  const uint8_t* sc_src = nullptr;
+  // ---- per-thread global sources for the loads of one K step (kept in scalar
+  // registers: no local arrays, no captures, nothing goes to scratch)
+  // A: 2 x 16 B per thread: tile rows tid/8 and tid/8 + 32, 16-byte chunk tid%8
+  int ma0 = m0 + tid / 8, ma1 = m0 + tid / 8 + 32;
+  if (ma0 >= m_end) ma0 = m_end - 1;  // padding rows repeat the last row (results discarded)
+  if (ma1 >= m_end) ma1 = m_end - 1;
+  const int64_t ar0 = (MODE == GM_GATEUP) ? (int64_t)(ga.perm[ma0] / ga.k) : (int64_t)ma0;
+  const int64_t ar1 = (MODE == GM_GATEUP) ? (int64_t)(ga.perm[ma1] / ga.k) : (int64_t)ma1;
+  const uint8_t* pa0 = ga.aq + ar0 * K + (tid % 8) * 16;
+  const uint8_t* pa1 = ga.aq + ar1 * K + (tid % 8) * 16;
+  // B: 2 x 16 B per thread: tile rows tid/4 and tid/4 + 64, chunk tid%4
+  // (gate/up: tile rows 0-63 are gate rows, 64-127 the same up rows)
+  const int br0 = tid / 4, br1 = tid / 4 + 64;
+  const int mat0 = (MODE == GM_GATEUP) ? 0 : 2, mat1 = (MODE == GM_GATEUP) ? 1 : 2;
+  const int row0 = (MODE == GM_GATEUP) ? ntile * 64 + br0 : ntile * 128 + br0;
+  const int row1 = (MODE == GM_GATEUP) ? ntile * 64 + (br1 - 64) : ntile * 128 + br1;
+  const uint8_t* pb0 = rec + L.code_off[mat0] + (int64_t)row0 * (K / 2) + (tid % 4) * 16;
+  const uint8_t* pb1 = rec + L.code_off[mat1] + (int64_t)row1 * (K / 2) + (tid % 4) * 16;
+  // scales: thread t < 64 -> A row t; 64 <= t < 192 -> B tile row t - 64
+  const uint8_t* psc = ga.as;
   if (tid < 64) {
     int m = m0 + tid;
     if (m >= m_end) m = m_end - 1;
     const int64_t ar = (MODE == GM_GATEUP) ? (int64_t)(ga.perm[m] / ga.k) : (int64_t)m;
-    sc_src = ga.as + ar * (K / 32);
+    psc = ga.as + ar * (K / 32);
   } else if (tid < 192) {
     const int br = tid - 64;
-    int mat, row;
-    if (MODE == GM_GATEUP) {
-      mat = br < 64 ? 0 : 1;
-      row = ntile * 64 + (br & 63);
-    } else {
-      mat = 2;
-      row = ntile * 128 + br;
-    }
-    sc_src = rec + L.scale_off[mat] + (int64_t)row * (K / 32);
+    const int mat = (MODE == GM_GATEUP) ? (br < 64 ? 0 : 1) : 2;
+    const int row = (MODE == GM_GATEUP) ? ntile * 64 + (br & 63) : ntile * 128 + br;
+    psc = rec + L.scale_off[mat] + (int64_t)row * (K / 32);
   }
 
   // stage b: A at b*STAGE, B at b*STAGE + A bytes; scales after both stages
   constexpr int STAGE = GM_BM * GM_ASTR + GM_BN * GM_BSTR;
-  auto sA = [&](int b) { return smem + b * STAGE; };
-  auto sB = [&](int b) { return smem + b * STAGE + GM_BM * GM_ASTR; };
-  auto sS = [&](int b) { return reinterpret_cast<uint32_t*>(smem + 2 * STAGE) + b * (GM_BM + GM_BN); };
-
-  uint4 ra[2], rb[2];
-  uint32_t rs = 0;
-  auto gload = [&](int ks) {
-    const int kb = ks * GM_BK;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      ra[r] = *reinterpret_cast<const uint4*>(ga.aq + a_row[r] * K + kb + (tid % 8) * 16);
-      rb[r] = *reinterpret_cast<const uint4*>(b_row[r] + kb / 2 + (tid % 4) * 16);
-    }
-    if (tid < 192) rs = *reinterpret_cast<const uint32_t*>(sc_src + kb / 32);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      *reinterpret_cast<uint4*>(sA(buf) + (tid / 8 + 32 * r) * GM_ASTR + (tid % 8) * 16) = ra[r];
-      *reinterpret_cast<uint4*>(sB(buf) + (tid / 4 + 64 * r) * GM_BSTR + (tid % 4) * 16) = rb[r];
-    }
-    if (tid < 192) sS(buf)[tid] = rs;
-  };
+  uint8_t* const s_a0 = smem + (tid / 8) * GM_ASTR + (tid % 8) * 16;
+  uint8_t* const s_b0 = smem + GM_BM * GM_ASTR + (tid / 4) * GM_BSTR + (tid % 4) * 16;
+  uint32_t* const s_sc = reinterpret_cast<uint32_t*>(smem + 2 * STAGE);
 
   f32x4_t acc[2][4];
 #pragma unroll
@@ -261,37 +227,67 @@ __global__ void __launch_bounds__(256) grouped_mx_gemm_kernel(GemmArgs ga) {
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
   const int nks = K / GM_BK;
-  gload(0);
-  lstore(0);
+  uint4 ra0, ra1, rb0, rb1;
+  uint32_t rs = 0;
+  // prologue: stage 0
+  ra0 = *reinterpret_cast<const uint4*>(pa0);
+  ra1 = *reinterpret_cast<const uint4*>(pa1);
+  rb0 = *reinterpret_cast<const uint4*>(pb0);
+  rb1 = *reinterpret_cast<const uint4*>(pb1);
+  if (tid < 192) rs = *reinterpret_cast<const uint32_t*>(psc);
+  *reinterpret_cast<uint4*>(s_a0) = ra0;
+  *reinterpret_cast<uint4*>(s_a0 + 32 * GM_ASTR) = ra1;
+  *reinterpret_cast<uint4*>(s_b0) = rb0;
+  *reinterpret_cast<uint4*>(s_b0 + 64 * GM_BSTR) = rb1;
+  if (tid < 192) s_sc[tid] = rs;
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
     const int cur = ks & 1;
-    if (ks + 1 < nks) gload(ks + 1);
-    // operands from LDS
-    i32x8_t af[2];
-    int asc[2];
-#pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
-      const int row = wm * 32 + ms * 16 + c16;
-      const uint8_t* p = sA(cur) + row * GM_ASTR;
-      const uint4 lo = *reinterpret_cast<const uint4*>(p + 16 * g);
-      const uint4 hi = *reinterpret_cast<const uint4*>(p + 64 + 16 * g);
-      af[ms] = (i32x8_t){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      asc[ms] = (int)((sS(cur)[row] >> (8 * g)) & 0xFFu);
+    const bool more = ks + 1 < nks;
+    if (more) {  // next stage's global loads, in flight during this stage's MFMAs
+      const int kb = (ks + 1) * GM_BK;
+      ra0 = *reinterpret_cast<const uint4*>(pa0 + kb);
+      ra1 = *reinterpret_cast<const uint4*>(pa1 + kb);
+      rb0 = *reinterpret_cast<const uint4*>(pb0 + kb / 2);
+      rb1 = *reinterpret_cast<const uint4*>(pb1 + kb / 2);
+      if (tid < 192) rs = *reinterpret_cast<const uint32_t*>(psc + kb / 32);
+    }
+    const uint8_t* sa = smem + cur * STAGE;
+    const uint8_t* sb = smem + cur * STAGE + GM_BM * GM_ASTR;
+    const uint32_t* ss = s_sc + cur * (GM_BM + GM_BN);
+    i32x8_t af0, af1;
+    int asc0, asc1;
+    {
+      const int row = wm * 32 + c16;
+      const uint4 lo = *reinterpret_cast<const uint4*>(sa + row * GM_ASTR + 16 * g);
+      const uint4 hi = *reinterpret_cast<const uint4*>(sa + row * GM_ASTR + 64 + 16 * g);
+      af0 = (i32x8_t){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      asc0 = (int)((ss[row] >> (8 * g)) & 0xFFu);
+      const int row2 = row + 16;
+      const uint4 lo2 = *reinterpret_cast<const uint4*>(sa + row2 * GM_ASTR + 16 * g);
+      const uint4 hi2 = *reinterpret_cast<const uint4*>(sa + row2 * GM_ASTR + 64 + 16 * g);
+      af1 = (i32x8_t){(int)lo2.x, (int)lo2.y, (int)lo2.z, (int)lo2.w, (int)hi2.x, (int)hi2.y, (int)hi2.z, (int)hi2.w};
+      asc1 = (int)((ss[row2] >> (8 * g)) & 0xFFu);
     }
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
       int brow;
       if (MODE == GM_GATEUP) brow = (ns < 2) ? (32 * wn + 16 * ns + c16) : (64 + 32 * wn + 16 * (ns - 2) + c16);
       else brow = 64 * wn + 16 * ns + c16;
-      const uint4 q = *reinterpret_cast<const uint4*>(sB(cur) + brow * GM_BSTR + 16 * g);
+      const uint4 q = *reinterpret_cast<const uint4*>(sb + brow * GM_BSTR + 16 * g);
       const i32x8_t bf = (i32x8_t){(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      const int bsc = (int)((sS(cur)[GM_BM + brow] >> (8 * g)) & 0xFFu);
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms)
-        acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[ms], bf, acc[ms][ns], 0, 4, 0, asc[ms], 0, bsc);
+      const int bsc = (int)((ss[GM_BM + brow] >> (8 * g)) & 0xFFu);
+      acc[0][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af0, bf, acc[0][ns], 0, 4, 0, asc0, 0, bsc);
+      acc[1][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af1, bf, acc[1][ns], 0, 4, 0, asc1, 0, bsc);
     }
-    if (ks + 1 < nks) lstore(cur ^ 1);
+    if (more) {
+      const int nb = cur ^ 1;
+      *reinterpret_cast<uint4*>(s_a0 + nb * STAGE) = ra0;
+      *reinterpret_cast<uint4*>(s_a0 + nb * STAGE + 32 * GM_ASTR) = ra1;
+      *reinterpret_cast<uint4*>(s_b0 + nb * STAGE) = rb0;
+      *reinterpret_cast<uint4*>(s_b0 + nb * STAGE + 64 * GM_BSTR) = rb1;
+      if (tid < 192) s_sc[nb * (GM_BM + GM_BN) + tid] = rs;
+    }
     __syncthreads();
   }
 

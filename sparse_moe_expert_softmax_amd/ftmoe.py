@@ -123,7 +123,11 @@ def ft_expert_upload(pool, expert_stride: int, record_bytes: int, slots, host_pt
     n = len(slots)
     arr_s = (_i32 * max(n, 1))(*slots)
     arr_p = (_vp * max(n, 1))(*host_ptrs)
-    ev = None if done_event is None else ctypes.c_void_p(done_event.cuda_event)
+    ev = None
+    if done_event is not None:
+        if not done_event.cuda_event:  # torch creates the HIP event lazily: create it on this stream first
+            done_event.record(torch.cuda.current_stream() if stream is None else stream)
+        ev = ctypes.c_void_p(done_event.cuda_event)
     _check(lib().ft_expert_upload(_ptr(pool), expert_stride, record_bytes, arr_s, arr_p, n, _stream(stream), ev))
 
 

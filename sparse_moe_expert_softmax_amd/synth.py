@@ -259,3 +259,59 @@ def bits_to_mask(bits: np.ndarray) -> np.ndarray:
     for e in range(E):
         out[:, e // 32] |= (bits[:, e].astype(np.uint32) << np.uint32(e % 32))
     return out
+
+
+# ------------------------------------------------- device-side generation ---
+# The benchmark pools (tens of GB) are generated on the device with torch's
+# seeded generator: the same distribution and the same encoding rules as the
+# host generator above, different random streams.  Parity tests use the host
+# generator.
+def _torch_e2m1_codes(torch, m):
+    code = (m > 0.25).to(torch.uint8)
+    code += (m >= 0.75).to(torch.uint8)
+    code += (m > 1.25).to(torch.uint8)
+    code += (m >= 1.75).to(torch.uint8)
+    code += (m > 2.5).to(torch.uint8)
+    code += (m >= 3.5).to(torch.uint8)
+    code += (m > 5.0).to(torch.uint8)
+    return code
+
+
+def _torch_pack(torch, q):
+    codes = _torch_e2m1_codes(torch, q.abs()) | (torch.signbit(q).to(torch.uint8) << 3)
+    codes = codes.reshape(codes.shape[0], -1, 2)
+    return (codes[..., 0] | (codes[..., 1] << 4)).reshape(codes.shape[0], -1)
+
+
+def device_record_fp4(torch, gen, H: int, I: int, std: float, w_dtype: int, stride: int):
+    """One packed MXFP4 / NVFP4-like record generated on the current device."""
+    rec = torch.zeros(stride, dtype=torch.uint8, device="cuda")
+    codes, scales, tscales = [], [], []
+    for rows, K in ((I, H), (I, H), (H, I)):
+        w = torch.randn((rows, K), generator=gen, device="cuda", dtype=torch.float32) * std
+        if w_dtype == MXFP4:
+            blk = w.view(rows, K // 32, 32)
+            amax = blk.abs().amax(-1)
+            _, e = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))
+            X = torch.where(amax > 0, e - 1 - 2, torch.full_like(e, -127)).clamp(-127, 127)
+            q = blk * torch.ldexp(torch.ones_like(amax), -X)[..., None]
+            codes.append(_torch_pack(torch, q.view(rows, K)).flatten())
+            scales.append((X + 127).to(torch.uint8).flatten())
+        else:
+            amax_t = float(w.abs().max())
+            ts = amax_t / (6.0 * 448.0) if amax_t > 0 else 1.0
+            ts = float(np.float32(ts))
+            blk = w.view(rows, K // 16, 16)
+            sc = (blk.abs().amax(-1) / 6.0 / ts).to(torch.float8_e4m3fn)
+            sv = sc.to(torch.float32) * ts
+            q = blk / torch.where(sv > 0, sv, torch.ones_like(sv))[..., None]
+            q = torch.where(sv[..., None] > 0, q, torch.zeros_like(q))
+            codes.append(_torch_pack(torch, q.view(rows, K)).flatten())
+            scales.append(sc.view(torch.uint8).flatten())
+            tscales.append(ts)
+    parts = codes + scales
+    if w_dtype == NVFP4:
+        parts.append(torch.from_numpy(np.array(tscales, dtype="<f4").view(np.uint8)).cuda())
+    flat = torch.cat(parts)
+    rec[: flat.numel()] = flat
+    return rec

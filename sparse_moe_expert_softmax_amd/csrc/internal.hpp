@@ -62,6 +62,6 @@ hipError_t launch_combine(const FwdPlan& pl, const int32_t* pos, const float* ga
 hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const void* x, const int32_t* slot_ids,
                                const void* pool, const float* gates, float* out, char* ws, hipStream_t st);
 
-constexpr int PERM_CHUNK = 4096;  // pairs per permute block
+constexpr int PERM_CHUNK = 1024;  // pairs per permute block (one per thread)
 
 }  // namespace ft

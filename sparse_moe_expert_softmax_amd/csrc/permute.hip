@@ -60,8 +60,8 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(
     const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P, int E, int nb,
     const int32_t* __restrict__ block_hist, int32_t* __restrict__ offsets, int32_t* __restrict__ active,
     int32_t* __restrict__ perm, int32_t* __restrict__ pos_of_pair) {
-  __shared__ int32_t base_e[1024];   // where this block's pairs of expert e start
-  __shared__ int32_t running[1024];  // pairs of expert e already placed by this block
+  __shared__ int32_t base_e[1024];        // where this block's pairs of expert e start
+  __shared__ uint16_t wcnt[16][1024];     // per-wave counts, then per-wave prefixes
   __shared__ int32_t tmp[16];
   __shared__ int32_t tot;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -75,11 +75,11 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(
       if (bb < b) before += c;
     }
   }
+  for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
   const int eoff = block_exclusive_scan(tid < E ? total : 0, tmp, &tot);
   const int aoff = block_exclusive_scan((tid < E && total > 0) ? 1 : 0, tmp, &tot);
   if (tid < E) {
     base_e[tid] = eoff + before;
-    running[tid] = 0;
     if (b == 0) {
       offsets[tid] = eoff;
       if (total > 0) active[aoff] = tid;
@@ -87,42 +87,42 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(
   }
   if (b == 0 && tid == E - 1) offsets[E] = eoff + total;  // pairs kept
   if (b == 0 && tid == 0) offsets[E + 1] = tot;             // number of active experts
+  // one pair per thread: rank among earlier lanes of the wave with the same expert
+  const int p = b * PERM_CHUNK + tid;
+  int e = -1;
+  bool valid = false;
+  if (p < P) {
+    e = ids[p];
+    valid = e >= 0 && e < E && in_mask(mask, e);
+    if (!valid) pos_of_pair[p] = -1;
+  }
+  uint64_t todo = __ballot(valid);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int rank = 0;
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const int el = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t m = __ballot(valid && e == el);
+    if (valid && e == el) rank = __popcll(m & below);
+    if (lane == leader) wcnt[wv][el] = (uint16_t)__popcll(m);
+    todo &= ~m;
+  }
   __syncthreads();
-  // stable scatter: 4 rounds of 1024 pairs; waves of a round in order
-  const int base = b * PERM_CHUNK;
-  for (int r = 0; r < PERM_CHUNK / 1024; ++r) {
-    const int p = base + r * 1024 + tid;
-    int e = -1;
-    bool valid = false;
-    if (p < P) {
-      e = ids[p];
-      valid = e >= 0 && e < E && in_mask(mask, e);
-      if (!valid) pos_of_pair[p] = -1;
-    }
+  // exclusive prefix of the per-wave counts, wave order, for every expert
+  if (tid < E) {
+    int run = 0;
+#pragma unroll
     for (int w = 0; w < 16; ++w) {
-      if (wv == w) {
-        uint64_t todo = __ballot(valid);
-        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        int rank = 0, lead_cnt = 0;
-        while (todo) {
-          const int leader = __ffsll((unsigned long long)todo) - 1;
-          const int el = __shfl(e, leader, 64);
-          const uint64_t m = __ballot(valid && e == el);
-          if (valid && e == el) rank = __popcll(m & below);
-          if (lane == leader) lead_cnt = __popcll(m);
-          todo &= ~m;
-        }
-        if (valid) {
-          const int pos = base_e[e] + running[e] + rank;
-          perm[pos] = p;
-          pos_of_pair[p] = pos;
-        }
-        // wave-converged: leaders publish their counts after everyone read running[]
-        __builtin_amdgcn_wave_barrier();
-        if (lead_cnt > 0) running[e] += lead_cnt;
-      }
-      __syncthreads();
+      const int c = wcnt[w][tid];
+      wcnt[w][tid] = (uint16_t)run;
+      run += c;
     }
+  }
+  __syncthreads();
+  if (valid) {
+    const int pos = base_e[e] + wcnt[wv][e] + rank;
+    perm[pos] = p;
+    pos_of_pair[p] = pos;
   }
 }
 

@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=8192, help="prefill: prompt tokens (multiples of 8192 run as chunks)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--host-layers", type=int, default=2, help="distinct pinned host layer images (aliased)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 256 MiB device-to-device copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -159,6 +161,12 @@ def main():
             if ev is not None:
                 ev[l][1].record(stream)
 
+    if args.calibrate_copy:  # a plain copy kernel of known size, for hardware-counter calibration
+        src_c = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst_c = torch.empty_like(src_c)
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()

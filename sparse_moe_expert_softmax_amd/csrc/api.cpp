@@ -74,7 +74,8 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T) {
     p.off_xq = o;    o = align256(o + (size_t)T * p.H);                     // MXFP8 x codes
     p.off_xs = o;    o = align256(o + (size_t)T * p.H / 32);                // and scales
     p.off_hs = o;    o = align256(o + (size_t)p.P * p.I / 32);              // h scales
-    p.off_tiles = o; o = align256(o + sizeof(int32_t) * (size_t)(2 * p.max_tiles + 1));
+    p.off_tiles = o; o = align256(o + sizeof(int32_t) * ((size_t)2 * p.max_tiles + 1 +
+                                                          (size_t)p.max_tiles * (p.I / 128 + p.H / 256)));
   } else {
     p.off_xq = p.off_xs = p.off_hs = p.off_tiles = o;
   }

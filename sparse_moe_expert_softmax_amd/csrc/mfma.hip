@@ -37,10 +37,10 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int GM_BM = 64;      // pair rows per tile
-constexpr int GM_BN = 128;     // weight rows per tile
+constexpr int GM_BN = 256;     // weight rows per tile (gate/up: 128 gate rows + the same 128 up rows)
 constexpr int GM_BK = 128;     // K per step
-constexpr int GM_ASTR = 144;   // LDS row stride of A (bytes), padded
-constexpr int GM_BSTR = 80;    // LDS row stride of B (bytes), padded
+constexpr int GM_ASTR = 144;   // LDS row stride of A (bytes), padded: conflict-free 16-byte fragment reads
+constexpr int GM_HSTR = 33;    // LDS row stride of the h epilogue tile (floats)
 
 // -------------------------------------------------------- E4M3 rounding --
 // |v| (already divided by the block scale, finite) -> E4M3 code, nearest
@@ -119,9 +119,15 @@ __global__ void __launch_bounds__(256) quant_x_kernel(const uint16_t* __restrict
 
 // ------------------------------------------------------------ tile list --
 // tiles[2*i] = expert, tiles[2*i+1] = first row (sorted position) of tile i;
-// tiles are grouped by expert; count in *n_tiles.  One workgroup.
+// tiles are grouped by expert; count in *n_tiles.  Work lists (one per GEMM,
+// n_nt weight tiles each): item = tile | (ntile << 20), ordered by expert,
+// then weight tile, then row tile, so that the row tiles sharing a weight
+// tile run side by side and an expert's activation rows stay in one L2.
+// One workgroup.
 __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                           int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+                                                           int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+                                                           int32_t* __restrict__ work_a, int n_nt_a,
+                                                           int32_t* __restrict__ work_b, int n_nt_b) {
   __shared__ int32_t start[1025];
   if (threadIdx.x == 0) {
     int run = 0;
@@ -136,15 +142,36 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int cnt = offsets[e + 1] - offsets[e];
-    for (int i = 0; i * GM_BM < cnt; ++i) {
+    const int mt = start[e + 1] - start[e];
+    for (int i = 0; i < mt; ++i) {
       tiles[2 * (start[e] + i)] = e;
       tiles[2 * (start[e] + i) + 1] = offsets[e] + i * GM_BM;
     }
+    for (int nt = 0; nt < n_nt_a; ++nt)
+      for (int i = 0; i < mt; ++i) work_a[start[e] * n_nt_a + nt * mt + i] = (start[e] + i) | (nt << 20);
+    for (int nt = 0; nt < n_nt_b; ++nt)
+      for (int i = 0; i < mt; ++i) work_b[start[e] * n_nt_b + nt * mt + i] = (start[e] + i) | (nt << 20);
+    (void)cnt;
   }
 }
 
 // -------------------------------------------------------------- the GEMM --
 enum { GM_GATEUP = 0, GM_DOWN = 1 };
+
+// Buffer descriptor word 3 for untyped 32-bit accesses on gfx9-family parts.
+constexpr int GM_RSRC_WORD3 = 0x00020000;
+
+__device__ __forceinline__ uint3 gm_ld96(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  typedef int i32x3_t __attribute__((ext_vector_type(3)));
+  const i32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+  return make_uint3((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z);
+}
+
+__device__ __forceinline__ uint4 gm_ld128(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
 
 struct GemmArgs {
   const uint8_t* aq;       // A codes: x_q [T, K] (gate/up) or h_q [P, K] (down)
@@ -153,197 +180,259 @@ struct GemmArgs {
   const int32_t* offsets;  // [E+2]
   const int32_t* tiles;    // tile list
   const int32_t* n_tiles;
+  const int32_t* work;     // work items of this GEMM
   const int32_t* slot_ids; // per pair (nullable)
   const uint8_t* pool;
   int64_t stride;
   uint8_t* hq;             // gate/up out: h codes [P, I]
   uint8_t* hs;             // gate/up out: h scales [P, I/32]
   float* y;                // down out: [P, H]
+  int64_t a_bytes;         // size of the A code array (< 2^31)
   int H, I, k, n_ntiles, total_wg;
 };
 
+// Workgroup tile: 64 pair rows x 256 weight rows, K advancing 128 per step.
+// The four waves split the weight rows: each wave owns all 64 pair rows and
+// 64 weight rows (4 x 4 MFMAs per K step, 16 independent accumulators).
+//   A (activations, shared by the waves) goes global -> registers -> LDS,
+//     double-buffered; each wave reads its fragments from LDS.
+//   B (weights, private to one wave) goes global -> registers straight into
+//     the MFMA operand: lane l loads the 16 bytes (one MX block of 32 E2M1
+//     codes) of weight row l % 16, K block l / 16, and the matching scale byte.
+// A ring of three register slots keeps the loads of two K steps in flight;
+// every step issues the same loads unconditionally (the step index is
+// clamped at the end), so the compiler's wait counts stay exact.
 template <int MODE>
-__global__ void __launch_bounds__(256) grouped_mx_gemm_kernel(GemmArgs ga) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (GM_BM * GM_ASTR + GM_BN * GM_BSTR) + 2 * (GM_BM + GM_BN) * 4];
+__global__ void __launch_bounds__(256, 2) grouped_mx_gemm_kernel(GemmArgs ga) {
+  constexpr int A_STAGE = GM_BM * GM_ASTR;
+  constexpr int LDS_MAIN = 2 * A_STAGE + 2 * GM_BM * 12 + 2 * GM_BN * 12;
+  constexpr int LDS_EPI = 4 * GM_BM * GM_HSTR * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI];
   // map workgroups XCD-major: consecutive work items run on one XCD
   const int G = ga.total_wg;
   const int per_xcd = (G + 7) / 8;
   const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   const int nt = *ga.n_tiles;
   if (w >= nt * ga.n_ntiles) return;
-  const int tile = w / ga.n_ntiles, ntile = w % ga.n_ntiles;
+  const int item = ga.work[w];
+  const int tile = item & 0xFFFFF, ntile = item >> 20;
   const int e = ga.tiles[2 * tile], m0 = ga.tiles[2 * tile + 1];
   const int m_end = ga.offsets[e + 1];
   const int K = (MODE == GM_GATEUP) ? ga.H : ga.I;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int wm = wv >> 1, wn = wv & 1;
 
   const int slot = ga.slot_ids ? ga.slot_ids[ga.perm[m0]] : e;
   const uint8_t* rec = ga.pool + (int64_t)slot * ga.stride;
   const RecordLayout L = record_layout(ga.H, ga.I, FT_MXFP4);
 
-  // ---- per-thread global sources for the loads of one K step (kept in scalar
-  // registers: no local arrays, no captures, nothing goes to scratch)
-  // A: 2 x 16 B per thread: tile rows tid/8 and tid/8 + 32, 16-byte chunk tid%8
-  int ma0 = m0 + tid / 8, ma1 = m0 + tid / 8 + 32;
+  // ---- A sources: 2 x 16 B per thread (tile rows tid/8 and tid/8 + 32,
+  // 16-byte chunk tid%8) and one scale word per thread (row tid%64; only
+  // threads < 64 store theirs)
+  int ma0 = m0 + tid / 8, ma1 = m0 + tid / 8 + 32, mas = m0 + 16 * wv + c16;
   if (ma0 >= m_end) ma0 = m_end - 1;  // padding rows repeat the last row (results discarded)
   if (ma1 >= m_end) ma1 = m_end - 1;
+  if (mas >= m_end) mas = m_end - 1;
   const int64_t ar0 = (MODE == GM_GATEUP) ? (int64_t)(ga.perm[ma0] / ga.k) : (int64_t)ma0;
   const int64_t ar1 = (MODE == GM_GATEUP) ? (int64_t)(ga.perm[ma1] / ga.k) : (int64_t)ma1;
-  const uint8_t* pa0 = ga.aq + ar0 * K + (tid % 8) * 16;
-  const uint8_t* pa1 = ga.aq + ar1 * K + (tid % 8) * 16;
-  // B: 2 x 16 B per thread: tile rows tid/4 and tid/4 + 64, chunk tid%4
-  // (gate/up: tile rows 0-63 are gate rows, 64-127 the same up rows)
-  const int br0 = tid / 4, br1 = tid / 4 + 64;
-  const int mat0 = (MODE == GM_GATEUP) ? 0 : 2, mat1 = (MODE == GM_GATEUP) ? 1 : 2;
-  const int row0 = (MODE == GM_GATEUP) ? ntile * 64 + br0 : ntile * 128 + br0;
-  const int row1 = (MODE == GM_GATEUP) ? ntile * 64 + (br1 - 64) : ntile * 128 + br1;
-  const uint8_t* pb0 = rec + L.code_off[mat0] + (int64_t)row0 * (K / 2) + (tid % 4) * 16;
-  const uint8_t* pb1 = rec + L.code_off[mat1] + (int64_t)row1 * (K / 2) + (tid % 4) * 16;
-  // scales: thread t < 64 -> A row t; 64 <= t < 192 -> B tile row t - 64
-  const uint8_t* psc = ga.as;
-  if (tid < 64) {
-    int m = m0 + tid;
-    if (m >= m_end) m = m_end - 1;
-    const int64_t ar = (MODE == GM_GATEUP) ? (int64_t)(ga.perm[m] / ga.k) : (int64_t)m;
-    psc = ga.as + ar * (K / 32);
-  } else if (tid < 192) {
-    const int br = tid - 64;
-    const int mat = (MODE == GM_GATEUP) ? (br < 64 ? 0 : 1) : 2;
-    const int row = (MODE == GM_GATEUP) ? ntile * 64 + (br & 63) : ntile * 128 + br;
-    psc = rec + L.scale_off[mat] + (int64_t)row * (K / 32);
+  const int64_t ars = (MODE == GM_GATEUP) ? (int64_t)(ga.perm[mas] / ga.k) : (int64_t)mas;
+  // Loads go through buffer descriptors: a per-lane 32-bit offset that stays
+  // fixed over the K loop plus a scalar K offset, so the loop keeps no 64-bit
+  // addresses in vector registers.
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ga.aq, (short)0, (int)ga.a_bytes, GM_RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rAs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ga.as, (short)0, (int)(ga.a_bytes / 32), GM_RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)rec, (short)0, (int)L.bytes, GM_RSRC_WORD3);
+  const int oa0 = (int)(ar0 * K) + (tid % 8) * 16;
+  const int oa1 = (int)(ar1 * K) + (tid % 8) * 16;
+  // scales travel in groups of three K steps (12 blocks, 12 bytes per row):
+  // lane l of wave w loads dword min(l/16, 2) of A row 16w + l%16, and the 12
+  // bytes of its wave's weight row 16*(l/16) + l%16 (sub-tile l/16)
+  const int oas = (int)(ars * (K / 32)) + 4 * (g < 3 ? g : 2);
+
+  // ---- B sources: weight row of sub-tile ns for this lane, K block g
+  // gate/up: ns 0,1 = gate rows, ns 2,3 = the same up rows
+  //          (ntile*128 + 32*wave + 16*(ns&1) + lane%16)
+  // down:    rows ntile*256 + 64*wave + 16*ns + lane%16
+  auto brow = [&](int ns) {
+    return (MODE == GM_GATEUP) ? ntile * 128 + 32 * wv + 16 * (ns & 1) + c16 : ntile * 256 + 64 * wv + 16 * ns + c16;
+  };
+  auto bmat = [&](int ns) { return (MODE == GM_GATEUP) ? (ns < 2 ? 0 : 1) : 2; };
+  // one per-lane offset (sub-tile 0) for all four sub-tiles; the others
+  // differ by a uniform amount that rides in the scalar offset
+  const int ob = (int)L.code_off[bmat(0)] + brow(0) * (K / 2) + 16 * g;
+  auto bdelta = [&](int ns) {
+    return (int)(L.code_off[bmat(ns)] - L.code_off[bmat(0)]) + (brow(ns) - brow(0)) * (K / 2);
+  };
+  const int db1 = bdelta(1), db2 = bdelta(2), db3 = bdelta(3);
+  int obs;  // this lane's weight-scale row: sub-tile g, row lane%16
+  {
+    const int ns = g;
+    const int row = (MODE == GM_GATEUP) ? ntile * 128 + 32 * wv + 16 * (ns & 1) + c16 : ntile * 256 + 64 * wv + 16 * ns + c16;
+    const int mat = (MODE == GM_GATEUP) ? (ns < 2 ? 0 : 1) : 2;
+    obs = (int)L.scale_off[mat] + row * (K / 32);
   }
 
-  // stage b: A at b*STAGE, B at b*STAGE + A bytes; scales after both stages
-  constexpr int STAGE = GM_BM * GM_ASTR + GM_BN * GM_BSTR;
-  uint8_t* const s_a0 = smem + (tid / 8) * GM_ASTR + (tid % 8) * 16;
-  uint8_t* const s_b0 = smem + GM_BM * GM_ASTR + (tid / 4) * GM_BSTR + (tid % 4) * 16;
-  uint32_t* const s_sc = reinterpret_cast<uint32_t*>(smem + 2 * STAGE);
+  uint8_t* const s_a = smem + (tid / 8) * GM_ASTR + (tid % 8) * 16;  // this thread's A store address
+  // scale groups, double-buffered: A [2][64 rows][3 dwords], weights [2][4 waves][64 rows][3 dwords]
+  uint32_t* const s_as = reinterpret_cast<uint32_t*>(smem + 2 * A_STAGE);
+  uint32_t* const s_bs = s_as + 2 * GM_BM * 3;
 
-  f32x4_t acc[2][4];
+  f32x4_t acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
   const int nks = K / GM_BK;
-  uint4 ra0, ra1, rb0, rb1;
-  uint32_t rs = 0;
-  // prologue: stage 0
-  ra0 = *reinterpret_cast<const uint4*>(pa0);
-  ra1 = *reinterpret_cast<const uint4*>(pa1);
-  rb0 = *reinterpret_cast<const uint4*>(pb0);
-  rb1 = *reinterpret_cast<const uint4*>(pb1);
-  if (tid < 192) rs = *reinterpret_cast<const uint32_t*>(psc);
-  *reinterpret_cast<uint4*>(s_a0) = ra0;
-  *reinterpret_cast<uint4*>(s_a0 + 32 * GM_ASTR) = ra1;
-  *reinterpret_cast<uint4*>(s_b0) = rb0;
-  *reinterpret_cast<uint4*>(s_b0 + 64 * GM_BSTR) = rb1;
-  if (tid < 192) s_sc[tid] = rs;
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < nks;
-    if (more) {  // next stage's global loads, in flight during this stage's MFMAs
-      const int kb = (ks + 1) * GM_BK;
-      ra0 = *reinterpret_cast<const uint4*>(pa0 + kb);
-      ra1 = *reinterpret_cast<const uint4*>(pa1 + kb);
-      rb0 = *reinterpret_cast<const uint4*>(pb0 + kb / 2);
-      rb1 = *reinterpret_cast<const uint4*>(pb1 + kb / 2);
-      if (tid < 192) rs = *reinterpret_cast<const uint32_t*>(psc + kb / 32);
-    }
-    const uint8_t* sa = smem + cur * STAGE;
-    const uint8_t* sb = smem + cur * STAGE + GM_BM * GM_ASTR;
-    const uint32_t* ss = s_sc + cur * (GM_BM + GM_BN);
-    i32x8_t af0, af1;
-    int asc0, asc1;
-    {
-      const int row = wm * 32 + c16;
-      const uint4 lo = *reinterpret_cast<const uint4*>(sa + row * GM_ASTR + 16 * g);
-      const uint4 hi = *reinterpret_cast<const uint4*>(sa + row * GM_ASTR + 64 + 16 * g);
-      af0 = (i32x8_t){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      asc0 = (int)((ss[row] >> (8 * g)) & 0xFFu);
-      const int row2 = row + 16;
-      const uint4 lo2 = *reinterpret_cast<const uint4*>(sa + row2 * GM_ASTR + 16 * g);
-      const uint4 hi2 = *reinterpret_cast<const uint4*>(sa + row2 * GM_ASTR + 64 + 16 * g);
-      af1 = (i32x8_t){(int)lo2.x, (int)lo2.y, (int)lo2.z, (int)lo2.w, (int)hi2.x, (int)hi2.y, (int)hi2.z, (int)hi2.w};
-      asc1 = (int)((ss[row2] >> (8 * g)) & 0xFFu);
-    }
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-      int brow;
-      if (MODE == GM_GATEUP) brow = (ns < 2) ? (32 * wn + 16 * ns + c16) : (64 + 32 * wn + 16 * (ns - 2) + c16);
-      else brow = 64 * wn + 16 * ns + c16;
-      const uint4 q = *reinterpret_cast<const uint4*>(sb + brow * GM_BSTR + 16 * g);
-      const i32x8_t bf = (i32x8_t){(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      const int bsc = (int)((ss[GM_BM + brow] >> (8 * g)) & 0xFFu);
-      acc[0][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af0, bf, acc[0][ns], 0, 4, 0, asc0, 0, bsc);
-      acc[1][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af1, bf, acc[1][ns], 0, 4, 0, asc1, 0, bsc);
-    }
-    if (more) {
-      const int nb = cur ^ 1;
-      *reinterpret_cast<uint4*>(s_a0 + nb * STAGE) = ra0;
-      *reinterpret_cast<uint4*>(s_a0 + nb * STAGE + 32 * GM_ASTR) = ra1;
-      *reinterpret_cast<uint4*>(s_b0 + nb * STAGE) = rb0;
-      *reinterpret_cast<uint4*>(s_b0 + nb * STAGE + 64 * GM_BSTR) = rb1;
-      if (tid < 192) s_sc[nb * (GM_BM + GM_BN) + tid] = rs;
-    }
-    __syncthreads();
-  }
+#define GM_DECL(r) uint4 ra0_##r, ra1_##r, rb0_##r, rb1_##r, rb2_##r, rb3_##r;
+  GM_DECL(0) GM_DECL(1) GM_DECL(2)
+#undef GM_DECL
+  uint32_t gsa;  // A-scale dword of the group in flight
+  uint3 gsb;     // weight-scale bytes (12) of the group in flight
+#define GM_LOAD(r, st)                                                              \
+  do {                                                                              \
+    const int kb_ = ((st) < nks ? (st) : nks - 1) * GM_BK;                          \
+    ra0_##r = gm_ld128(rA, oa0, kb_);                                               \
+    ra1_##r = gm_ld128(rA, oa1, kb_);                                               \
+    rb0_##r = gm_ld128(rB, ob, kb_ / 2);                                            \
+    rb1_##r = gm_ld128(rB, ob, db1 + kb_ / 2);                                      \
+    rb2_##r = gm_ld128(rB, ob, db2 + kb_ / 2);                                      \
+    rb3_##r = gm_ld128(rB, ob, db3 + kb_ / 2);                                      \
+  } while (0)
+#define GM_STORE(r, buf)                                                            \
+  do {                                                                              \
+    *reinterpret_cast<uint4*>(s_a + (buf) * A_STAGE) = ra0_##r;                     \
+    *reinterpret_cast<uint4*>(s_a + (buf) * A_STAGE + 32 * GM_ASTR) = ra1_##r;      \
+  } while (0)
+  // scale group G covers K steps 3G .. 3G+2 (clamped at the end; the bytes of
+  // a partial last group past the row are never used)
+#define GM_GLOAD(G)                                                                 \
+  do {                                                                              \
+    const int gg_ = ((G) <= (nks - 1) / 3 ? (G) : (nks - 1) / 3) * 12;              \
+    gsa = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rAs, oas, gg_, 0);         \
+    gsb = gm_ld96(rB, obs, gg_);                                                    \
+  } while (0)
+#define GM_GSTORE(buf)                                                              \
+  do {                                                                              \
+    if (g < 3) s_as[(buf) * GM_BM * 3 + (16 * wv + c16) * 3 + g] = gsa;             \
+    uint32_t* d_ = s_bs + (buf) * GM_BN * 3 + (64 * wv + lane) * 3;                 \
+    d_[0] = gsb.x; d_[1] = gsb.y; d_[2] = gsb.z;                                    \
+  } while (0)
+#define GM_BOP(v_) ((i32x8_t){(int)(v_).x, (int)(v_).y, (int)(v_).z, (int)(v_).w, 0, 0, 0, 0})
+#define GM_STEP(r, buf, sbuf, j)                                                                  \
+  do {                                                                                            \
+    const uint8_t* sa_ = smem + (buf) * A_STAGE;                                                  \
+    const uint8_t* sas_ = reinterpret_cast<const uint8_t*>(s_as + (sbuf) * GM_BM * 3) + 4 * (j) + g; \
+    const uint8_t* sbs_ = reinterpret_cast<const uint8_t*>(s_bs + (sbuf) * GM_BN * 3 + 64 * wv * 3) + 4 * (j) + g; \
+    const i32x8_t b0_ = GM_BOP(rb0_##r), b1_ = GM_BOP(rb1_##r);                                   \
+    const i32x8_t b2_ = GM_BOP(rb2_##r), b3_ = GM_BOP(rb3_##r);                                   \
+    const int bs0_ = sbs_[(c16) * 12], bs1_ = sbs_[(16 + c16) * 12];                              \
+    const int bs2_ = sbs_[(32 + c16) * 12], bs3_ = sbs_[(48 + c16) * 12];                         \
+    _Pragma("unroll") for (int ms = 0; ms < 4; ++ms) {                                            \
+      const int row_ = 16 * ms + c16;                                                             \
+      const uint4 lo_ = *reinterpret_cast<const uint4*>(sa_ + row_ * GM_ASTR + 16 * g);           \
+      const uint4 hi_ = *reinterpret_cast<const uint4*>(sa_ + row_ * GM_ASTR + 64 + 16 * g);      \
+      const i32x8_t a_ = (i32x8_t){(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w,                \
+                                   (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w};               \
+      const int as_ = sas_[row_ * 12];                                                            \
+      acc[ms][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_, b0_, acc[ms][0], 0, 4, 0, as_, 0, bs0_); \
+      acc[ms][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_, b1_, acc[ms][1], 0, 4, 0, as_, 0, bs1_); \
+      acc[ms][2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_, b2_, acc[ms][2], 0, 4, 0, as_, 0, bs2_); \
+      acc[ms][3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_, b3_, acc[ms][3], 0, 4, 0, as_, 0, bs3_); \
+    }                                                                                             \
+  } while (0)
+  // An empty asm that reads and writes every accumulator ends each K step:
+  // without it the compiler sinks a step's MFMAs past the barrier into the
+  // next steps, keeping several steps' operands live at once (and spilling).
+#define GM_PIN_ACC()                                                                \
+  do {                                                                              \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                \
+    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) asm volatile("" : "+v"(acc[i_][j_])); \
+  } while (0)
+  // iteration for K step q = q0 + J (ring slot J = q % 3, scale group q0 / 3):
+  // A of step q+1 goes to LDS, the loads of step q+2 refill the slot that held
+  // step q-1, step q computes.  The next scale group is loaded at J = 0 and
+  // stored at J = 2, before the barrier that precedes its first step.
+#define GM_ITER(J, JN, JL)                                                          \
+  do {                                                                              \
+    const int q = q0 + J;                                                           \
+    const int cur = q & 1;                                                          \
+    GM_STORE(JN, cur ^ 1);                                                          \
+    GM_LOAD(JL, q + 2);                                                             \
+    if (J == 0) GM_GLOAD(q0 / 3 + 1);                                               \
+    GM_STEP(J, cur, gb, J);                                                         \
+    if (J == 2) GM_GSTORE(gb ^ 1);                                                  \
+    GM_PIN_ACC();                                                                   \
+    __syncthreads();                                                                \
+  } while (0)
 
-  // ---- epilogue through LDS (reuses the operand buffers)
-  float* sh = reinterpret_cast<float*>(smem);
+  GM_GLOAD(0);
+  GM_LOAD(0, 0);
+  GM_LOAD(1, 1);
+  GM_GSTORE(0);
+  GM_STORE(0, 0);
+  __syncthreads();
+  int q0 = 0, gb = 0;
+  for (; q0 + 3 <= nks; q0 += 3, gb ^= 1) {
+    GM_ITER(0, 1, 2);
+    GM_ITER(1, 2, 0);
+    GM_ITER(2, 0, 1);
+  }
+  // K-step tail: the ring is back at slot 0 here.
+  const int rem = nks - q0;
+  if (rem >= 1) GM_ITER(0, 1, 2);
+  if (rem >= 2) GM_ITER(1, 2, 0);
+#undef GM_ITER
+#undef GM_STEP
+#undef GM_GLOAD
+#undef GM_GSTORE
+#undef GM_PIN_ACC
+#undef GM_BOP
+#undef GM_LOAD
+#undef GM_STORE
+
+  // ---- epilogue (accumulator element i of sub-tile (ms, ns) is row
+  // 16 ms + 4 g + i, weight row 16 ns + lane%16 of the wave's 64)
   if (MODE == GM_GATEUP) {
-    // h tile: 64 rows x 64 columns (i0 = ntile*64), row stride 68 floats
-    constexpr int HS = 68;
+    // The wave's 32 h columns (i0 = ntile*128 + 32*wave) are one MX block per
+    // row: stage h = silu(gate) * up in the wave's own LDS area, then lane r
+    // quantises row r.  (The loop's last barrier freed the A buffers.)
+    float* sh = reinterpret_cast<float*>(smem) + wv * GM_BM * GM_HSTR;
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms)
+    for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
       for (int nsub = 0; nsub < 2; ++nsub)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float gv = acc[ms][nsub][i], uv = acc[ms][nsub + 2][i];
-          const int r = wm * 32 + ms * 16 + 4 * g + i;
-          const int c = 32 * wn + 16 * nsub + c16;
-          sh[r * HS + c] = gv / (1.0f + expf(-gv)) * uv;
+          sh[(16 * ms + 4 * g + i) * GM_HSTR + 16 * nsub + c16] = gv / (1.0f + expf(-gv)) * uv;
         }
     __syncthreads();
-    if (tid < 128) {  // one 32-block per thread: row tid/2, block tid%2
-      const int r = tid / 2, b = tid % 2;
-      const int m = m0 + r;
-      if (m < m_end) {
-        float v[32];
+    const int m = m0 + lane;
+    if (m < m_end) {
+      float v[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = sh[r * HS + 32 * b + i];
-        const int i0 = ntile * 64 + 32 * b;
-        const uint32_t sb = quant_block32(v, ga.hq + (int64_t)m * ga.I + i0);
-        ga.hs[(int64_t)m * (ga.I / 32) + i0 / 32] = (uint8_t)sb;
-      }
+      for (int i = 0; i < 32; ++i) v[i] = sh[lane * GM_HSTR + i];
+      const int i0 = ntile * 128 + 32 * wv;
+      const uint32_t sb = quant_block32(v, ga.hq + (int64_t)m * ga.I + i0);
+      ga.hs[(int64_t)m * (ga.I / 32) + i0 / 32] = (uint8_t)sb;
     }
   } else {
-    // y tile: 64 rows x 128 columns, row stride 132 floats
-    constexpr int YS = 132;
+    // y rows straight from the accumulators: 16 lanes store 64 contiguous bytes
+    float* yb = ga.y + ntile * 256 + 64 * wv + c16;
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms)
+    for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-      for (int ns = 0; ns < 4; ++ns)
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 16 * ms + 4 * g + i;
+        if (m < m_end) {
+          float* yr = yb + (int64_t)m * ga.H;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = wm * 32 + ms * 16 + 4 * g + i;
-          const int c = 64 * wn + 16 * ns + c16;
-          sh[r * YS + c] = acc[ms][ns][i];
+          for (int ns = 0; ns < 4; ++ns) yr[16 * ns] = acc[ms][ns][i];
         }
-    __syncthreads();
-    // 64 rows x 32 float4 = 2048 stores, 8 per thread
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int idx = q * 256 + tid;
-      const int r = idx / 32, c4 = idx % 32;
-      const int m = m0 + r;
-      if (m < m_end)
-        *reinterpret_cast<float4*>(ga.y + (int64_t)m * ga.H + ntile * 128 + 4 * c4) =
-            *reinterpret_cast<const float4*>(sh + r * YS + 4 * c4);
-    }
+      }
   }
 }
 
@@ -357,6 +446,8 @@ hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
   float* y = reinterpret_cast<float*>(ws + pl.off_y);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + pl.off_tiles);
   int32_t* n_tiles = tiles + 2 * pl.max_tiles;
+  int32_t* work_a = n_tiles + 1;                            // gate/up work items
+  int32_t* work_b = work_a + (size_t)pl.max_tiles * (I / 128);  // down work items
   const int32_t* offsets = reinterpret_cast<const int32_t*>(ws + pl.off_offsets);
   const int32_t* perm = reinterpret_cast<const int32_t*>(ws + pl.off_perm);
   const int32_t* pos = reinterpret_cast<const int32_t*>(ws + pl.off_pos);
@@ -365,7 +456,7 @@ hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
   quant_x_kernel<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(reinterpret_cast<const uint16_t*>(x), xq, xs, nblk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  build_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, tiles, n_tiles);
+  build_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, tiles, n_tiles, work_a, I / 128, work_b, H / 256);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   GemmArgs ga{};
@@ -379,20 +470,24 @@ hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
   ga.H = H;
   ga.I = I;
   ga.k = k;
-  // gate/up: A = x_q gathered by token, N = I in 64-column tiles (gate + up rows)
+  // gate/up: A = x_q gathered by token, N = I in 128-column tiles (gate + up rows)
   ga.aq = xq;
   ga.as = xs;
+  ga.a_bytes = (int64_t)T * H;
   ga.hq = hq;
   ga.hs = hs;
-  ga.n_ntiles = I / 64;
+  ga.n_ntiles = I / 128;
+  ga.work = work_a;
   ga.total_wg = (pl.max_tiles * ga.n_ntiles + 7) / 8 * 8;  // a multiple of 8 keeps the XCD mapping a bijection
   grouped_mx_gemm_kernel<GM_GATEUP><<<ga.total_wg, 256, 0, st>>>(ga);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  // down: A = h_q by sorted position, N = H in 128-row tiles
+  // down: A = h_q by sorted position, N = H in 256-row tiles
   ga.aq = hq;
   ga.as = hs;
+  ga.a_bytes = (int64_t)pl.P * I;
   ga.y = y;
-  ga.n_ntiles = H / 128;
+  ga.n_ntiles = H / 256;
+  ga.work = work_b;
   ga.total_wg = (pl.max_tiles * ga.n_ntiles + 7) / 8 * 8;
   grouped_mx_gemm_kernel<GM_DOWN><<<ga.total_wg, 256, 0, st>>>(ga);
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -400,8 +495,10 @@ hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
 }
 
 bool mfma_supported(const ft_moe_desc& d, int T) {
-  return d.w_dtype == FT_MXFP4 && d.act_dtype == FT_BF16 && T >= MFMA_MIN_TOKENS && d.hidden % 128 == 0 &&
-         d.inter % 128 == 0;
+  return d.w_dtype == FT_MXFP4 && d.act_dtype == FT_BF16 && T >= MFMA_MIN_TOKENS && d.hidden % 256 == 0 &&
+         d.inter % 128 == 0 && (int64_t)T * d.hidden < (1ll << 31) &&
+         (int64_t)T * d.top_k * d.inter < (1ll << 31) &&
+         record_layout(d.hidden, d.inter, FT_MXFP4).bytes < (1ll << 31);
 }
 
 }  // namespace ft

@@ -136,7 +136,7 @@ int ft_expert_upload(void* pool_base, int64_t expert_stride, int64_t record_byte
  * The record of expert e is at pool_base + slot * expert_stride where slot =
  * slot_ids[t*k+j] (slot_ids nullable -> slot = e).  Masked-out experts are
  * never read.  expert_mask: bitset u32 [ceil(E/32)], nullable = all.
- * out: fp32 [T, H], fully overwritten.
+ * out: fp32 [T, H], fully overwritten; it must not overlap any input.
  * Decode-sized calls (few pairs per expert) run as bandwidth-bound grouped
  * GEMV; large MXFP4 calls run on gfx950 scaled MFMA with activations
  * quantised to MXFP8 (E4M3, E8M0 per 32) first.

@@ -14,18 +14,20 @@
 // reads h as two bf16 terms h = hi + lo (|h - hi - lo| <= 2^-18 |h|).
 //
 // Two kernels per layer:
-//  1. gate/up: grid = (distinct expert d) x (16-row tile of I).  Each
+//  1. gate/up: grid = (distinct expert d) x (8-row tile of I).  Each
 //     workgroup derives the expert grouping of the <= 64 (token, rank) pairs
 //     itself (no separate permutation launch), splits K over its 4 waves,
 //     sums the wave partials in LDS in a fixed order, applies SwiGLU and
 //     stores g * h (gate of the pair folded in).
-//  2. down + combine: grid = 16-row tiles of H.  The gate is folded into h
-//     (h' = g_tj * h_tj), so out[t] = sum over routed experts of D_e h'_t is
+//  2. down + combine: grid = 16-row tiles of H x 2 halves of the expert
+//     list.  The gate is folded into h (h' = g_tj * h_tj), so the part of
+//     out[t] = sum over routed experts of D_e h'_t that one workgroup owns is
 //     one accumulation: every (expert, K chunk) job of the tile adds into the
 //     same 16 x 16 (rows x tokens) accumulator.  Jobs are dealt to the 16
 //     waves round-robin and the wave partials are summed in LDS in a fixed
-//     order, so the result is deterministic without any cross-workgroup
-//     synchronisation or floating-point atomics.
+//     order; the two halves are added into the output, which the gate/up
+//     kernel zeroed.  Two addends onto zero commute exactly in IEEE
+//     arithmetic, so the result does not depend on which half lands first.
 // The combine is the weighted sum of partial expert outputs that the pages
 // rely on for exactness (FreeToken explainer page, "how" section).
 #include "common.hpp"
@@ -203,34 +205,42 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 }
 
 // -------------------------------------------------------------- gate / up --
+// A workgroup covers 8 rows of h for one expert: the 16 A-operand rows are the
+// 8 gate rows (tile rows 0-7) and the same 8 up rows (tile rows 8-15), so one
+// accumulator chain carries both and the grid has I/8 tiles per expert.
 template <int WD, int UNROLL>
 __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P,
     int k, const void* __restrict__ pool, int64_t stride, const int32_t* __restrict__ slot_ids,
-    const float* __restrict__ gates, uint16_t* __restrict__ hbuf, int H, int I, int E) {
+    const float* __restrict__ gates, uint16_t* __restrict__ hbuf, float* __restrict__ out, int T, int H, int I,
+    int E) {
   __shared__ PairInfo pi;
-  __shared__ f32x4_t red[DM_WAVES][2][64];
+  __shared__ f32x4_t red[DM_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
-  const int n_rt = I / 16;
+  // out starts at zero: the down kernel adds its two halves into it
+  for (int i = blockIdx.x * DM_THREADS + tid; i < T * H / 4; i += gridDim.x * DM_THREADS)
+    reinterpret_cast<float4*>(out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int n_rt = I / 8;
   const int d = blockIdx.x / n_rt, rt = blockIdx.x % n_rt;
   if (wv == 0) dm_group_pairs(ids, mask, P, E, d, &pi);
   __syncthreads();
   if (d >= pi.n_distinct) return;
   const int e = pi.expert, np = pi.npairs;
   const int slot = slot_ids ? slot_ids[pi.pair[0]] : e;
-  const int row = rt * 16 + col;  // A-operand row of this lane
   if (slot < 0) {  // failed lookup: poison this expert's h, never read out of bounds
     if (wv == 0)
-      for (int q = lane; q < np * 16; q += 64) {
-        const int p = pi.pair[q / 16];
-        hbuf[(int64_t)p * 2 * I + rt * 16 + (q % 16)] = 0x7FC0u;
-        hbuf[(int64_t)p * 2 * I + I + rt * 16 + (q % 16)] = 0u;
+      for (int q = lane; q < np * 8; q += 64) {
+        const int p = pi.pair[q / 8];
+        hbuf[(int64_t)p * 2 * I + rt * 8 + (q % 8)] = 0x7FC0u;
+        hbuf[(int64_t)p * 2 * I + I + rt * 8 + (q % 8)] = 0u;
       }
     return;
   }
   const uint8_t* rec = reinterpret_cast<const uint8_t*>(pool) + (int64_t)slot * stride;
   const RecordLayout L = record_layout(H, I, WD);
   const WMat Gm = wmat<WD>(rec, L, 0, H), Um = wmat<WD>(rec, L, 1, H);
+  const WMat& Wl = (col < 8) ? Gm : Um;   // this lane's A-operand matrix
+  const int row = rt * 8 + (col & 7);     // and row
   constexpr int CK = Chunk<WD>::K, NM = Chunk<WD>::NM;
   const int nchunk = H / CK;
 
@@ -239,16 +249,15 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     const int t = tok_ok ? pi.pair[tg + col] / k : 0;
     const float gate = (tok_ok && wv == 0) ? gates[pi.pair[tg + col]] : 0.f;  // issued before the stream
     const uint16_t* xr = x + (int64_t)t * H;
-    f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = wv; c0 < nchunk; c0 += DM_WAVES * UNROLL) {
-      RawW<WD> rg[UNROLL], ru[UNROLL];
+      RawW<WD> rw[UNROLL];
       uint4 xb[UNROLL][NM];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const int c = c0 + u * DM_WAVES;
         if (c < nchunk) {
-          load_raw<WD>(Gm, row, c, g, rg[u]);
-          load_raw<WD>(Um, row, c, g, ru[u]);
+          load_raw<WD>(Wl, row, c, g, rw[u]);
 #pragma unroll
           for (int j = 0; j < NM; ++j)
             xb[u][j] = tok_ok ? *reinterpret_cast<const uint4*>(xr + kofs<WD>(c, j, g)) : make_uint4(0, 0, 0, 0);
@@ -259,38 +268,35 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
         const int c = c0 + u * DM_WAVES;
         if (c < nchunk) {
 #pragma unroll
-          for (int j = 0; j < NM; ++j) {
-            const bf16x8_t b = as_bf16x8(xb[u][j]);
-            ag = mfma(decode_a<WD>(rg[u], j), b, ag);
-            au = mfma(decode_a<WD>(ru[u], j), b, au);
-          }
+          for (int j = 0; j < NM; ++j) acc = mfma(decode_a<WD>(rw[u], j), as_bf16x8(xb[u][j]), acc);
         }
       }
     }
-    red[wv][0][lane] = ag;
-    red[wv][1][lane] = au;
+    red[wv][lane] = acc;
     __syncthreads();
     if (wv == 0) {
-      f32x4_t sg = red[0][0][lane], su = red[0][1][lane];
+      f32x4_t s = red[0][lane];
 #pragma unroll
-      for (int w = 1; w < DM_WAVES; ++w) { sg += red[w][0][lane]; su += red[w][1][lane]; }
-      if (tok_ok) {
-        const int p = pi.pair[tg + col];
-        uint16_t hi[4], lo[4];
+      for (int w = 1; w < DM_WAVES; ++w) s += red[w][lane];
+      red[0][lane] = s;  // lanes 32-63 (tile rows 8-15) hold the up rows of lanes 0-31
+    }
+    __syncthreads();
+    if (wv == 0 && g < 2 && tok_ok) {
+      const f32x4_t sg = red[0][lane], su = red[0][lane + 32];
+      const int p = pi.pair[tg + col];
+      uint16_t hi[4], lo[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gv = sg[i] * Gm.tscale, uv = su[i] * Um.tscale;
-          const float h = gate * (gv / (1.0f + expf(-gv)) * uv);
-          const uint32_t hb = bf16_rne_bits(h);
-          hi[i] = (uint16_t)hb;
-          lo[i] = (uint16_t)bf16_rne_bits(h - __uint_as_float(hb << 16));
-        }
-        // output rows of this lane: rt*16 + 4*g + i
-        uint16_t* hp = hbuf + (int64_t)p * 2 * I + rt * 16 + 4 * g;
-        *reinterpret_cast<uint2*>(hp) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-        *reinterpret_cast<uint2*>(hp + I) =
-            make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+      for (int i = 0; i < 4; ++i) {
+        const float gv = sg[i] * Gm.tscale, uv = su[i] * Um.tscale;
+        const float h = gate * (gv / (1.0f + expf(-gv)) * uv);
+        const uint32_t hb = bf16_rne_bits(h);
+        hi[i] = (uint16_t)hb;
+        lo[i] = (uint16_t)bf16_rne_bits(h - __uint_as_float(hb << 16));
       }
+      // h rows of this lane: rt*8 + 4*g + i
+      uint16_t* hp = hbuf + (int64_t)p * 2 * I + rt * 8 + 4 * g;
+      *reinterpret_cast<uint2*>(hp) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+      *reinterpret_cast<uint2*>(hp + I) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
     }
     __syncthreads();
   }
@@ -345,14 +351,16 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
   __shared__ DownInfo di;
   __shared__ f32x4_t red[DD_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
-  const int rt = blockIdx.x;
+  // two workgroups per 16-row tile: half s takes the distinct experts d = s, s+2, ...
+  const int rt = blockIdx.x >> 1, half = blockIdx.x & 1;
   if (wv == 0) dd_group_all(ids, mask, slot_ids, P, k, E, &di);
   __syncthreads();
   const int nd = di.n_distinct;
+  const int ndh = (nd - half + 1) / 2;  // experts of this half
   const int row = rt * 16 + col;
   constexpr int CK = Chunk<WD>::K, NM = Chunk<WD>::NM;
   const int nchunk = I / CK;
-  const int njobs = nd * nchunk;
+  const int njobs = ndh * nchunk;
   const RecordLayout L = record_layout(H, I, WD);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   bool poisoned = false;
@@ -365,7 +373,7 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
       const int job = j0 + u * DD_WAVES;
       ts[u] = 0.f;
       if (job < njobs) {
-        const int d = job / nchunk, c = job % nchunk;
+        const int d = half + 2 * (job / nchunk), c = job % nchunk;
         const int slot = di.slot[d];
         const int p = (col < T) ? di.pair[d][col] : -1;
         if (slot < 0) {
@@ -407,8 +415,11 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
     f32x4_t s = red[0][lane];
 #pragma unroll
     for (int w = 1; w < DD_WAVES; ++w) s += red[w][lane];
+    // exactly two addends land on each zeroed output element, and
+    // (0 + a) + b == (0 + b) + a in IEEE arithmetic: the sum is deterministic
+    float* o = out + (int64_t)col * H + rt * 16 + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[(int64_t)col * H + rt * 16 + 4 * g + i] = s[i];
+    for (int i = 0; i < 4; ++i) unsafeAtomicAdd(o + i, s[i]);
   }
 }
 
@@ -419,12 +430,12 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
   const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k;
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + pl.off_h);
   const int nd_max = pl.P < E ? pl.P : E;
-  dec_gateup_kernel<WD, 4><<<nd_max * (I / 16), DM_THREADS, 0, st>>>(
-      reinterpret_cast<const uint16_t*>(x), ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, H, I,
-      E);
+  dec_gateup_kernel<WD, (WD == FT_BF16) ? 6 : 4><<<nd_max * (I / 8), DM_THREADS, 0, st>>>(
+      reinterpret_cast<const uint16_t*>(x), ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out,
+      pl.T, H, I, E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  dec_down_kernel<WD, (WD == FT_BF16) ? 4 : 2><<<H / 16, DD_THREADS, 0, st>>>(hbuf, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids,
+  dec_down_kernel<WD, (WD == FT_BF16) ? 3 : 2><<<(H / 16) * 2, DD_THREADS, 0, st>>>(hbuf, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids,
                                                         out, pl.T, H, I, E);
   return hipGetLastError();
 }

@@ -351,12 +351,125 @@ __global__ void __launch_bounds__(256) route_logits_tiled_kernel(const void* __r
   }
 }
 
+// Many tokens on the fp64 matrix cores: v_mfma_f64_16x16x4_f64 multiplies
+// 16 tokens x 4 h by 4 h x 16 experts into a 16 x 16 fp64 tile (lane l holds
+// A[l%16][l/16] and B[l/16][l%16]; D[l/16 + 4i][l%16] in its 4 results, as
+// measured on the device).
+// Products of widened bf16 / fp32 operands are exact in fp64; only the sums
+// round.  A workgroup (2 x 2 waves) computes 64 tokens x 64 experts, each
+// wave 32 x 32 (2 x 2 tiles).  Along h, 32-element chunks are consumed in 8
+// MFMA steps with lane group g taking h = 8g + s at step s, so every lane
+// loads 8 consecutive elements of its token row and of its expert row per
+// chunk (16 B of bf16); the next chunk's raw loads are in flight while the
+// current one computes.  Every expert column goes through the same sequence
+// of operations, so bitwise-equal expert rows give bitwise-equal logits.
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr int RM_T = 64, RM_E = 64;
+
+template <int DT> struct Raw8;
+template <> struct Raw8<FT_BF16> { uint4 q; };
+template <> struct Raw8<FT_F32> { uint4 q[2]; };
+
+template <int DT>
+__device__ __forceinline__ void raw8_load(const void* base, int64_t i, Raw8<DT>& r) {
+  if constexpr (DT == FT_BF16) {
+    r.q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + i);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + i);
+    r.q[0] = p[0];
+    r.q[1] = p[1];
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ double raw8_get(const Raw8<DT>& r, int j) {
+  if constexpr (DT == FT_BF16) {
+    const uint32_t w = (j < 2) ? r.q.x : (j < 4) ? r.q.y : (j < 6) ? r.q.z : r.q.w;
+    return (double)((j & 1) ? bf16_hi(w) : bf16_lo(w));
+  } else {
+    const uint4 q = r.q[j >> 2];
+    const uint32_t w = ((j & 3) == 0) ? q.x : ((j & 3) == 1) ? q.y : ((j & 3) == 2) ? q.z : q.w;
+    return (double)__uint_as_float(w);
+  }
+}
+
+template <int XDT, int WDT>
+__global__ void __launch_bounds__(256) route_logits_mfma_kernel(const void* __restrict__ x, const void* __restrict__ wr,
+                                                                double* __restrict__ logits, int T, int H, int E) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+  const int tw = blockIdx.x * RM_T + (wv >> 1) * 32, ew = blockIdx.y * RM_E + (wv & 1) * 32;
+  int64_t xrow[2], wrow[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    int t = tw + 16 * m + c;
+    if (t >= T) t = T - 1;  // rows past the end repeat the last row (never stored)
+    int e = ew + 16 * m + c;
+    if (e >= E) e = E - 1;
+    xrow[m] = (int64_t)t * H + 8 * g;
+    wrow[m] = (int64_t)e * H + 8 * g;
+  }
+  f64x4_t acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) acc[m][n] = (f64x4_t){0.0, 0.0, 0.0, 0.0};
+  Raw8<XDT> ax[2];
+  Raw8<WDT> bw[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    raw8_load<XDT>(x, xrow[m], ax[m]);
+    raw8_load<WDT>(wr, wrow[m], bw[m]);
+  }
+  const int nch = H / 32;
+  for (int ch = 0; ch < nch; ++ch) {
+    Raw8<XDT> cx[2] = {ax[0], ax[1]};
+    Raw8<WDT> cw[2] = {bw[0], bw[1]};
+    if (ch + 1 < nch) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        raw8_load<XDT>(x, xrow[m] + 32 * (ch + 1), ax[m]);
+        raw8_load<WDT>(wr, wrow[m] + 32 * (ch + 1), bw[m]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const double a0 = raw8_get<XDT>(cx[0], s), a1 = raw8_get<XDT>(cx[1], s);
+      const double b0 = raw8_get<WDT>(cw[0], s), b1 = raw8_get<WDT>(cw[1], s);
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int e = ew + 16 * n + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tw + 16 * m + g + 4 * i;
+        if (t < T && e < E) logits[(int64_t)t * E + e] = acc[m][n][i];
+      }
+    }
+}
+
 hipError_t launch_route(const ft_moe_desc& d, const void* x, int T, const void* wr,
                         const float* sel_bias, int32_t* ids, float* gates, double* logits,
                         hipStream_t st) {
   dim3 grid((T + RL_TT - 1) / RL_TT, (d.n_experts + RL_TE - 1) / RL_TE);
   const int xd = d.act_dtype, wd = d.router_dtype, H = d.hidden, E = d.n_experts;
-  if (xd == FT_BF16 && wd == FT_BF16)
+  dim3 mgrid((T + RM_T - 1) / RM_T, (E + RM_E - 1) / RM_E);
+  if (H % 32 == 0) {  // matrix-core path
+    if (xd == FT_BF16 && wd == FT_BF16)
+      route_logits_mfma_kernel<FT_BF16, FT_BF16><<<mgrid, 256, 0, st>>>(x, wr, logits, T, H, E);
+    else if (xd == FT_F32 && wd == FT_F32)
+      route_logits_mfma_kernel<FT_F32, FT_F32><<<mgrid, 256, 0, st>>>(x, wr, logits, T, H, E);
+    else if (xd == FT_BF16 && wd == FT_F32)
+      route_logits_mfma_kernel<FT_BF16, FT_F32><<<mgrid, 256, 0, st>>>(x, wr, logits, T, H, E);
+    else
+      route_logits_mfma_kernel<FT_F32, FT_BF16><<<mgrid, 256, 0, st>>>(x, wr, logits, T, H, E);
+  } else if (xd == FT_BF16 && wd == FT_BF16)
     route_logits_tiled_kernel<FT_BF16, FT_BF16><<<grid, 256, 0, st>>>(x, wr, logits, T, H, E);
   else if (xd == FT_F32 && wd == FT_F32)
     route_logits_tiled_kernel<FT_F32, FT_F32><<<grid, 256, 0, st>>>(x, wr, logits, T, H, E);

@@ -44,26 +44,29 @@ def run_layer(cfg, layer, step, T, mask=None, x=None, wr=None):
 
 
 # --------------------------------------------------------------- routing --
-@pytest.mark.parametrize("cfg,T", [(C1, 16), (C2, 4), (C3, 4), (C5, 4), (C1, 1), (C2, 37)])
+@pytest.mark.parametrize("cfg,T", [(C1, 16), (C2, 4), (C3, 4), (C5, 4), (C1, 1), (C2, 37), (C1, 40), (C5, 70)])
 def test_route_matches_oracle(cfg, T):
     print(f"route {cfg.name} T={T}", flush=True)
     check_route(LayerData(cfg, 0, 0, T))
 
 
-def test_route_ties_zero_router_and_duplicate_rows():
+@pytest.mark.parametrize("T", [4, 40])
+def test_route_ties_zero_router_and_duplicate_rows(T):
+    """Ties go to the lowest ids, at decode size (T <= 16) and on the
+    many-token path (T > 16) alike."""
     cfg = C2
-    ld = LayerData(cfg, 0, 1, 4, wr=np.zeros((cfg.n_experts, cfg.hidden), dtype=np.uint16))
+    ld = LayerData(cfg, 0, 1, T, wr=np.zeros((cfg.n_experts, cfg.hidden), dtype=np.uint16))
     ids, gates, _ = ld.gpu_route()
-    np.testing.assert_array_equal(ids.cpu().numpy(), np.tile(np.arange(cfg.top_k), (4, 1)))
+    np.testing.assert_array_equal(ids.cpu().numpy(), np.tile(np.arange(cfg.top_k), (T, 1)))
     np.testing.assert_allclose(gates.cpu().numpy(), 1.0 / cfg.top_k, rtol=0, atol=1e-7)
     wr = synth.router_weights(cfg, 3).copy()
     for dup in (17, 64, 101):
         wr[dup] = wr[5]
-    x = synth.activations(cfg, 0, 3, 8)
+    x = synth.activations(cfg, 0, 3, 2 * T)
     # make expert 5 win for every token so its duplicates are selected too
     wr[5] = wr[17] = wr[64] = wr[101] = (synth.f32_to_bf16_bits(np.full(cfg.hidden, 0.0, np.float32)))
     x = x.copy()
-    check_route(LayerData(cfg, 3, 0, 8, x=x, wr=wr))
+    check_route(LayerData(cfg, 3, 0, 2 * T, x=x, wr=wr))
 
 
 def test_route_selection_bias_follows_trace():

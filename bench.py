@@ -27,6 +27,25 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
+# Measured HBM bytes per ft_moe_forward call of the default decode workload
+# (bf16, H2048, E128, top-8, batch 1): rocprofv3 FETCH_SIZE and WRITE_SIZE of
+# the two decode kernels per call, scaled by what the same counters read for a
+# plain 256 MiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by the
+# SHA-256 prefix of the kernel source the counters were taken on: any change to
+# that source reports null until the counters are taken again.
+DECODE_TRAFFIC = {"7384c61bf7d6104f": 75894374}
+DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_expert_softmax_amd", "csrc",
+                          "decode_mfma.hip")
+
+
+def measured_decode_traffic(cfg_name, batch):
+    import hashlib
+    if cfg_name != "decode_bf16_h2048_e128" or batch != 1:
+        return None
+    with open(DECODE_SRC, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()[:16]
+    return DECODE_TRAFFIC.get(h)
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -250,7 +269,8 @@ def main():
         "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "ft_moe_forward (expert GEMV)",
                      "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_decode_traffic(cfg.name, B),
                      "bytes_per_launch": round(float(np.mean(fwd_bytes))), "avg_launch_us": round(float(np.mean(fwd_ms)) * 1e3, 2),
                      "distinct_experts_per_call": round(float(np.mean(d_meas)), 2)},
     }

@@ -152,11 +152,6 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return r;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16_trunc(float a, float b) {
-  // exact values only (the low 16 bits are zero): take the upper halves
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-}
-
 // 8 E2M1 codes (one dword) -> 8 bf16, each times `scale` (a power of two).
 __device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t q, float scale) {
   union { bf16x2_t h[4]; bf16x8_t v; } u;
@@ -167,16 +162,17 @@ __device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t q, float scale) {
   return u.v;
 }
 
-// 8 E2M1 codes times an arbitrary fp32 block scale (exact products) -> bf16.
+// 8 E2M1 codes times an arbitrary fp32 block scale (exact products, so the
+// bf16 conversion, one v_cvt_pk_bf16_f32 per pair, does not round) -> bf16.
 __device__ __forceinline__ bf16x8_t fp4x8_bf16_mul(uint32_t q, float s) {
-  uint4 o;
-  uint32_t* op = reinterpret_cast<uint32_t*>(&o);
+  bf16x8_t r;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q >> (8 * b), 1.0f, 0);
-    op[b] = pack_bf16_trunc(v[0] * s, v[1] * s);
+    r[2 * b] = (__bf16)(v[0] * s);
+    r[2 * b + 1] = (__bf16)(v[1] * s);
   }
-  return as_bf16x8(o);
+  return r;
 }
 
 // A operand (weights) of MFMA j of a chunk.

@@ -61,3 +61,61 @@ def test_prefill_full_chunk_routing_and_sampled_outputs():
     sample = [0, 1234, 5000, 8191]
     _, _, _, _, _, err = run_prefill(cfg, T, 2, 0, sample=sample)
     print(f"  sampled max rel err {err:.3g}")
+
+
+MID = MoEConfig("prefill_mid_mxfp4", 91, hidden=512, inter=384, n_experts=16, top_k=4, act_dtype=BF16,
+                router_dtype=BF16, w_dtype=MXFP4, n_layers=1)
+
+
+def test_prefill_k_tails_and_several_weight_tiles():
+    """H 512 (four 128-K steps: one full group of three plus a tail), I 384
+    (three steps, no tail), two gate/up and two down weight tiles, ragged
+    expert row counts over 777 tokens."""
+    print("prefill mid T=777", flush=True)
+    _, _, _, _, _, err = run_prefill(MID, 777, 0, 3)
+    print(f"  max rel err {err:.3g}")
+
+
+def test_prefill_slot_indirection_matches_identity_slots():
+    """The forward reads expert e at pool + slot_ids[pair] * stride: records
+    moved to other slots give bitwise the same output."""
+    cfg, T = SMALL, 320
+    ld, ids, gates, out, _, _ = run_prefill(cfg, T, 0, 9)
+    E = cfg.n_experts
+    perm = np.random.default_rng(5).permutation(E)          # expert e lives in slot perm[e]
+    pool2 = torch.full((E, ld.stride), 0xFF, dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        pool2[perm[e]].copy_(ld.pool[e])
+    slots = torch.from_numpy(perm[ids.cpu().numpy()].astype(np.int32)).cuda()
+    moved = ld.gpu_forward(ids, gates, slot_ids=slots, pool=pool2).cpu().numpy()
+    assert np.array_equal(moved, out)
+
+
+def test_prefill_masked_out_experts_are_never_read():
+    """Poison (NaN) the records of the masked-out experts: the masked output
+    stays finite and equals the masked output over the intact pool."""
+    cfg, T = SMALL, 300
+    ld, ids, gates, _, _, _ = run_prefill(cfg, T, 0, 11)
+    m = np.array([0b01011001], dtype=np.uint32)
+    ref = ld.gpu_forward(ids, gates, mask=m).cpu().numpy()
+    for e in range(cfg.n_experts):
+        if not (int(m[0]) >> e) & 1:
+            ld.pool[e].fill_(0xFF)
+    got = ld.gpu_forward(ids, gates, mask=m).cpu().numpy()
+    assert not np.isnan(got).any()
+    assert np.array_equal(got, ref)
+
+
+def test_prefill_threshold_general_path_below_256_tokens():
+    """255 tokens take the general (fp32 GEMV) path with unquantised
+    activations; 256 take the matrix cores. Both against the oracle."""
+    cfg = SMALL
+    ld = LayerData(cfg, 0, 13, 255)
+    ids, gates, _ = ld.gpu_route()
+    o_ids, _, _ = ld.oracle_route()
+    np.testing.assert_array_equal(ids.cpu().numpy(), o_ids)
+    ld.build_pool(o_ids.ravel())
+    out = ld.gpu_forward(ids, gates).cpu().numpy()
+    ref, _, _ = ld.oracle_layer()
+    assert max_rel_err(out, ref) <= 1e-2
+    run_prefill(cfg, 256, 0, 13)

@@ -30,10 +30,10 @@ HBM_PEAK_GBS = 8000.0
 # Measured HBM bytes per ft_moe_forward call of the default decode workload
 # (bf16, H2048, E128, top-8, batch 1): rocprofv3 FETCH_SIZE and WRITE_SIZE of
 # the two decode kernels per call, scaled by what the same counters read for a
-# plain 256 MiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by the
+# plain 256 MiB device copy (FETCH_SIZE x 1.9997, WRITE_SIZE x 1.0).  Keyed by the
 # SHA-256 prefix of the kernel source the counters were taken on: any change to
 # that source reports null until the counters are taken again.
-DECODE_TRAFFIC = {"7384c61bf7d6104f": 75894374}
+DECODE_TRAFFIC = {"9f17590dcc54b428": 75883833}
 DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_expert_softmax_amd", "csrc",
                           "decode_mfma.hip")
 

@@ -204,7 +204,19 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 // A workgroup covers 8 rows of h for one expert: the 16 A-operand rows are the
 // 8 gate rows (tile rows 0-7) and the same 8 up rows (tile rows 8-15), so one
 // accumulator chain carries both and the grid has I/8 tiles per expert.
-template <int WD, int UNROLL>
+//
+// Two options for the fp4 formats, where a chunk's codes are only 16 bytes
+// per lane and every further small load per chunk costs as much L1 work:
+//  XL:  the token group's activation rows are staged once in LDS (dynamic
+//       shared memory, row stride H + 8) and the MFMA's B operand is read
+//       from there, instead of loading it from memory for every chunk;
+//  GRP: each wave takes a contiguous quarter of the chunks, four at a time,
+//       and loads the block scales of those four chunks with one 16-byte
+//       (MXFP4) or two 16-byte (NVFP4) loads per lane instead of one or two
+//       byte loads per chunk.
+// Weight scales of MXFP4 for chunk c, lane group g: byte 4c + g of the row;
+// NVFP4: bytes 8c + 2g and 8c + 2g + 1.
+template <int WD, int UNROLL, bool XL, bool GRP>
 __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P,
     int k, const void* __restrict__ pool, int64_t stride, const int32_t* __restrict__ slot_ids,
@@ -240,33 +252,117 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
   constexpr int CK = Chunk<WD>::K, NM = Chunk<WD>::NM;
   const int nchunk = H / CK;
 
+  extern __shared__ uint4 xs_dyn[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(xs_dyn);
+  const int XS = H + 8;  // LDS row stride of the staged activations (elements)
+  // chunk of pass c0, step u: strided over the waves, or (GRP) a contiguous
+  // quarter per wave taken four chunks at a time
+  const int cpw = nchunk / DM_WAVES;
+  const int cbeg = GRP ? wv * cpw : wv, cend = GRP ? cbeg + cpw : nchunk;
+  const int cstep = GRP ? UNROLL : DM_WAVES * UNROLL, ustep = GRP ? 1 : DM_WAVES;
   for (int tg = 0; tg < np; tg += 16) {
     const bool tok_ok = tg + col < np;
     const int t = tok_ok ? pi.pair[tg + col] / k : 0;
     const float gate = (tok_ok && wv == 0) ? gates[pi.pair[tg + col]] : 0.f;  // issued before the stream
     const uint16_t* xr = x + (int64_t)t * H;
+    if constexpr (XL) {  // stage the group's activation rows (at most 16)
+      const int nt = (np - tg) < 16 ? (np - tg) : 16;
+      for (int q = tid; q < nt * (H / 8); q += DM_THREADS) {
+        const int r = q / (H / 8), c8 = q % (H / 8);
+        const int tr = pi.pair[tg + r] / k;
+        *reinterpret_cast<uint4*>(xs + r * XS + 8 * c8) = *reinterpret_cast<const uint4*>(x + (int64_t)tr * H + 8 * c8);
+      }
+    }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = wv; c0 < nchunk; c0 += DM_WAVES * UNROLL) {
-      RawW<WD> rw[UNROLL];
-      uint4 xb[UNROLL][NM];
+    if constexpr (!XL && !GRP) {
+      for (int c0 = wv; c0 < nchunk; c0 += DM_WAVES * UNROLL) {
+        RawW<WD> rw[UNROLL];
+        uint4 xb[UNROLL][NM];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int c = c0 + u * DM_WAVES;
-        if (c < nchunk) {
-          load_raw<WD>(Wl, row, c, g, rw[u]);
+        for (int u = 0; u < UNROLL; ++u) {
+          const int c = c0 + u * DM_WAVES;
+          if (c < nchunk) {
+            load_raw<WD>(Wl, row, c, g, rw[u]);
 #pragma unroll
-          for (int j = 0; j < NM; ++j)
-            xb[u][j] = tok_ok ? *reinterpret_cast<const uint4*>(xr + kofs<WD>(c, j, g)) : make_uint4(0, 0, 0, 0);
+            for (int j = 0; j < NM; ++j)
+              xb[u][j] = tok_ok ? *reinterpret_cast<const uint4*>(xr + kofs<WD>(c, j, g)) : make_uint4(0, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int c = c0 + u * DM_WAVES;
+          if (c < nchunk) {
+#pragma unroll
+            for (int j = 0; j < NM; ++j) acc = mfma(decode_a<WD>(rw[u], j), as_bf16x8(xb[u][j]), acc);
+          }
         }
       }
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int c = c0 + u * DM_WAVES;
-        if (c < nchunk) {
-#pragma unroll
-          for (int j = 0; j < NM; ++j) acc = mfma(decode_a<WD>(rw[u], j), as_bf16x8(xb[u][j]), acc);
+    } else {
+      // every wave runs the first pass (its chunks are guarded), so the barrier
+      // that publishes the staged activations is reached by all waves
+      int c0 = cbeg;
+      do {
+        RawW<WD> rw[UNROLL];
+        uint4 xb[XL ? 1 : UNROLL][NM];
+        if constexpr (GRP && WD != FT_BF16) {  // four consecutive chunks, scales in one go
+          const WMat& W = Wl;
+          uint4 sg[(WD == FT_MXFP4) ? 1 : 2];
+          if constexpr (WD == FT_MXFP4) {
+            sg[0] = *reinterpret_cast<const uint4*>(W.scales + (int64_t)row * (W.K / 32) + 4 * c0);
+          } else {
+            const uint4* sp = reinterpret_cast<const uint4*>(W.scales + (int64_t)row * (W.K / 16) + 8 * c0);
+            sg[0] = sp[0];
+            sg[1] = sp[1];
+          }
+          uint32_t sw[8];  // the group's scale words (constant indices only: stays in registers)
+          sw[0] = sg[0].x; sw[1] = sg[0].y; sw[2] = sg[0].z; sw[3] = sg[0].w;
+          if constexpr (WD == FT_NVFP4) { sw[4] = sg[1].x; sw[5] = sg[1].y; sw[6] = sg[1].z; sw[7] = sg[1].w; }
+  #pragma unroll
+          for (int u = 0; u < UNROLL; ++u) {
+            const int c = c0 + u;
+            rw[u].q = *reinterpret_cast<const uint4*>(W.codes + ((int64_t)row * W.K + c * 128 + 32 * g) / 2);
+            if constexpr (WD == FT_MXFP4) {
+              rw[u].s = (sw[u] >> (8 * g)) & 0xFFu;
+            } else {
+              const uint32_t lo = sw[2 * u], hi = sw[2 * u + 1];
+              rw[u].s = (((g >> 1) ? hi : lo) >> (16 * (g & 1))) & 0xFFFFu;
+            }
+          }
+        } else {
+  #pragma unroll
+          for (int u = 0; u < UNROLL; ++u) {
+            const int c = c0 + u * ustep;
+            if (c < cend) load_raw<WD>(Wl, row, c, g, rw[u]);
+          }
         }
-      }
+        if constexpr (!XL) {
+  #pragma unroll
+          for (int u = 0; u < UNROLL; ++u) {
+            const int c = c0 + u * ustep;
+            if (c < cend) {
+  #pragma unroll
+              for (int j = 0; j < NM; ++j)
+                xb[u][j] = tok_ok ? *reinterpret_cast<const uint4*>(xr + kofs<WD>(c, j, g)) : make_uint4(0, 0, 0, 0);
+            }
+          }
+        } else {
+          if (c0 == cbeg) __syncthreads();  // staged activations visible (first pass only)
+        }
+  #pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int c = c0 + u * ustep;
+          if (c < cend) {
+  #pragma unroll
+            for (int j = 0; j < NM; ++j) {
+              uint4 xv;
+              if constexpr (XL) xv = tok_ok ? *reinterpret_cast<const uint4*>(xs + col * XS + kofs<WD>(c, j, g)) : make_uint4(0, 0, 0, 0);
+              else xv = xb[u][j];
+              acc = mfma(decode_a<WD>(rw[u], j), as_bf16x8(xv), acc);
+            }
+          }
+        }
+        c0 += cstep;
+      } while (c0 < cend);
     }
     red[wv][lane] = acc;
     __syncthreads();
@@ -426,9 +522,24 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
   const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k;
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + pl.off_h);
   const int nd_max = pl.P < E ? pl.P : E;
-  dec_gateup_kernel<WD, (WD == FT_BF16) ? 6 : 4><<<nd_max * (I / 8), DM_THREADS, 0, st>>>(
-      reinterpret_cast<const uint16_t*>(x), ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out,
-      pl.T, H, I, E);
+  const int nchunk = H / ((WD == FT_BF16) ? 64 : 128);
+  const int tmax = pl.T < 16 ? pl.T : 16;
+  const size_t xl_bytes = (size_t)tmax * (H + 8) * 2;
+  const unsigned grid = nd_max * (I / 8);
+  bool done = false;
+  if constexpr (WD != FT_BF16) {
+    if (xl_bytes <= 56 * 1024 && nchunk % 16 == 0) {
+      dec_gateup_kernel<WD, 4, true, true><<<grid, DM_THREADS, xl_bytes, st>>>(
+          reinterpret_cast<const uint16_t*>(x), ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf,
+          out, pl.T, H, I, E);
+      done = true;
+    }
+  }
+  if (!done) {
+    dec_gateup_kernel<WD, (WD == FT_BF16) ? 6 : 4, false, false><<<grid, DM_THREADS, 0, st>>>(
+        reinterpret_cast<const uint16_t*>(x), ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out,
+        pl.T, H, I, E);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   dec_down_kernel<WD, (WD == FT_BF16) ? 3 : 2><<<(H / 16) * 2, DD_THREADS, 0, st>>>(hbuf, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids,

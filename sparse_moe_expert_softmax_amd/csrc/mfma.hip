@@ -123,36 +123,42 @@ __global__ void __launch_bounds__(256) quant_x_kernel(const uint16_t* __restrict
 // n_nt weight tiles each): item = tile | (ntile << 20), ordered by expert,
 // then weight tile, then row tile, so that the row tiles sharing a weight
 // tile run side by side and an expert's activation rows stay in one L2.
-// One workgroup.
+// One workgroup per expert.
 __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                            int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                                            int32_t* __restrict__ work_a, int n_nt_a,
                                                            int32_t* __restrict__ work_b, int n_nt_b) {
-  __shared__ int32_t start[1025];
-  if (threadIdx.x == 0) {
+  // Workgroup b writes expert b's entries; every workgroup first forms the
+  // exclusive prefix sum of the per-expert tile counts (E <= 1024): wave scans
+  // of 64 lanes, then a scan of the wave totals.
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t s_start, s_mt;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, eb = blockIdx.x;
+  const int cnt = (t < E) ? offsets[t + 1] - offsets[t] : 0;
+  const int mt_own = (cnt + GM_BM - 1) / GM_BM;
+  int incl = mt_own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  if (t == 0) {
     int run = 0;
-    for (int e = 0; e < E; ++e) {
-      start[e] = run;
-      const int cnt = offsets[e + 1] - offsets[e];
-      run += (cnt + GM_BM - 1) / GM_BM;
-    }
-    start[E] = run;
-    *n_tiles = run;
+    for (int i = 0; i < 16; ++i) { const int v = wsum[i]; wsum[i] = run; run += v; }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const int cnt = offsets[e + 1] - offsets[e];
-    const int mt = start[e + 1] - start[e];
-    for (int i = 0; i < mt; ++i) {
-      tiles[2 * (start[e] + i)] = e;
-      tiles[2 * (start[e] + i) + 1] = offsets[e] + i * GM_BM;
-    }
-    for (int nt = 0; nt < n_nt_a; ++nt)
-      for (int i = 0; i < mt; ++i) work_a[start[e] * n_nt_a + nt * mt + i] = (start[e] + i) | (nt << 20);
-    for (int nt = 0; nt < n_nt_b; ++nt)
-      for (int i = 0; i < mt; ++i) work_b[start[e] * n_nt_b + nt * mt + i] = (start[e] + i) | (nt << 20);
-    (void)cnt;
+  if (t == eb) { s_start = wsum[w] + incl - mt_own; s_mt = mt_own; }
+  if (eb == 0 && t == E - 1) *n_tiles = wsum[w] + incl;
+  __syncthreads();
+  const int st = s_start, mt = s_mt, o0 = offsets[eb];
+  for (int i = t; i < mt; i += blockDim.x) {
+    tiles[2 * (st + i)] = eb;
+    tiles[2 * (st + i) + 1] = o0 + i * GM_BM;
   }
+  for (int j = t; j < mt * n_nt_a; j += blockDim.x) work_a[st * n_nt_a + j] = (st + j % mt) | ((j / mt) << 20);
+  for (int j = t; j < mt * n_nt_b; j += blockDim.x) work_b[st * n_nt_b + j] = (st + j % mt) | ((j / mt) << 20);
 }
 
 // -------------------------------------------------------------- the GEMM --
@@ -456,7 +462,7 @@ hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
   quant_x_kernel<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(reinterpret_cast<const uint16_t*>(x), xq, xs, nblk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  build_tiles_kernel<<<1, 1024, 0, st>>>(offsets, E, tiles, n_tiles, work_a, I / 128, work_b, H / 256);
+  build_tiles_kernel<<<E, 1024, 0, st>>>(offsets, E, tiles, n_tiles, work_a, I / 128, work_b, H / 256);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   GemmArgs ga{};

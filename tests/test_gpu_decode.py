@@ -132,6 +132,16 @@ def test_forward_mxfp4_decode():
         run_layer(cfg, 5, 3, b)
 
 
+@pytest.mark.parametrize("cfg,T", [(C3, 8), (C5, 6), (C5, 1)])
+def test_forward_fp4_decode_both_gate_up_paths(cfg, T):
+    """fp4 gate/up has two loops: activations staged in LDS with block scales
+    loaded four chunks at a time (when the token group's rows fit in 56 KB),
+    and the per-chunk register loop otherwise. H4096 at 8 tokens and H6144
+    at 6 tokens take the second; one token takes the first."""
+    print(f"fp4 decode {cfg.name} T={T}", flush=True)
+    run_layer(cfg, 2, 4, T)
+
+
 def test_forward_nvfp4_decode_with_partition_masks():
     cfg = C5
     ld, ids, gates, out, ref = run_layer(cfg, 1, 2, 4)

@@ -129,9 +129,12 @@ def swiglu_expert(x_t: np.ndarray, G: np.ndarray, U: np.ndarray, D: np.ndarray,
 
 
 def moe_layer(x: np.ndarray, wr: np.ndarray, expert, k: int, bias=None, mask=None,
-              renormalize: bool = True, x_quant=None, h_quant=None, tokens=None):
+              renormalize: bool = True, x_quant=None, h_quant=None, tokens=None, y_quant=None):
     """Full layer.  `expert(e)` returns (G, U, D) in fp64.  `tokens` limits the
     output rows computed (routing is still per token, independent of others).
+    x_quant / h_quant / y_quant mirror a storage precision of the activations,
+    of h before the down projection, and of each expert output before the
+    combine (identity when None).
     -> out [T,H] (rows outside `tokens` are NaN), ids, gates."""
     T, H = x.shape
     ids, gates, _ = route(x, wr, k, bias=bias, renormalize=renormalize)
@@ -145,6 +148,7 @@ def moe_layer(x: np.ndarray, wr: np.ndarray, expert, k: int, bias=None, mask=Non
             if not mask_has(mask, e):
                 continue
             G, U, D = expert(e)
-            acc = acc + gates[t, j] * swiglu_expert(xt, G, U, D, quant=h_quant)
+            y = swiglu_expert(xt, G, U, D, quant=h_quant)
+            acc = acc + gates[t, j] * (y if y_quant is None else y_quant(y))
         out[t] = acc
     return out, ids, gates

@@ -1,5 +1,6 @@
-"""MXFP8 (E4M3 elements, E8M0 scale per 32) quantisation, mirrored for the
-prefill path (test infrastructure).
+"""MXFP8 (E4M3 elements, E8M0 scale per 32) quantisation, and the bf16
+rounding of the expert outputs y, both mirrored for the prefill path (test
+infrastructure).
 
 Written from the OCP Microscaling Formats (MX) v1.0 conversion rule: for each
 block of 32 consecutive values, shared exponent X = floor(log2(max|V|)) - 8
@@ -54,3 +55,23 @@ def mxfp8_quantize_f32(v: np.ndarray) -> np.ndarray:
     h in fp32 when they quantise it, so the oracle takes the same decision on
     the same precision."""
     return mxfp8_quantize(np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64))
+
+
+def bf16_round_f32(v: np.ndarray) -> np.ndarray:
+    """The prefill path stores each expert output y in bf16: the kernel holds
+    y in fp32 and rounds it to the nearest bf16 value (8 significant bits,
+    ties to even).  Written from that definition: round to fp32 first, then
+    keep 8 significant bits of the mantissa with round-half-even (np.rint),
+    on the fixed 2^-133 grid below the smallest normal 2^-126; beyond the
+    largest bf16 value (just under 2^128) the result is infinite.  Returns fp64."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+    out = np.empty_like(f)
+    fin = np.isfinite(f)
+    out[~fin] = f[~fin]
+    a = f[fin]
+    m, e = np.frexp(a)                                  # a = m * 2^e, |m| in [0.5, 1)
+    normal = np.abs(a) >= np.ldexp(1.0, -126)
+    r = np.where(normal, np.ldexp(np.rint(np.ldexp(m, 8)), e - 8), np.ldexp(np.rint(np.ldexp(a, 133)), -133))
+    r = np.where(np.abs(r) >= np.ldexp(1.0, 128), np.copysign(np.inf, r), r)   # rounded past the largest bf16
+    out[fin] = r
+    return out

@@ -153,6 +153,28 @@ def test_mxfp8_zero_block_and_ties():
     assert q[0] == 256.0 and q[1] == 16.0 and q[2] == 20.0
 
 
+def test_bf16_round_matches_torch_including_ties_and_subnormals():
+    """The oracle's bf16 rounding of y (8 significant bits, ties to even) against
+    torch's fp32 -> bfloat16 conversion: random values over many binades, exact
+    midpoints between neighbouring bf16 values, fp32 subnormals, overflow."""
+    g = np.random.default_rng(11)
+    v = g.standard_normal(20000) * np.exp2(g.integers(-130, 126, 20000))
+    # exact midpoints: bf16 value b + half an ulp, for both parities of b
+    base = formats.bf16_bits_to_f64(g.integers(0x0080, 0x7F7F, 4000, dtype=np.int64).astype(np.uint16))
+    ulp = np.ldexp(1.0, np.frexp(base)[1] - 8)
+    mids = base + 0.5 * ulp
+    special = np.array([0.0, -0.0, 1e-40, -3e-45, 3.4e38, -3.4e38, np.inf, -np.inf, 1.0 + 2.0 ** -8,
+                        1.0 + 3 * 2.0 ** -8])
+    for arr in (v, mids, -mids, special):
+        f32 = arr.astype(np.float32)
+        ref = torch.from_numpy(f32).to(torch.bfloat16).to(torch.float64).numpy()
+        got = mx.bf16_round_f32(arr)
+        np.testing.assert_array_equal(got, ref)
+    # a hand case: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> even (1.0)
+    assert mx.bf16_round_f32(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    assert mx.bf16_round_f32(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
 # ------------------------------------------------------------------ routing --
 def _bf16_vals(shape, scale, seed):
     g = np.random.default_rng(seed)

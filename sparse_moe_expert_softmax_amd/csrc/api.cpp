@@ -69,7 +69,7 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T) {
   p.off_pos = o;     o = align256(o + sizeof(int32_t) * (size_t)p.P);
   p.off_cnt = o;     o = align256(o + sizeof(uint32_t) * (size_t)(p.H / 16 + 1));
   p.off_h = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.I);   // fp32 h, bf16 hi/lo, or MXFP8 codes
-  p.off_y = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.H);
+  p.off_y = o;       o = align256(o + (p.mfma ? 2 : 4) * (size_t)p.P * p.H);  // bf16 y on the matrix-core path
   if (p.mfma) {
     p.off_xq = o;    o = align256(o + (size_t)T * p.H);                     // MXFP8 x codes
     p.off_xs = o;    o = align256(o + (size_t)T * p.H / 32);                // and scales

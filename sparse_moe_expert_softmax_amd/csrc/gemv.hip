@@ -246,11 +246,38 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   *reinterpret_cast<float4*>(out + (int64_t)t * H + h) = acc;
 }
 
+// The same combine over expert outputs stored in bf16 (the matrix-core path):
+// 8 columns per thread, fp32 accumulation in the same fixed j order.
+__global__ void __launch_bounds__(256) combine_bf16_kernel(const uint16_t* __restrict__ ybuf,
+                                                           const int32_t* __restrict__ pos,
+                                                           const float* __restrict__ gates, float* __restrict__ out,
+                                                           int T, int H, int k) {
+  const int t = blockIdx.y;
+  const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (t >= T || h >= H) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int p = pos[(int64_t)t * k + j];
+    if (p < 0) continue;
+    const float g = gates[(int64_t)t * k + j];
+    const uint4 y = *reinterpret_cast<const uint4*>(ybuf + (int64_t)p * H + h);
+    const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = fmaf(g, bf16_lo(w[q]), acc[2 * q]);
+      acc[2 * q + 1] = fmaf(g, bf16_hi(w[q]), acc[2 * q + 1]);
+    }
+  }
+  float4* o = reinterpret_cast<float4*>(out + (int64_t)t * H + h);
+  o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
 hipError_t launch_combine(const FwdPlan& pl, const int32_t* pos, const float* gates, float* out, char* ws,
                           hipStream_t st) {
-  const float* ybuf = reinterpret_cast<const float*>(ws + pl.off_y);
-  dim3 cg((pl.H / 4 + 255) / 256, pl.T);
-  combine_kernel<<<cg, 256, 0, st>>>(ybuf, pos, gates, out, pl.T, pl.H, pl.P / pl.T);
+  const uint16_t* ybuf = reinterpret_cast<const uint16_t*>(ws + pl.off_y);
+  dim3 cg((pl.H / 8 + 255) / 256, pl.T);
+  combine_bf16_kernel<<<cg, 256, 0, st>>>(ybuf, pos, gates, out, pl.T, pl.H, pl.P / pl.T);
   return hipGetLastError();
 }
 

@@ -57,6 +57,7 @@ hipError_t launch_gemv_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
 // large-batch MXFP4 path on gfx950 scaled MFMA
 constexpr int MFMA_MIN_TOKENS = 256;
 bool mfma_supported(const ft_moe_desc& d, int T);
+// fixed-j-order fp32 combine over the bf16 expert outputs y [P, H] at off_y
 hipError_t launch_combine(const FwdPlan& pl, const int32_t* pos, const float* gates, float* out, char* ws,
                           hipStream_t st);
 hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const void* x, const int32_t* slot_ids,

@@ -26,7 +26,7 @@
 // tiles), with the eight XCDs taking workgroups round-robin.
 //   gate/up: weight rows = 64 gate rows + the same 64 up rows; epilogue
 //            h = silu(gate) * up, quantised to MXFP8 through LDS.
-//   down:    weight rows = 128 rows of D; epilogue stores y (fp32) through LDS.
+//   down:    weight rows = 256 rows of D; epilogue stores y rounded to bf16.
 // The combine (fixed j order, fp32) runs as its own kernel afterwards.
 #include "common.hpp"
 #include "internal.hpp"
@@ -192,7 +192,7 @@ struct GemmArgs {
   int64_t stride;
   uint8_t* hq;             // gate/up out: h codes [P, I]
   uint8_t* hs;             // gate/up out: h scales [P, I/32]
-  float* y;                // down out: [P, H]
+  __bf16* y;               // down out: [P, H], bf16
   int64_t a_bytes;         // size of the A code array (< 2^31)
   int H, I, k, n_ntiles, total_wg;
 };
@@ -426,17 +426,18 @@ __global__ void __launch_bounds__(256, 2) grouped_mx_gemm_kernel(GemmArgs ga) {
       ga.hs[(int64_t)m * (ga.I / 32) + i0 / 32] = (uint8_t)sb;
     }
   } else {
-    // y rows straight from the accumulators: 16 lanes store 64 contiguous bytes
-    float* yb = ga.y + ntile * 256 + 64 * wv + c16;
+    // y rows straight from the accumulators, rounded to bf16 (nearest even):
+    // 16 lanes store 32 contiguous bytes
+    __bf16* yb = ga.y + ntile * 256 + 64 * wv + c16;
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = m0 + 16 * ms + 4 * g + i;
         if (m < m_end) {
-          float* yr = yb + (int64_t)m * ga.H;
+          __bf16* yr = yb + (int64_t)m * ga.H;
 #pragma unroll
-          for (int ns = 0; ns < 4; ++ns) yr[16 * ns] = acc[ms][ns][i];
+          for (int ns = 0; ns < 4; ++ns) yr[16 * ns] = (__bf16)acc[ms][ns][i];
         }
       }
   }
@@ -449,7 +450,7 @@ hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
   uint8_t* xs = reinterpret_cast<uint8_t*>(ws + pl.off_xs);
   uint8_t* hq = reinterpret_cast<uint8_t*>(ws + pl.off_h);
   uint8_t* hs = reinterpret_cast<uint8_t*>(ws + pl.off_hs);
-  float* y = reinterpret_cast<float*>(ws + pl.off_y);
+  __bf16* y = reinterpret_cast<__bf16*>(ws + pl.off_y);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + pl.off_tiles);
   int32_t* n_tiles = tiles + 2 * pl.max_tiles;
   int32_t* work_a = n_tiles + 1;                            // gate/up work items

@@ -84,7 +84,7 @@ class LayerData:
         w64 = to_f64(self.wr, self.cfg.router_dtype)
         return route(x64, w64, self.cfg.top_k, bias=bias, renormalize=self.cfg.renormalize)
 
-    def oracle_layer(self, mask=None, bias=None, tokens=None, x_quant=None, h_quant=None):
+    def oracle_layer(self, mask=None, bias=None, tokens=None, x_quant=None, h_quant=None, y_quant=None):
         x64 = to_f64(self.x, self.cfg.act_dtype)
         w64 = to_f64(self.wr, self.cfg.router_dtype)
         cache = {}
@@ -95,4 +95,5 @@ class LayerData:
             return cache[e]
 
         return moe_layer(x64, w64, expert, self.cfg.top_k, bias=bias, mask=mask,
-                         renormalize=self.cfg.renormalize, tokens=tokens, x_quant=x_quant, h_quant=h_quant)
+                         renormalize=self.cfg.renormalize, tokens=tokens, x_quant=x_quant, h_quant=h_quant,
+                         y_quant=y_quant)

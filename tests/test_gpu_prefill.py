@@ -1,6 +1,7 @@
 """GPU parity of the prefill path (MXFP4 weights on scaled MFMA, activations
-quantised to MXFP8) against the fp64 oracle with the same quantisation
-mirrored (OCP MX rule for x before gate/up and for h before down).
+quantised to MXFP8) against the fp64 oracle with the same storage precisions
+mirrored (OCP MX rule for x before gate/up and for h before down; expert
+outputs y rounded to bf16 before the combine).
 
 Bars: routing ids bit-exact for every token; gates within 1e-6; outputs within
 max relative error 1e-2."""
@@ -9,7 +10,7 @@ import pytest
 import torch
 
 from gpu_util import LayerData, max_rel_err
-from oracle.mx import mxfp8_quantize, mxfp8_quantize_f32
+from oracle.mx import bf16_round_f32, mxfp8_quantize, mxfp8_quantize_f32
 from sparse_moe_expert_softmax_amd.configs import BF16, C4, MXFP4, MoEConfig
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
@@ -29,7 +30,8 @@ def run_prefill(cfg, T, layer, step, sample=None, mask=None):
     need = sorted(set(int(e) for t in rows for e in o_ids[t]))
     ld.build_pool(need)
     out = ld.gpu_forward(ids, gates, mask=mask).cpu().numpy()
-    ref, _, _ = ld.oracle_layer(mask=mask, tokens=list(rows), x_quant=mxfp8_quantize, h_quant=mxfp8_quantize_f32)
+    ref, _, _ = ld.oracle_layer(mask=mask, tokens=list(rows), x_quant=mxfp8_quantize, h_quant=mxfp8_quantize_f32,
+                                y_quant=bf16_round_f32)
     rows = list(rows)
     err = max_rel_err(out[rows], ref[rows])
     assert not np.isnan(out[rows]).any()

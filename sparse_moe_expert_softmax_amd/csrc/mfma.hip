@@ -18,13 +18,15 @@
 //   scale operand: E8M0 of row/column l % 16, K block g (32 wide)
 //   result: D[4 g + i][l % 16], i = 0..3
 //
-// Tiles: a workgroup (4 waves, 2 x 2) computes 64 pair-rows x 128 weight
-// rows; K advances 128 per step through double-buffered LDS (global loads
-// for step s+1 are in flight while step s computes).  The tile list (expert,
-// 64-row block) comes from the permutation; workgroups are mapped so that all
-// tiles of one expert land on one XCD (its L2 keeps the A rows and the weight
-// tiles), with the eight XCDs taking workgroups round-robin.
-//   gate/up: weight rows = 64 gate rows + the same 64 up rows; epilogue
+// Tiles: a workgroup (4 waves) computes 64 pair rows x 256 weight rows, each
+// wave all 64 rows x 64 weight rows; K advances 128 per step.  Activations go
+// through double-buffered LDS, weights straight from memory into the MFMA
+// operand registers, block scales in groups of three steps through LDS; the
+// loads of two steps are in flight while a step computes.  The tile list
+// (expert, 64-row block) comes from the permutation; work items are ordered
+// expert, weight tile, row tile and mapped so that consecutive items run on
+// one XCD (its L2 then serves a weight tile to all row tiles of the expert).
+//   gate/up: weight rows = 128 gate rows + the same 128 up rows; epilogue
 //            h = silu(gate) * up, quantised to MXFP8 through LDS.
 //   down:    weight rows = 256 rows of D; epilogue stores y rounded to bf16.
 // The combine (fixed j order, fp32) runs as its own kernel afterwards.

@@ -278,11 +278,13 @@ hipError_t launch_route_decode(const ft_moe_desc& d, const void* x, int T, const
 }
 
 // ---------------------------------------------------------------- prefill --
-// Many tokens: logits as a tiled fp64 GEMM.  A workgroup computes 128 tokens
-// x 64 experts; each thread holds 8 x 4 fp64 accumulators; K advances 16 per
-// step through double-buffered LDS holding the operands already widened to
-// fp64 (exact).  Each accumulator adds its products in ascending h order, the
-// same order for every expert.
+// Many tokens, hidden size not a multiple of 32 (the matrix-core kernel
+// below needs 32-element chunks): logits as a tiled fp64 GEMM on the vector
+// ALUs.  A workgroup computes 128 tokens x 64 experts; each thread holds
+// 8 x 4 fp64 accumulators; K advances 16 per step through double-buffered
+// LDS holding the operands already widened to fp64 (exact).  Each
+// accumulator adds its products in ascending h order, the same order for
+// every expert.
 constexpr int RL_TT = 128, RL_TE = 64, RL_KB = 16;
 
 template <int XDT, int WDT>

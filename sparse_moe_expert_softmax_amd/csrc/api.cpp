@@ -60,7 +60,7 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T) {
   if (p.nb < 1) p.nb = 1;
   p.mfma = mfma_supported(d, T);
   p.path = p.mfma ? PATH_MFMA : (dec_supported(d, T) ? PATH_DEC : PATH_GEMV);
-  p.max_tiles = p.P / 64 + p.E + 1;
+  p.max_tiles = p.P / 256 + p.E + 1;
   size_t o = 0;
   p.off_hist = o;    o = align256(o + sizeof(int32_t) * (size_t)p.nb * p.E);
   p.off_offsets = o; o = align256(o + sizeof(int32_t) * (size_t)(p.E + 2));

@@ -34,7 +34,7 @@ struct FwdPlan {
   bool mfma;                   // large-batch MXFP4 path on scaled MFMA
   size_t off_hist, off_offsets, off_active, off_perm, off_pos, off_h, off_y, off_xq, off_xs, off_hs, off_cnt;
   size_t off_tiles;            // MFMA path: tile list (2 ints per tile) + count
-  int max_tiles;               // upper bound of (expert, 64-row) tiles: P/64 + E
+  int max_tiles;               // upper bound of (expert, 256-row chunk) tiles: P/256 + E + 1
   size_t bytes;
 };
 typedef FwdPlan DecPlan;

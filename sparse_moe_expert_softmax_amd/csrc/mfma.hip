@@ -18,14 +18,15 @@
 //   scale operand: E8M0 of row/column l % 16, K block g (32 wide)
 //   result: D[4 g + i][l % 16], i = 0..3
 //
-// Tiles: a workgroup (4 waves) computes 64 pair rows x 256 weight rows, each
-// wave all 64 rows x 64 weight rows; K advances 128 per step.  Activations go
-// through double-buffered LDS, weights straight from memory into the MFMA
-// operand registers, block scales in groups of three steps through LDS; the
-// loads of two steps are in flight while a step computes.  The tile list
-// (expert, 64-row block) comes from the permutation; work items are ordered
-// expert, weight tile, row tile and mapped so that consecutive items run on
-// one XCD (its L2 then serves a weight tile to all row tiles of the expert).
+// Tiles: a workgroup (8 waves) computes all rows of one expert (in chunks of
+// up to 256 pair rows) x 256 weight rows; K advances 128 per step.  Both
+// operands and their block scales go global -> LDS through the buffer
+// unit's LDS-DMA path, three steps deep, so no registers are spent on staging
+// and every weight byte crosses L2 -> LDS once per expert chunk.  The tile
+// list (expert, 256-row chunk) comes from the permutation; work items are
+// ordered expert chunk, weight tile and mapped so that the weight tiles of
+// one expert run side by side on one XCD (its L2 then serves the expert's
+// activation rows to all of them).
 //   gate/up: weight rows = 128 gate rows + the same 128 up rows; epilogue
 //            h = silu(gate) * up, quantised to MXFP8 through LDS.
 //   down:    weight rows = 256 rows of D; epilogue stores y rounded to bf16.
@@ -38,11 +39,7 @@ namespace ft {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int GM_BM = 64;      // pair rows per tile
-constexpr int GM_BN = 256;     // weight rows per tile (gate/up: 128 gate rows + the same 128 up rows)
-constexpr int GM_BK = 128;     // K per step
-constexpr int GM_ASTR = 144;   // LDS row stride of A (bytes), padded: conflict-free 16-byte fragment reads
-constexpr int GM_HSTR = 33;    // LDS row stride of the h epilogue tile (floats)
+constexpr int GM_BK = 128;     // K per step (one scaled MFMA)
 
 // -------------------------------------------------------- E4M3 rounding --
 // |v| (already divided by the block scale, finite) -> E4M3 code, nearest
@@ -119,12 +116,33 @@ __global__ void __launch_bounds__(256) quant_x_kernel(const uint16_t* __restrict
   xs[b] = (uint8_t)quant_block32(v, xq + b * 32);
 }
 
+// Tile geometry of the expert GEMM (below).
+constexpr int BG_BM = 256;                    // pair rows per tile
+constexpr int BG_BN = 256;                    // weight rows per tile
+constexpr int BG_ASZ = BG_BM * 128;           // A bytes per step
+constexpr int BG_STG = BG_ASZ + BG_BN * 64;   // A + B bytes per step
+constexpr int BG_SCL = BG_BM * 16;            // bytes of one scale group of A (or B): 16-byte row slots
+constexpr int BG_HSTR = 33;                   // row stride (floats) of the h staging tile
+
+// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt at their no-wait maxima)
+#define BG_VMWAIT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+// A workgroup barrier without the memory fence that __syncthreads() carries:
+// the fence would wait for every LDS-DMA load in flight.  The empty asm keeps
+// the compiler from moving memory accesses across it.
+#define BG_BARRIER()                          \
+  do {                                        \
+    asm volatile("" ::: "memory");            \
+    __builtin_amdgcn_s_barrier();             \
+    asm volatile("" ::: "memory");            \
+  } while (0)
+
 // ------------------------------------------------------------ tile list --
-// tiles[2*i] = expert, tiles[2*i+1] = first row (sorted position) of tile i;
+// tiles[2*i] = expert, tiles[2*i+1] = first row (sorted position) of tile i
+// (chunks of up to BG_BM rows);
 // tiles are grouped by expert; count in *n_tiles.  Work lists (one per GEMM,
-// n_nt weight tiles each): item = tile | (ntile << 20), ordered by expert,
-// then weight tile, then row tile, so that the row tiles sharing a weight
-// tile run side by side and an expert's activation rows stay in one L2.
+// n_nt weight tiles each): item = tile | (ntile << 20), ordered by row
+// chunk, then weight tile, so that the weight tiles of one chunk run side by
+// side and its activation rows stay in one L2.
 // One workgroup per expert.
 __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                            int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
@@ -137,7 +155,7 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
   __shared__ int32_t s_start, s_mt;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, eb = blockIdx.x;
   const int cnt = (t < E) ? offsets[t + 1] - offsets[t] : 0;
-  const int mt_own = (cnt + GM_BM - 1) / GM_BM;
+  const int mt_own = (cnt + BG_BM - 1) / BG_BM;
   int incl = mt_own;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -157,7 +175,7 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
   const int st = s_start, mt = s_mt, o0 = offsets[eb];
   for (int i = t; i < mt; i += blockDim.x) {
     tiles[2 * (st + i)] = eb;
-    tiles[2 * (st + i) + 1] = o0 + i * GM_BM;
+    tiles[2 * (st + i) + 1] = o0 + i * BG_BM;
   }
   for (int j = t; j < mt * n_nt_a; j += blockDim.x) work_a[st * n_nt_a + j] = (st + j % mt) | ((j / mt) << 20);
   for (int j = t; j < mt * n_nt_b; j += blockDim.x) work_b[st * n_nt_b + j] = (st + j % mt) | ((j / mt) << 20);
@@ -168,18 +186,6 @@ enum { GM_GATEUP = 0, GM_DOWN = 1 };
 
 // Buffer descriptor word 3 for untyped 32-bit accesses on gfx9-family parts.
 constexpr int GM_RSRC_WORD3 = 0x00020000;
-
-__device__ __forceinline__ uint3 gm_ld96(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  typedef int i32x3_t __attribute__((ext_vector_type(3)));
-  const i32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
-  return make_uint3((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z);
-}
-
-__device__ __forceinline__ uint4 gm_ld128(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  typedef int i32x4_t __attribute__((ext_vector_type(4)));
-  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
-}
 
 struct GemmArgs {
   const uint8_t* aq;       // A codes: x_q [T, K] (gate/up) or h_q [P, K] (down)
@@ -196,250 +202,290 @@ struct GemmArgs {
   uint8_t* hs;             // gate/up out: h scales [P, I/32]
   __bf16* y;               // down out: [P, H], bf16
   int64_t a_bytes;         // size of the A code array (< 2^31)
-  int H, I, k, n_ntiles, total_wg;
+  int H, I, k, n_ntiles;
 };
 
-// Workgroup tile: 64 pair rows x 256 weight rows, K advancing 128 per step.
-// The four waves split the weight rows: each wave owns all 64 pair rows and
-// 64 weight rows (4 x 4 MFMAs per K step, 16 independent accumulators).
-//   A (activations, shared by the waves) goes global -> registers -> LDS,
-//     double-buffered; each wave reads its fragments from LDS.
-//   B (weights, private to one wave) goes global -> registers straight into
-//     the MFMA operand: lane l loads the 16 bytes (one MX block of 32 E2M1
-//     codes) of weight row l % 16, K block l / 16, and the matching scale byte.
-// A ring of three register slots keeps the loads of two K steps in flight;
-// every step issues the same loads unconditionally (the step index is
-// clamped at the end), so the compiler's wait counts stay exact.
+typedef int bg_i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer load of 16 (or 12) bytes per lane straight into LDS: lane l's bytes
+// land at lds + size * l.  Written as inline asm so that the compiler does not
+// add its own waits for these loads (its LDS-DMA tracking falls back to
+// waiting for all of them before any LDS read); the kernel waits for them
+// explicitly before each barrier.
+__device__ __forceinline__ void bg_dma16(bg_i32x4_t rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void bg_dma12(bg_i32x4_t rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx3 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ bg_i32x4_t bg_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return (bg_i32x4_t){(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xFFFFu), (int)bytes, GM_RSRC_WORD3};
+}
+__device__ __forceinline__ uint32_t bg_lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+
+// A workgroup of eight waves computes up to 256 pair rows (one expert's rows,
+// or a 256-row chunk of them) x 256 weight rows; K advances 128 per step.
+// All operand traffic goes global -> LDS by the buffer unit's LDS-DMA path
+// (no registers held), three stages deep: while step q computes, the loads of
+// steps q+1 and q+2 are in flight.  Block scales travel the same way in groups
+// of three steps (12 bytes per row, landing in 16-byte slots), double-buffered.
+//   wave w: row blocks wm + 4i (16 rows each, i = 0..3), wm = w & 3, so every
+//           wave holds a quarter of any prefix of rows; weight rows 128*(w>>2)
+//           .. +127 of the tile (gate/up: 64 gate + the same 64 up rows).
+// LDS layouts (16-byte chunks XOR-swizzled against bank conflicts):
+//   A: row r (128 B) at r*128, chunk c at 16*(c ^ ((r >> 1) & 7))
+//   B: weight row n (64 B) at n*64, chunk c at 16*(c ^ ((n >> 1) & 3))
+//   (both measured free of bank conflicts for the operand reads on gfx950)
+//   scales: row r of a group at r*16 (12 bytes used), byte 4*j + g for step j, block g.
 template <int MODE>
-__global__ void __launch_bounds__(256, 2) grouped_mx_gemm_kernel(GemmArgs ga) {
-  constexpr int A_STAGE = GM_BM * GM_ASTR;
-  constexpr int LDS_MAIN = 2 * A_STAGE + 2 * GM_BM * 12 + 2 * GM_BN * 12;
-  constexpr int LDS_EPI = 4 * GM_BM * GM_HSTR * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI];
-  // map workgroups XCD-major: consecutive work items run on one XCD
-  const int G = ga.total_wg;
-  const int per_xcd = (G + 7) / 8;
-  const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  const int nt = *ga.n_tiles;
-  if (w >= nt * ga.n_ntiles) return;
+__global__ void __launch_bounds__(512, 1) mx_gemm256_kernel(GemmArgs ga) {
+  // LDS: three operand stages, then two scale-group buffers (A rows, B rows each)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * BG_STG + 4 * BG_SCL];
+  // map workgroups XCD-major over the actual work items (the grid is sized
+  // for the most tiles possible): consecutive items run on one XCD
+  const int n_items = *ga.n_tiles * ga.n_ntiles;
+  const int per_xcd = (n_items + 7) / 8;
+  const int xk = blockIdx.x / 8;
+  if (xk >= per_xcd) return;
+  const int w = (blockIdx.x % 8) * per_xcd + xk;
+  if (w >= n_items) return;
   const int item = ga.work[w];
   const int tile = item & 0xFFFFF, ntile = item >> 20;
   const int e = ga.tiles[2 * tile], m0 = ga.tiles[2 * tile + 1];
-  const int m_end = ga.offsets[e + 1];
+  const int m_lim = ga.offsets[e + 1];
+  const int nv = (m_lim - m0 < BG_BM) ? m_lim - m0 : BG_BM;  // valid rows of this tile
   const int K = (MODE == GM_GATEUP) ? ga.H : ga.I;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int nks = K / GM_BK;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv & 3, wn = wv >> 2;
 
   const int slot = ga.slot_ids ? ga.slot_ids[ga.perm[m0]] : e;
   const uint8_t* rec = ga.pool + (int64_t)slot * ga.stride;
   const RecordLayout L = record_layout(ga.H, ga.I, FT_MXFP4);
+  const bg_i32x4_t rA = bg_rsrc(ga.aq, ga.a_bytes);
+  const bg_i32x4_t rAs = bg_rsrc(ga.as, ga.a_bytes / 32);
+  const bg_i32x4_t rB = bg_rsrc(rec, L.bytes);
 
-  // ---- A sources: 2 x 16 B per thread (tile rows tid/8 and tid/8 + 32,
-  // 16-byte chunk tid%8) and one scale word per thread (row tid%64; only
-  // threads < 64 store theirs)
-  int ma0 = m0 + tid / 8, ma1 = m0 + tid / 8 + 32, mas = m0 + 16 * wv + c16;
-  if (ma0 >= m_end) ma0 = m_end - 1;  // padding rows repeat the last row (results discarded)
-  if (ma1 >= m_end) ma1 = m_end - 1;
-  if (mas >= m_end) mas = m_end - 1;
-  const int64_t ar0 = (MODE == GM_GATEUP) ? (int64_t)(ga.perm[ma0] / ga.k) : (int64_t)ma0;
-  const int64_t ar1 = (MODE == GM_GATEUP) ? (int64_t)(ga.perm[ma1] / ga.k) : (int64_t)ma1;
-  const int64_t ars = (MODE == GM_GATEUP) ? (int64_t)(ga.perm[mas] / ga.k) : (int64_t)mas;
-  // Loads go through buffer descriptors: a per-lane 32-bit offset that stays
-  // fixed over the K loop plus a scalar K offset, so the loop keeps no 64-bit
-  // addresses in vector registers.
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)ga.aq, (short)0, (int)ga.a_bytes, GM_RSRC_WORD3);
-  const __amdgpu_buffer_rsrc_t rAs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)ga.as, (short)0, (int)(ga.a_bytes / 32), GM_RSRC_WORD3);
-  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)rec, (short)0, (int)L.bytes, GM_RSRC_WORD3);
-  const int oa0 = (int)(ar0 * K) + (tid % 8) * 16;
-  const int oa1 = (int)(ar1 * K) + (tid % 8) * 16;
-  // scales travel in groups of three K steps (12 blocks, 12 bytes per row):
-  // lane l of wave w loads dword min(l/16, 2) of A row 16w + l%16, and the 12
-  // bytes of its wave's weight row 16*(l/16) + l%16 (sub-tile l/16)
-  const int oas = (int)(ars * (K / 32)) + 4 * (g < 3 ? g : 2);
+  // activation row of tile row r (valid rows only)
+  auto arow = [&](int r) -> int {
+    const int m = m0 + r;
+    return (MODE == GM_GATEUP) ? ga.perm[m] / ga.k : m;
+  };
+  // tile weight row n -> matrix, row within it
+  auto wmat = [&](int n) { return (MODE == GM_GATEUP) ? (n < 128 ? 0 : 1) : 2; };
+  auto wrow = [&](int n) { return (MODE == GM_GATEUP) ? ntile * 128 + (n & 127) : ntile * 256 + n; };
 
-  // ---- B sources: weight row of sub-tile ns for this lane, K block g
-  // gate/up: ns 0,1 = gate rows, ns 2,3 = the same up rows
-  //          (ntile*128 + 32*wave + 16*(ns&1) + lane%16)
-  // down:    rows ntile*256 + 64*wave + 16*ns + lane%16
-  auto brow = [&](int ns) {
-    return (MODE == GM_GATEUP) ? ntile * 128 + 32 * wv + 16 * (ns & 1) + c16 : ntile * 256 + 64 * wv + 16 * ns + c16;
-  };
-  auto bmat = [&](int ns) { return (MODE == GM_GATEUP) ? (ns < 2 ? 0 : 1) : 2; };
-  // one per-lane offset (sub-tile 0) for all four sub-tiles; the others
-  // differ by a uniform amount that rides in the scalar offset
-  const int ob = (int)L.code_off[bmat(0)] + brow(0) * (K / 2) + 16 * g;
-  auto bdelta = [&](int ns) {
-    return (int)(L.code_off[bmat(ns)] - L.code_off[bmat(0)]) + (brow(ns) - brow(0)) * (K / 2);
-  };
-  const int db1 = bdelta(1), db2 = bdelta(2), db3 = bdelta(3);
-  int obs;  // this lane's weight-scale row: sub-tile g, row lane%16
-  {
-    const int ns = g;
-    const int row = (MODE == GM_GATEUP) ? ntile * 128 + 32 * wv + 16 * (ns & 1) + c16 : ntile * 256 + 64 * wv + 16 * ns + c16;
-    const int mat = (MODE == GM_GATEUP) ? (ns < 2 ? 0 : 1) : 2;
-    obs = (int)L.scale_off[mat] + row * (K / 32);
+  // ---- LDS-DMA sources (per-lane offsets fixed over K; the K step rides in
+  // the scalar offset).  A: instruction t of this wave fills tile rows
+  // 8j .. 8j+7, j = wv + 8t, lane -> row 8j + lane/8, physical chunk lane%8.
+  // Rows past the tile's valid rows read row 0's line (results discarded).
+  int voA[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int j = wv + 8 * t;
+    const int r = 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ (((lane >> 4) + 4 * (j & 1)) & 7);
+    voA[t] = (r < nv ? arow(r) * K : 0) + 16 * c;
   }
+  // B: instruction t fills tile weight rows 16j .. 16j+15, j = wv + 8t,
+  // lane -> row 16j + lane/4, physical chunk lane%4.
+  int voB[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = 16 * (wv + 8 * t) + (lane >> 2);
+    const int c = (lane & 3) ^ ((lane >> 3) & 3);
+    voB[t] = (int)(L.code_off[wmat(n)] + (int64_t)wrow(n) * (K / 2)) + 16 * c;
+  }
+  // scales: waves 0-3 fill A rows 64*wv + lane, waves 4-7 B rows 64*(wv-4) + lane
+  // (one buffer descriptor and LDS offset per wave, so a single load serves both halves)
+  const bg_i32x4_t rS = (wv < 4) ? rAs : rB;
+  const uint32_t lsS = (wv < 4) ? 1024 * wv : BG_SCL + 1024 * (wv - 4);
+  int voS;
+  {
+    const int r = 64 * (wv & 3) + lane;
+    if (wv < 4) voS = (r < nv ? arow(r) : arow(0)) * (K / 32);
+    else voS = (int)(L.scale_off[wmat(r)] + (int64_t)wrow(r) * (K / 32));
+  }
+  const int ngroups = (nks + 2) / 3;
 
-  uint8_t* const s_a = smem + (tid / 8) * GM_ASTR + (tid % 8) * 16;  // this thread's A store address
-  // scale groups, double-buffered: A [2][64 rows][3 dwords], weights [2][4 waves][64 rows][3 dwords]
-  uint32_t* const s_as = reinterpret_cast<uint32_t*>(smem + 2 * A_STAGE);
-  uint32_t* const s_bs = s_as + 2 * GM_BM * 3;
+  const uint32_t lbase = bg_lds_addr(smem);
+  const uint32_t la0 = lbase, la1 = lbase + BG_STG, la2 = lbase + 2 * BG_STG;
+  const uint32_t ls0 = lbase + 3 * BG_STG, ls1 = ls0 + 2 * BG_SCL;
+#define BG_DMA(lbuf, s)                                                                             \
+  do {                                                                                              \
+    const int ka_ = (s) * GM_BK, kb_ = (s) * (GM_BK / 2);                                           \
+    bg_dma16(rA, (lbuf) + 1024 * wv, voA[0], ka_);                                                  \
+    bg_dma16(rA, (lbuf) + 1024 * (wv + 8), voA[1], ka_);                                            \
+    bg_dma16(rA, (lbuf) + 1024 * (wv + 16), voA[2], ka_);                                           \
+    bg_dma16(rA, (lbuf) + 1024 * (wv + 24), voA[3], ka_);                                           \
+    bg_dma16(rB, (lbuf) + BG_ASZ + 1024 * wv, voB[0], kb_);                                         \
+    bg_dma16(rB, (lbuf) + BG_ASZ + 1024 * (wv + 8), voB[1], kb_);                                   \
+  } while (0)
+  // scale group G (clamped) into a group buffer: 12 bytes per lane, landing
+  // in 16-byte slots (lane l at 16*l), i.e. row 64*(wv&3) + l of the A or B half
+#define BG_SDMA(lsbuf, G)                                                                           \
+  do {                                                                                              \
+    const int gg_ = ((G) < ngroups ? (G) : ngroups - 1) * 12;                                       \
+    bg_dma12(rS, (lsbuf) + lsS, voS, gg_);                                                          \
+  } while (0)
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-  const int nks = K / GM_BK;
-#define GM_DECL(r) uint4 ra0_##r, ra1_##r, rb0_##r, rb1_##r, rb2_##r, rb3_##r;
-  GM_DECL(0) GM_DECL(1) GM_DECL(2)
-#undef GM_DECL
-  uint32_t gsa;  // A-scale dword of the group in flight
-  uint3 gsb;     // weight-scale bytes (12) of the group in flight
-#define GM_LOAD(r, st)                                                              \
-  do {                                                                              \
-    const int kb_ = ((st) < nks ? (st) : nks - 1) * GM_BK;                          \
-    ra0_##r = gm_ld128(rA, oa0, kb_);                                               \
-    ra1_##r = gm_ld128(rA, oa1, kb_);                                               \
-    rb0_##r = gm_ld128(rB, ob, kb_ / 2);                                            \
-    rb1_##r = gm_ld128(rB, ob, db1 + kb_ / 2);                                      \
-    rb2_##r = gm_ld128(rB, ob, db2 + kb_ / 2);                                      \
-    rb3_##r = gm_ld128(rB, ob, db3 + kb_ / 2);                                      \
+  // per-lane LDS read offsets (the rest of every address is a constant):
+  //   A row block i, half h:  stage + lA[h] + 8192 i
+  //   B sub-tile s:           stage + lB + bsub(s)
+  //   scales (group buffer):  A: lSA + 1024 i + 4 j;  B: lSB + 16 bsrow(s) + 4 j
+  const int swa = (c16 >> 1) & 7;
+  const int lA0 = (16 * wm + c16) * 128 + 16 * (g ^ swa);
+  const int lA1 = (16 * wm + c16) * 128 + 16 * ((g + 4) ^ swa);
+  const int nB0 = (MODE == GM_GATEUP) ? 64 * wn : 128 * wn;  // first tile weight row of the wave
+  const int lB = BG_ASZ + (nB0 + c16) * 64 + 16 * (g ^ ((c16 >> 1) & 3));
+  const int lSA = (16 * wm + c16) * 16 + g;
+  const int lSB = BG_SCL + (nB0 + c16) * 16 + g;
+  // sub-tile s of the wave: weight rows nB0 + bsrow(s) .. + 15
+#define BG_BSROW(s) ((MODE == GM_GATEUP) ? ((s) < 4 ? 16 * (s) : 128 + 16 * ((s) - 4)) : 16 * (s))
+  auto nB = [&](int s) { return nB0 + BG_BSROW(s); };
+
+#define BG_STEP(SOFF, SCOFF, j, NB)                                                                 \
+  do {                                                                                              \
+    i32x8_t fa_[4], fb_[4];                                                                         \
+    int fas_[4], fbs_[4];                                                                           \
+    _Pragma("unroll") for (int i = 0; i < (NB); ++i) {                                              \
+      const uint4 lo_ = *reinterpret_cast<const uint4*>(smem + (SOFF) + 8192 * i + lA0);            \
+      const uint4 hi_ = *reinterpret_cast<const uint4*>(smem + (SOFF) + 8192 * i + lA1);            \
+      fa_[i] = (i32x8_t){(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w,                            \
+                         (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w};                           \
+      fas_[i] = smem[(SCOFF) + 1024 * i + 4 * (j) + lSA];                                            \
+    }                                                                                               \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                 \
+      __builtin_amdgcn_sched_barrier(0);                                                            \
+      _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                               \
+        const uint4 b_ = *reinterpret_cast<const uint4*>(smem + (SOFF) + 64 * BG_BSROW(4 * h + s) + lB); \
+        fb_[s] = (i32x8_t){(int)b_.x, (int)b_.y, (int)b_.z, (int)b_.w, 0, 0, 0, 0};                 \
+        fbs_[s] = smem[(SCOFF) + 16 * BG_BSROW(4 * h + s) + 4 * (j) + lSB];                         \
+      }                                                                                             \
+      _Pragma("unroll") for (int i = 0; i < (NB); ++i)                                              \
+      _Pragma("unroll") for (int s = 0; s < 4; ++s)                                                 \
+        acc[i][4 * h + s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                       \
+            fa_[i], fb_[s], acc[i][4 * h + s], 0, 4, 0, fas_[i], 0, fbs_[s]);                       \
+    }                                                                                               \
   } while (0)
-#define GM_STORE(r, buf)                                                            \
-  do {                                                                              \
-    *reinterpret_cast<uint4*>(s_a + (buf) * A_STAGE) = ra0_##r;                     \
-    *reinterpret_cast<uint4*>(s_a + (buf) * A_STAGE + 32 * GM_ASTR) = ra1_##r;      \
+#define BG_PIN_ACC()                                                                                \
+  do {                                                                                              \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                                \
+    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) asm volatile("" : "+v"(acc[i_][j_]));           \
   } while (0)
-  // scale group G covers K steps 3G .. 3G+2 (clamped at the end; the bytes of
-  // a partial last group past the row are never used)
-#define GM_GLOAD(G)                                                                 \
-  do {                                                                              \
-    const int gg_ = ((G) <= (nks - 1) / 3 ? (G) : (nks - 1) / 3) * 12;              \
-    gsa = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rAs, oas, gg_, 0);         \
-    gsb = gm_ld96(rB, obs, gg_);                                                    \
+  // iteration for step q = q0 + J (stage buffer cur = st[J], the loads of
+  // step q+2 go to st[(J+2)%3]; scale group q0/3 in scur, the next group is
+  // loaded into snxt at J = 0).  Loads per iteration, in issue order: [J = 0:
+  // one scale load] then six operand loads (while q+2 < nks).  At the top
+  // this wave's loads of step q must have landed: allowed in flight are the
+  // loads of step q+1 and, at J = 1, the scale load issued just before them.
+#define BG_ITER(J, QO, CUR, lnxt2, SCUR, lsnxt, NB)                                                 \
+  do {                                                                                              \
+    const int q = q0 + (QO);                                                                        \
+    if ((J) == 1) BG_VMWAIT(7); else BG_VMWAIT(6);                                                  \
+    BG_BARRIER();                                                                                   \
+    if ((J) == 0) BG_SDMA(lsnxt, q / 3 + 1);                                                        \
+    BG_DMA(lnxt2, (q + 2 < nks ? q + 2 : nks - 1));                                                 \
+    BG_STEP((CUR) * BG_STG, 3 * BG_STG + (SCUR) * 2 * BG_SCL, J, NB);                               \
+    BG_PIN_ACC();                                                                                   \
   } while (0)
-#define GM_GSTORE(buf)                                                              \
-  do {                                                                              \
-    if (g < 3) s_as[(buf) * GM_BM * 3 + (16 * wv + c16) * 3 + g] = gsa;             \
-    uint32_t* d_ = s_bs + (buf) * GM_BN * 3 + (64 * wv + lane) * 3;                 \
-    d_[0] = gsb.x; d_[1] = gsb.y; d_[2] = gsb.z;                                    \
-  } while (0)
-#define GM_BOP(v_) ((i32x8_t){(int)(v_).x, (int)(v_).y, (int)(v_).z, (int)(v_).w, 0, 0, 0, 0})
-#define GM_STEP(r, buf, sbuf, j)                                                                  \
-  do {                                                                                            \
-    const uint8_t* sa_ = smem + (buf) * A_STAGE;                                                  \
-    const uint8_t* sas_ = reinterpret_cast<const uint8_t*>(s_as + (sbuf) * GM_BM * 3) + 4 * (j) + g; \
-    const uint8_t* sbs_ = reinterpret_cast<const uint8_t*>(s_bs + (sbuf) * GM_BN * 3 + 64 * wv * 3) + 4 * (j) + g; \
-    const i32x8_t b0_ = GM_BOP(rb0_##r), b1_ = GM_BOP(rb1_##r);                                   \
-    const i32x8_t b2_ = GM_BOP(rb2_##r), b3_ = GM_BOP(rb3_##r);                                   \
-    const int bs0_ = sbs_[(c16) * 12], bs1_ = sbs_[(16 + c16) * 12];                              \
-    const int bs2_ = sbs_[(32 + c16) * 12], bs3_ = sbs_[(48 + c16) * 12];                         \
-    _Pragma("unroll") for (int ms = 0; ms < 4; ++ms) {                                            \
-      const int row_ = 16 * ms + c16;                                                             \
-      const uint4 lo_ = *reinterpret_cast<const uint4*>(sa_ + row_ * GM_ASTR + 16 * g);           \
-      const uint4 hi_ = *reinterpret_cast<const uint4*>(sa_ + row_ * GM_ASTR + 64 + 16 * g);      \
-      const i32x8_t a_ = (i32x8_t){(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w,                \
-                                   (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w};               \
-      const int as_ = sas_[row_ * 12];                                                            \
-      acc[ms][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_, b0_, acc[ms][0], 0, 4, 0, as_, 0, bs0_); \
-      acc[ms][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_, b1_, acc[ms][1], 0, 4, 0, as_, 0, bs1_); \
-      acc[ms][2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_, b2_, acc[ms][2], 0, 4, 0, as_, 0, bs2_); \
-      acc[ms][3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_, b3_, acc[ms][3], 0, 4, 0, as_, 0, bs3_); \
-    }                                                                                             \
-  } while (0)
-  // An empty asm that reads and writes every accumulator ends each K step:
-  // without it the compiler sinks a step's MFMAs past the barrier into the
-  // next steps, keeping several steps' operands live at once (and spilling).
-#define GM_PIN_ACC()                                                                \
-  do {                                                                              \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                \
-    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) asm volatile("" : "+v"(acc[i_][j_])); \
-  } while (0)
-  // iteration for K step q = q0 + J (ring slot J = q % 3, scale group q0 / 3):
-  // A of step q+1 goes to LDS, the loads of step q+2 refill the slot that held
-  // step q-1, step q computes.  The next scale group is loaded at J = 0 and
-  // stored at J = 2, before the barrier that precedes its first step.
-#define GM_ITER(J, JN, JL)                                                          \
-  do {                                                                              \
-    const int q = q0 + J;                                                           \
-    const int cur = q & 1;                                                          \
-    GM_STORE(JN, cur ^ 1);                                                          \
-    GM_LOAD(JL, q + 2);                                                             \
-    if (J == 0) GM_GLOAD(q0 / 3 + 1);                                               \
-    GM_STEP(J, cur, gb, J);                                                         \
-    if (J == 2) GM_GSTORE(gb ^ 1);                                                  \
-    GM_PIN_ACC();                                                                   \
-    __syncthreads();                                                                \
+  // steps q0 .. q0+5: stage buffers 0 1 2 0 1 2, scale groups in buffer 0
+  // then 1.  Every iteration issues the same loads (past the last step they
+  // repeat it into a buffer nobody reads), so the wait counts are the same
+  // everywhere.  NB = row blocks this wave computes (the rest are padding).
+#define BG_KLOOP(NB)                                                                                \
+  do {                                                                                              \
+    int q0 = 0;                                                                                     \
+    for (; q0 + 6 <= nks; q0 += 6) {                                                                \
+      BG_ITER(0, 0, 0, la2, 0, ls1, NB);                                                            \
+      BG_ITER(1, 1, 1, la0, 0, ls1, NB);                                                            \
+      BG_ITER(2, 2, 2, la1, 0, ls1, NB);                                                            \
+      BG_ITER(0, 3, 0, la2, 1, ls0, NB);                                                            \
+      BG_ITER(1, 4, 1, la0, 1, ls0, NB);                                                            \
+      BG_ITER(2, 5, 2, la1, 1, ls0, NB);                                                            \
+    }                                                                                               \
+    if (q0 < nks) BG_ITER(0, 0, 0, la2, 0, ls1, NB);                                                \
+    if (q0 + 1 < nks) BG_ITER(1, 1, 1, la0, 0, ls1, NB);                                            \
+    if (q0 + 2 < nks) BG_ITER(2, 2, 2, la1, 0, ls1, NB);                                            \
+    if (q0 + 3 < nks) BG_ITER(0, 3, 0, la2, 1, ls0, NB);                                            \
+    if (q0 + 4 < nks) BG_ITER(1, 4, 1, la0, 1, ls0, NB);                                            \
   } while (0)
 
-  GM_GLOAD(0);
-  GM_LOAD(0, 0);
-  GM_LOAD(1, 1);
-  GM_GSTORE(0);
-  GM_STORE(0, 0);
-  __syncthreads();
-  int q0 = 0, gb = 0;
-  for (; q0 + 3 <= nks; q0 += 3, gb ^= 1) {
-    GM_ITER(0, 1, 2);
-    GM_ITER(1, 2, 0);
-    GM_ITER(2, 0, 1);
+  BG_SDMA(ls0, 0);
+  BG_DMA(la0, 0);
+  BG_DMA(la1, (nks > 1 ? 1 : 0));
+  {
+    // row blocks 16 (wm + 4 i) of this wave that hold valid rows (at least one is run)
+    const int nbr = (nv - 16 * wm + 63) / 64;
+    const int nbv = nbr < 1 ? 1 : (nbr > 4 ? 4 : nbr);
+    if (nbv == 4) BG_KLOOP(4);
+    else if (nbv == 3) BG_KLOOP(3);
+    else if (nbv == 2) BG_KLOOP(2);
+    else BG_KLOOP(1);
   }
-  // K-step tail: the ring is back at slot 0 here.
-  const int rem = nks - q0;
-  if (rem >= 1) GM_ITER(0, 1, 2);
-  if (rem >= 2) GM_ITER(1, 2, 0);
-#undef GM_ITER
-#undef GM_STEP
-#undef GM_GLOAD
-#undef GM_GSTORE
-#undef GM_PIN_ACC
-#undef GM_BOP
-#undef GM_LOAD
-#undef GM_STORE
+#undef BG_KLOOP
+#undef BG_ITER
+#undef BG_STEP
+#undef BG_PIN_ACC
+#undef BG_DMA
+#undef BG_SDMA
+  BG_VMWAIT(0);     // no LDS-DMA load may still be landing in the stage buffers
+  __syncthreads();  // all operand reads done: the stage buffers now hold the epilogue tiles
 
-  // ---- epilogue (accumulator element i of sub-tile (ms, ns) is row
-  // 16 ms + 4 g + i, weight row 16 ns + lane%16 of the wave's 64)
+  // ---- epilogue: accumulator element k of (i, s) is tile row
+  // 16 (wm + 4 i) + 4 g + k, weight row nB(s) + c16
   if (MODE == GM_GATEUP) {
-    // The wave's 32 h columns (i0 = ntile*128 + 32*wave) are one MX block per
-    // row: stage h = silu(gate) * up in the wave's own LDS area, then lane r
-    // quantises row r.  (The loop's last barrier freed the A buffers.)
-    float* sh = reinterpret_cast<float*>(smem) + wv * GM_BM * GM_HSTR;
+    // two MX blocks of h per row: h columns 64 wn + 32 hb .. + 31 of the
+    // tile's 128 (gate sub-tiles 2hb, 2hb+1 with up sub-tiles 4+2hb, 5+2hb);
+    // staged per wave in LDS so that lane l quantises wave row l
+    float* sh = reinterpret_cast<float*>(smem) + wv * (BG_BM / 4) * BG_HSTR;
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
+    for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-      for (int nsub = 0; nsub < 2; ++nsub)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gv = acc[ms][nsub][i], uv = acc[ms][nsub + 2][i];
-          sh[(16 * ms + 4 * g + i) * GM_HSTR + 16 * nsub + c16] = gv / (1.0f + expf(-gv)) * uv;
-        }
-    __syncthreads();
-    const int m = m0 + lane;
-    if (m < m_end) {
-      float v[32];
+        for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = sh[lane * GM_HSTR + i];
-      const int i0 = ntile * 128 + 32 * wv;
-      const uint32_t sb = quant_block32(v, ga.hq + (int64_t)m * ga.I + i0);
-      ga.hs[(int64_t)m * (ga.I / 32) + i0 / 32] = (uint8_t)sb;
+          for (int k = 0; k < 4; ++k) {
+            const float gv = acc[i][2 * hb + ss][k], uv = acc[i][4 + 2 * hb + ss][k];
+            sh[(16 * i + 4 * g + k) * BG_HSTR + 16 * ss + c16] = gv / (1.0f + expf(-gv)) * uv;
+          }
+      __syncthreads();
+      const int tr = 16 * (wm + 4 * (lane >> 4)) + (lane & 15);
+      if (tr < nv) {
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = sh[lane * BG_HSTR + i];
+        const int m = m0 + tr;
+        const int i0 = ntile * 128 + 64 * wn + 32 * hb;
+        const uint32_t sb = quant_block32(v, ga.hq + (int64_t)m * ga.I + i0);
+        ga.hs[(int64_t)m * (ga.I / 32) + i0 / 32] = (uint8_t)sb;
+      }
+      __syncthreads();
     }
   } else {
-    // y rows straight from the accumulators, rounded to bf16 (nearest even):
-    // 16 lanes store 32 contiguous bytes
-    __bf16* yb = ga.y + ntile * 256 + 64 * wv + c16;
+    __bf16* yb = ga.y + ntile * 256 + c16;
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 16 * ms + 4 * g + i;
-        if (m < m_end) {
-          __bf16* yr = yb + (int64_t)m * ga.H;
+      for (int k = 0; k < 4; ++k) {
+        const int tr = 16 * (wm + 4 * i) + 4 * g + k;
+        if (tr < nv) {
+          __bf16* yr = yb + (int64_t)(m0 + tr) * ga.H;
 #pragma unroll
-          for (int ns = 0; ns < 4; ++ns) yr[16 * ns] = (__bf16)acc[ms][ns][i];
+          for (int s = 0; s < 8; ++s) yr[nB(s)] = (__bf16)acc[i][s][k];
         }
       }
   }
@@ -487,8 +533,8 @@ hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
   ga.hs = hs;
   ga.n_ntiles = I / 128;
   ga.work = work_a;
-  ga.total_wg = (pl.max_tiles * ga.n_ntiles + 7) / 8 * 8;  // a multiple of 8 keeps the XCD mapping a bijection
-  grouped_mx_gemm_kernel<GM_GATEUP><<<ga.total_wg, 256, 0, st>>>(ga);
+  // the grid covers the most items possible; surplus workgroups exit at once
+  mx_gemm256_kernel<GM_GATEUP><<<(unsigned)((pl.max_tiles * ga.n_ntiles + 7) / 8 * 8), 512, 0, st>>>(ga);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // down: A = h_q by sorted position, N = H in 256-row tiles
   ga.aq = hq;
@@ -497,8 +543,7 @@ hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
   ga.y = y;
   ga.n_ntiles = H / 256;
   ga.work = work_b;
-  ga.total_wg = (pl.max_tiles * ga.n_ntiles + 7) / 8 * 8;
-  grouped_mx_gemm_kernel<GM_DOWN><<<ga.total_wg, 256, 0, st>>>(ga);
+  mx_gemm256_kernel<GM_DOWN><<<(unsigned)((pl.max_tiles * ga.n_ntiles + 7) / 8 * 8), 512, 0, st>>>(ga);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   return launch_combine(pl, pos, gates, out, ws, st);
 }

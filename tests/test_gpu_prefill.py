@@ -121,3 +121,34 @@ def test_prefill_threshold_general_path_below_256_tokens():
     ref, _, _ = ld.oracle_layer()
     assert max_rel_err(out, ref) <= 1e-2
     run_prefill(cfg, 256, 0, 13)
+
+
+SPARSE = MoEConfig("prefill_sparse_mxfp4", 92, hidden=768, inter=640, n_experts=128, top_k=2, act_dtype=BF16,
+                   router_dtype=BF16, w_dtype=MXFP4, n_layers=1)
+
+
+def test_prefill_sparse_experts_and_k_tails():
+    """128 experts for 600 pairs: one expert without rows, the others with
+    1-13 (so most waves of a row chunk hold no valid row), H 768 (six 128-K
+    steps: two full scale groups, no tail) and I 640 (five steps: a partial
+    scale group and a tail of five), five gate/up and three down weight tiles."""
+    print("prefill sparse T=300", flush=True)
+    _, ids, _, _, _, err = run_prefill(SPARSE, 300, 0, 17)
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=SPARSE.n_experts)
+    assert counts.min() == 0 and counts.max() < 16, (counts.min(), counts.max())
+    print(f"  max rel err {err:.3g}")
+
+
+FAT = MoEConfig("prefill_fat_mxfp4", 93, hidden=256, inter=128, n_experts=2, top_k=1, act_dtype=BF16,
+                router_dtype=BF16, w_dtype=MXFP4, n_layers=1)
+
+
+def test_prefill_experts_spanning_several_row_chunks():
+    """Two experts, top-1, 1,100 tokens: each expert's rows span three
+    256-row chunks (the last one partial); the down projection has a single
+    128-K step (I 128)."""
+    print("prefill fat T=1100", flush=True)
+    ld, ids, _, _, _, err = run_prefill(FAT, 1100, 0, 19)
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=2)
+    assert counts.min() > 512, counts
+    print(f"  rows per expert {counts.tolist()}, max rel err {err:.3g}")

@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of HIP-graph replay")
+    ap.add_argument("--separate", action="store_true",
+                    help="decode: ft_moe_route then ft_moe_forward instead of the fused ft_moe_route_forward")
     ap.add_argument("--graphs", type=int, default=16, help="distinct captured steps (distinct inputs) replayed in turn")
     ap.add_argument("--tokens", type=int, default=8192, help="prefill: prompt tokens (multiples of 8192 run as chunks)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
@@ -166,19 +168,31 @@ def main():
     out = torch.empty((B, H), dtype=torch.float32, device="cuda")
     ws = torch.empty(ftmoe.ft_moe_workspace_bytes(desc, B), dtype=torch.uint8, device="cuda")
     rws = torch.zeros(ftmoe.ft_route_workspace_bytes(desc, B), dtype=torch.uint8, device="cuda")
+    fws = torch.zeros(ftmoe.ft_moe_route_forward_workspace_bytes(desc, B), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     print("[bench] inputs resident; warming up", file=sys.stderr, flush=True)
 
+    def layer_call(s, l, st):
+        """One MoE layer: route + forward, as one fused call unless --separate."""
+        if args.separate:
+            ftmoe.ft_moe_route(desc, xs[s, l], routers[l], ids_all[s, l], gates_all[s, l], workspace=rws, stream=st)
+            ftmoe.ft_moe_forward(desc, xs[s, l], ids_all[s, l], gates_all[s, l], pools[l], out, ws, stream=st)
+        else:
+            ftmoe.ft_moe_route_forward(desc, xs[s, l], routers[l], ids_all[s, l], gates_all[s, l], pools[l], out,
+                                       fws, stream=st)
+
     def step(s, ev=None):
         for l in range(L):
+            if ev is None:
+                layer_call(s, l, stream)
+                continue
+            # per-forward timing: the route, then the forward between events
             ftmoe.ft_moe_route(desc, xs[s, l], routers[l], ids_all[s, l], gates_all[s, l], workspace=rws,
                                stream=stream)
-            if ev is not None:
-                ev[l][0].record(stream)
+            ev[l][0].record(stream)
             ftmoe.ft_moe_forward(desc, xs[s, l], ids_all[s, l], gates_all[s, l], pools[l], out, ws, stream=stream)
-            if ev is not None:
-                ev[l][1].record(stream)
+            ev[l][1].record(stream)
 
     if args.calibrate_copy:  # a plain copy kernel of known size, for hardware-counter calibration
         src_c = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
@@ -201,11 +215,7 @@ def main():
                 with torch.cuda.graph(g, stream=cap):
                     step_stream = torch.cuda.current_stream()
                     for l in range(L):
-                        s_ = args.warmup + gi
-                        ftmoe.ft_moe_route(desc, xs[s_, l], routers[l], ids_all[s_, l], gates_all[s_, l],
-                                           workspace=rws, stream=step_stream)
-                        ftmoe.ft_moe_forward(desc, xs[s_, l], ids_all[s_, l], gates_all[s_, l], pools[l], out, ws,
-                                             stream=step_stream)
+                        layer_call(args.warmup + gi, l, step_stream)
                 graphs.append(g)
         stream.wait_stream(cap)
         torch.cuda.synchronize()
@@ -264,7 +274,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": B, "layers": L, "hidden": H, "experts": E, "top_k": k,
                    "inter": I, "weights": "bf16", "resident_gb": round(L * E * stride / 1e9, 1),
-                   "launch": "eager" if not graphs else f"hip graphs ({len(graphs)} captured steps)"},
+                   "launch": "eager" if not graphs else f"hip graphs ({len(graphs)} captured steps)",
+                   "calls": "ft_moe_route + ft_moe_forward" if args.separate else "ft_moe_route_forward"},
         "stack_tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
         "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "ft_moe_forward (expert GEMV)",

@@ -149,6 +149,25 @@ int ft_moe_forward(const ft_moe_desc* desc, const void* x, int32_t n_tokens,
                    const uint32_t* expert_mask, float* out,
                    void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------ route + forward --
+ * One call doing ft_moe_route followed by ft_moe_forward with every expert
+ * resident at its own slot (slot = expert id), for callers whose pool holds
+ * all experts: the results (topk_ids, topk_gates, out) are bitwise those of
+ * the two calls.  For decode-sized calls (at most 16 tokens on the grouped
+ * GEMV path, at most 256 experts) the selection runs inside the gate/up
+ * kernel instead of as a launch of its own (the routing rule itself is
+ * unchanged: pages, explainer "how" and "who" sections); other sizes run
+ * the two calls in sequence.
+ * workspace: ft_moe_route_forward_workspace_bytes(desc, T) bytes, 256-byte
+ * aligned; calls sharing it must not overlap.  out must not overlap any
+ * input.  Errors: those of ft_moe_route and ft_moe_forward. */
+size_t ft_moe_route_forward_workspace_bytes(const ft_moe_desc* desc, int32_t n_tokens);
+int ft_moe_route_forward(const ft_moe_desc* desc, const void* x, int32_t n_tokens,
+                         const void* w_router, const float* sel_bias,
+                         int32_t* topk_ids, float* topk_gates,
+                         const void* pool_base, const uint32_t* expert_mask, float* out,
+                         void* workspace, size_t ws_bytes, void* stream);
+
 /* Thread-local message for the last non-OK status of this thread. */
 const char* ft_last_error(void);
 

@@ -221,4 +221,49 @@ int ft_moe_forward(const ft_moe_desc* desc, const void* x, int32_t n_tokens, con
   return FT_OK;
 }
 
+size_t ft_moe_route_forward_workspace_bytes(const ft_moe_desc* desc, int32_t n_tokens) {
+  if (check_desc(desc) || n_tokens < 0) return 0;
+  return align256(ft_route_workspace_bytes(desc, n_tokens)) + ft_moe_workspace_bytes(desc, n_tokens);
+}
+
+int ft_moe_route_forward(const ft_moe_desc* desc, const void* x, int32_t n_tokens, const void* w_router,
+                         const float* sel_bias, int32_t* topk_ids, float* topk_gates, const void* pool_base,
+                         const uint32_t* expert_mask, float* out, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (n_tokens < 0) return fail(FT_EINVAL, "n_tokens < 0");
+  if (n_tokens == 0) return FT_OK;
+  const size_t need = ft_moe_route_forward_workspace_bytes(desc, n_tokens);
+  if (!workspace || ws_bytes < need) return fail(FT_EWORKSPACE, "route + forward needs %zu workspace bytes", need);
+  if (!aligned(workspace, 256)) return fail(FT_EINVAL, "workspace must be 256-byte aligned");
+  char* rws = reinterpret_cast<char*>(workspace);
+  const size_t rbytes = align256(ft_route_workspace_bytes(desc, n_tokens));
+  char* fws = rws + rbytes;
+  const size_t fbytes = ws_bytes - rbytes;
+  const ft::FwdPlan pl = ft::plan_forward(*desc, n_tokens);
+  const bool fuse = pl.path == ft::PATH_DEC && n_tokens <= ft::ROUTE_DECODE_MAX_T && desc->n_experts <= 256;
+  if (!fuse) {
+    rc = ft_moe_route(desc, x, n_tokens, w_router, sel_bias, topk_ids, topk_gates, nullptr, rws, rbytes, stream);
+    if (rc) return rc;
+    return ft_moe_forward(desc, x, n_tokens, topk_ids, topk_gates, nullptr, pool_base, expert_mask, out, fws, fbytes,
+                          stream);
+  }
+  // the argument checks of both calls
+  if (!x || !w_router || !topk_ids || !topk_gates || !pool_base || !out)
+    return fail(FT_EINVAL, "NULL argument to ft_moe_route_forward");
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(out, 16) || !aligned(pool_base, 256))
+    return fail(FT_EINVAL, "x/w_router/out must be 16-byte aligned, pool_base 256-byte aligned");
+  const size_t rec = ft_record_bytes(desc->hidden, desc->inter, desc->w_dtype);
+  if (desc->expert_stride < (int64_t)rec || desc->expert_stride % 256)
+    return fail(FT_EINVAL, "expert_stride %lld must be >= %zu and a multiple of 256", (long long)desc->expert_stride, rec);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  double* lg = reinterpret_cast<double*>(rws + 256);
+  hipError_t e = ft::launch_route_logits_decode(*desc, x, n_tokens, w_router, lg, st);
+  if (e != hipSuccess) return hip_fail(e, "ft_moe_route_forward logits launch");
+  e = ft::launch_dec_forward(*desc, pl, x, nullptr, expert_mask, nullptr, pool_base, nullptr, out, fws, st, lg, sel_bias,
+                             topk_ids, topk_gates);
+  if (e != hipSuccess) return hip_fail(e, "ft_moe_route_forward launch");
+  return FT_OK;
+}
+
 }  // extern "C"

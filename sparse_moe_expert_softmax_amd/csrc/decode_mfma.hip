@@ -32,6 +32,7 @@
 // rely on for exactness (FreeToken explainer page, "how" section).
 #include "common.hpp"
 #include "internal.hpp"
+#include "topk.hpp"
 
 namespace ft {
 
@@ -216,12 +217,27 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 //       byte loads per chunk.
 // Weight scales of MXFP4 for chunk c, lane group g: byte 4c + g of the row;
 // NVFP4: bytes 8c + 2g and 8c + 2g + 1.
-template <int WD, int UNROLL, bool XL, bool GRP>
+// In-kernel routing for the fused route + forward call: the fp64 logits come
+// from the router's logit kernel; every gate/up workgroup selects the top-k
+// of each token itself (one wave per token) instead of waiting for a separate
+// selection launch, and workgroup 0 stores the selection as the call's
+// outputs.  logits == nullptr: ids and gates are inputs.  The kernel is
+// instantiated per logits-per-lane count (E <= 64 * RPER) so that the
+// selection code does not raise the register count of the streaming loop.
+struct DecRoute {
+  const double* logits;   // [T, E] fp64
+  const float* sel_bias;  // [T, E] selection-only bias, nullable
+  int32_t* ids_out;       // [T, k]
+  float* gates_out;       // [T, k]
+  int renormalize;
+};
+
+template <int WD, int UNROLL, bool XL, bool GRP, int RPER>
 __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P,
     int k, const void* __restrict__ pool, int64_t stride, const int32_t* __restrict__ slot_ids,
     const float* __restrict__ gates, uint16_t* __restrict__ hbuf, float* __restrict__ out, int T, int H, int I,
-    int E) {
+    int E, DecRoute route) {
   __shared__ PairInfo pi;
   __shared__ f32x4_t red[DM_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
@@ -230,6 +246,22 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     reinterpret_cast<float4*>(out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   const int n_rt = I / 8;
   const int d = blockIdx.x / n_rt, rt = blockIdx.x % n_rt;
+  if constexpr (RPER > 0) {
+    __shared__ int32_t s_ids[DEC_MAX_PAIRS];
+    __shared__ float s_gates[DEC_MAX_PAIRS];
+    __shared__ TopkScratch tsc[DM_WAVES];
+    for (int t = wv; t < T; t += DM_WAVES)
+      topk_one_token<RPER>(route.logits + (int64_t)t * E, route.sel_bias ? route.sel_bias + (int64_t)t * E : nullptr,
+                           E, k, route.renormalize, s_ids + t * k, s_gates + t * k, &tsc[wv]);
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int q = tid; q < P; q += DM_THREADS) {
+        route.ids_out[q] = s_ids[q];
+        route.gates_out[q] = s_gates[q];
+      }
+    ids = s_ids;
+    gates = s_gates;
+  }
   if (wv == 0) dm_group_pairs(ids, mask, P, E, d, &pi);
   __syncthreads();
   if (d >= pi.n_distinct) return;
@@ -518,7 +550,7 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
 template <int WD>
 static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const void* x, const int32_t* ids,
                                 const uint32_t* mask, const int32_t* slot_ids, const void* pool, const float* gates,
-                                float* out, char* ws, hipStream_t st) {
+                                float* out, char* ws, const DecRoute& route, hipStream_t st) {
   const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k;
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + pl.off_h);
   const int nd_max = pl.P < E ? pl.P : E;
@@ -526,23 +558,36 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
   const int tmax = pl.T < 16 ? pl.T : 16;
   const size_t xl_bytes = (size_t)tmax * (H + 8) * 2;
   const unsigned grid = nd_max * (I / 8);
+  const int rper = !route.logits ? 0 : (E <= 64 ? 1 : (E <= 128 ? 2 : 4));
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+#define DM_GATEUP(UN, XL_, GRP_, SH)                                                                   \
+  do {                                                                                               \
+    if (rper == 0)                                                                                   \
+      dec_gateup_kernel<WD, UN, XL_, GRP_, 0><<<grid, DM_THREADS, SH, st>>>(                         \
+          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route); \
+    else if (rper == 1)                                                                              \
+      dec_gateup_kernel<WD, UN, XL_, GRP_, 1><<<grid, DM_THREADS, SH, st>>>(                         \
+          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route); \
+    else if (rper == 2)                                                                              \
+      dec_gateup_kernel<WD, UN, XL_, GRP_, 2><<<grid, DM_THREADS, SH, st>>>(                         \
+          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route); \
+    else                                                                                             \
+      dec_gateup_kernel<WD, UN, XL_, GRP_, 4><<<grid, DM_THREADS, SH, st>>>(                         \
+          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route); \
+  } while (0)
   bool done = false;
   if constexpr (WD != FT_BF16) {
     if (xl_bytes <= 56 * 1024 && nchunk % 16 == 0) {
-      dec_gateup_kernel<WD, 4, true, true><<<grid, DM_THREADS, xl_bytes, st>>>(
-          reinterpret_cast<const uint16_t*>(x), ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf,
-          out, pl.T, H, I, E);
+      DM_GATEUP(4, true, true, xl_bytes);
       done = true;
     }
   }
-  if (!done) {
-    dec_gateup_kernel<WD, (WD == FT_BF16) ? 6 : 4, false, false><<<grid, DM_THREADS, 0, st>>>(
-        reinterpret_cast<const uint16_t*>(x), ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out,
-        pl.T, H, I, E);
-  }
+  if (!done) DM_GATEUP((WD == FT_BF16) ? 6 : 4, false, false, 0);
+#undef DM_GATEUP
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  dec_down_kernel<WD, (WD == FT_BF16) ? 3 : 2><<<(H / 16) * 2, DD_THREADS, 0, st>>>(hbuf, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids,
+  const int32_t* ids_down = route.logits ? route.ids_out : ids;  // the selection the gate/up kernel stored
+  dec_down_kernel<WD, (WD == FT_BF16) ? 3 : 2><<<(H / 16) * 2, DD_THREADS, 0, st>>>(hbuf, ids_down, mask, pl.P, k, pool, d.expert_stride, slot_ids,
                                                         out, pl.T, H, I, E);
   return hipGetLastError();
 }
@@ -558,11 +603,13 @@ bool dec_supported(const ft_moe_desc& d, int T) {
 
 hipError_t launch_dec_forward(const ft_moe_desc& d, const DecPlan& pl, const void* x, const int32_t* ids,
                               const uint32_t* mask, const int32_t* slot_ids, const void* pool, const float* gates,
-                              float* out, char* ws, hipStream_t st) {
+                              float* out, char* ws, hipStream_t st, const double* route_logits,
+                              const float* sel_bias, int32_t* ids_out, float* gates_out) {
+  const DecRoute route{route_logits, sel_bias, ids_out, gates_out, d.renormalize};
   switch (d.w_dtype) {
-    case FT_BF16: return dec_forward_t<FT_BF16>(d, pl, x, ids, mask, slot_ids, pool, gates, out, ws, st);
-    case FT_MXFP4: return dec_forward_t<FT_MXFP4>(d, pl, x, ids, mask, slot_ids, pool, gates, out, ws, st);
-    default: return dec_forward_t<FT_NVFP4>(d, pl, x, ids, mask, slot_ids, pool, gates, out, ws, st);
+    case FT_BF16: return dec_forward_t<FT_BF16>(d, pl, x, ids, mask, slot_ids, pool, gates, out, ws, route, st);
+    case FT_MXFP4: return dec_forward_t<FT_MXFP4>(d, pl, x, ids, mask, slot_ids, pool, gates, out, ws, route, st);
+    default: return dec_forward_t<FT_NVFP4>(d, pl, x, ids, mask, slot_ids, pool, gates, out, ws, route, st);
   }
 }
 

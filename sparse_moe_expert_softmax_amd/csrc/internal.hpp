@@ -14,6 +14,9 @@ hipError_t launch_route(const ft_moe_desc& d, const void* x, int T, const void* 
 constexpr int ROUTE_DECODE_MAX_T = 16;
 hipError_t launch_route_decode(const ft_moe_desc& d, const void* x, int T, const void* wr, const float* sel_bias,
                                int32_t* ids, float* gates, double* logits, hipStream_t st);
+// the fp64 logit kernel of the decode router alone (T <= ROUTE_DECODE_MAX_T)
+hipError_t launch_route_logits_decode(const ft_moe_desc& d, const void* x, int T, const void* wr, double* logits,
+                                      hipStream_t st);
 
 // slot table
 size_t slot_table_bytes(int L, int E, int S);
@@ -42,9 +45,14 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T);
 
 // decode path (matrix-core GEMV, in-kernel grouping, fused combine)
 bool dec_supported(const ft_moe_desc& d, int T);
+// route_logits != nullptr: the gate/up kernel selects the top-k from these
+// fp64 logits itself (ids and gates are then ignored) and stores the
+// selection in ids_out / gates_out.
 hipError_t launch_dec_forward(const ft_moe_desc& d, const DecPlan& pl, const void* x, const int32_t* ids,
                               const uint32_t* mask, const int32_t* slot_ids, const void* pool, const float* gates,
-                              float* out, char* ws, hipStream_t st);
+                              float* out, char* ws, hipStream_t st, const double* route_logits = nullptr,
+                              const float* sel_bias = nullptr, int32_t* ids_out = nullptr,
+                              float* gates_out = nullptr);
 
 // permutation (grouping pairs by expert, stable in pair order)
 hipError_t launch_permute(const FwdPlan& pl, const int32_t* ids, const uint32_t* mask, char* ws,

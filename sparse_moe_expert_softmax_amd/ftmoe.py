@@ -45,6 +45,9 @@ _SIGS = {
     "ft_expert_upload": (ctypes.c_int, [_vp, _i64, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_vp), _i32, _vp, _vp]),
     "ft_moe_workspace_bytes": (_sz, [ctypes.POINTER(Desc), _i32]),
     "ft_moe_forward": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ft_moe_route_forward_workspace_bytes": (_sz, [ctypes.POINTER(Desc), _i32]),
+    "ft_moe_route_forward": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _sz, _vp]),
     "ft_last_error": (ctypes.c_char_p, []),
 }
 EXPORTED = tuple(_SIGS)
@@ -141,6 +144,18 @@ def ft_moe_forward(desc: Desc, x, topk_ids, topk_gates, pool, out, workspace, sl
     _check(lib().ft_moe_forward(ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(topk_ids), _ptr(topk_gates),
                                 _ptr(slot_ids), _ptr(pool), _ptr(expert_mask), _ptr(out), _ptr(workspace),
                                 ws_bytes, _stream(stream)))
+
+
+def ft_moe_route_forward_workspace_bytes(desc: Desc, n_tokens: int) -> int:
+    return int(lib().ft_moe_route_forward_workspace_bytes(ctypes.byref(desc), n_tokens))
+
+
+def ft_moe_route_forward(desc: Desc, x, w_router, topk_ids, topk_gates, pool, out, workspace, sel_bias=None,
+                         expert_mask=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().ft_moe_route_forward(ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(w_router), _ptr(sel_bias),
+                                      _ptr(topk_ids), _ptr(topk_gates), _ptr(pool), _ptr(expert_mask), _ptr(out),
+                                      _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def ft_last_error() -> str:

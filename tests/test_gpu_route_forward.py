@@ -1,0 +1,82 @@
+"""GPU: the fused route + forward entry point against the two calls it
+replaces (ft_moe_route, then ft_moe_forward with every expert at its own
+slot) on the same inputs, bit for bit, and against the oracle.
+
+At decode sizes the selection runs inside the gate/up kernel; at other sizes
+the entry point runs the two calls in sequence.  Both branches are covered."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import LayerData, dev, max_rel_err
+from sparse_moe_expert_softmax_amd import ftmoe
+from sparse_moe_expert_softmax_amd.configs import BF16, C1, C2, C3, C5, MXFP4, MoEConfig
+
+pytestmark = pytest.mark.gpu
+
+SMALL = MoEConfig("prefill_small_mxfp4", 90, hidden=256, inter=256, n_experts=8, top_k=2, act_dtype=BF16,
+                  router_dtype=BF16, w_dtype=MXFP4, n_layers=1)
+NORENORM = MoEConfig("decode_bf16_full_softmax", 94, hidden=512, inter=256, n_experts=40, top_k=3,
+                     act_dtype=BF16, router_dtype=BF16, w_dtype=BF16, n_layers=1, renormalize=False)
+
+
+def fused_vs_separate(cfg, T, step, bias=None, mask=None):
+    ld = LayerData(cfg, 0, step, T)
+    ids, gates, _ = ld.gpu_route(bias=bias)
+    ld.build_pool(ids.cpu().numpy().ravel())
+    out = ld.gpu_forward(ids, gates, mask=mask)
+    torch.cuda.synchronize()
+
+    k = cfg.top_k
+    f_ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    f_gates = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    f_out = torch.full((T, cfg.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(ftmoe.ft_moe_route_forward_workspace_bytes(ld.desc, T), dtype=torch.uint8, device="cuda")
+    b = None if bias is None else dev(bias.astype(np.float32))
+    m = None if mask is None else dev(np.asarray(mask, dtype=np.uint32))
+    for _ in range(2):  # a second call on the same workspace gives the same results
+        ftmoe.ft_moe_route_forward(ld.desc, dev(ld.x), dev(ld.wr), f_ids, f_gates, ld.pool, f_out, ws,
+                                   sel_bias=b, expert_mask=m)
+        torch.cuda.synchronize()
+        assert torch.equal(f_ids, ids)
+        assert torch.equal(f_gates.view(torch.int32), gates.view(torch.int32))
+        assert torch.equal(f_out.view(torch.int32), out.view(torch.int32))
+    return ld, f_ids, f_gates, f_out
+
+
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_fused_bf16_decode_matches_separate_calls(T):
+    print(f"fused C2 T={T}", flush=True)
+    fused_vs_separate(C2, T, 100 + T)
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_fused_mxfp4_decode_with_selection_bias(T):
+    print(f"fused C3 T={T} with selection bias", flush=True)
+    bias = np.random.default_rng(3 + T).normal(0.0, 0.5, (T, C3.n_experts))
+    fused_vs_separate(C3, T, 110 + T, bias=bias)
+
+
+def test_fused_nvfp4_decode_with_partition_mask():
+    print("fused C5 T=4 with mask", flush=True)
+    m = np.array([0xA5A5A5A5, 0x0F0F0F0F, 0xFFFF0000, 0x12345678, 0x0, 0xFFFFFFFF, 0x3C3C3C3C, 0x55555555],
+                 dtype=np.uint32)
+    fused_vs_separate(C5, 4, 120, mask=m)
+
+
+def test_fused_full_softmax_gates_and_oracle():
+    """renormalize off (gates are full-softmax probabilities), 16 tokens:
+    the largest decode batch the fused kernel selects for."""
+    print("fused full-softmax T=16", flush=True)
+    ld, f_ids, f_gates, f_out = fused_vs_separate(NORENORM, 16, 130)
+    o_ids, o_gates, _ = ld.oracle_route()
+    np.testing.assert_array_equal(f_ids.cpu().numpy(), o_ids)
+    np.testing.assert_allclose(f_gates.cpu().numpy(), o_gates, rtol=0, atol=1e-6)
+    ref, _, _ = ld.oracle_layer()
+    assert max_rel_err(f_out.cpu().numpy(), ref) <= 1e-3
+
+
+@pytest.mark.parametrize("cfg,T", [(C1, 16), (SMALL, 300), (C2, 17)])
+def test_unfused_sizes_run_the_two_calls(cfg, T):
+    print(f"route+forward {cfg.name} T={T}", flush=True)
+    fused_vs_separate(cfg, T, 140 + T)

@@ -249,10 +249,9 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
   if constexpr (RPER > 0) {
     __shared__ int32_t s_ids[DEC_MAX_PAIRS];
     __shared__ float s_gates[DEC_MAX_PAIRS];
-    __shared__ TopkScratch tsc[DM_WAVES];
     for (int t = wv; t < T; t += DM_WAVES)
       topk_one_token<RPER>(route.logits + (int64_t)t * E, route.sel_bias ? route.sel_bias + (int64_t)t * E : nullptr,
-                           E, k, route.renormalize, s_ids + t * k, s_gates + t * k, &tsc[wv]);
+                           E, k, route.renormalize, s_ids + t * k, s_gates + t * k);
     __syncthreads();
     if (blockIdx.x == 0)
       for (int q = tid; q < P; q += DM_THREADS) {

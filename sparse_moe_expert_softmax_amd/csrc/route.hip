@@ -109,12 +109,11 @@ __global__ void __launch_bounds__(1024) route_topk_decode_kernel(const double* _
                                                                  const float* __restrict__ sel_bias,
                                                                  int32_t* __restrict__ ids, float* __restrict__ gates,
                                                                  int T, int E, int k, int renormalize) {
-  __shared__ TopkScratch sc[16];
   const int w = threadIdx.x >> 6;
   const int t = blockIdx.x * (blockDim.x >> 6) + w;
   if (t >= T) return;
   topk_one_token<PER>(logits + (int64_t)t * E, sel_bias ? sel_bias + (int64_t)t * E : nullptr, E, k, renormalize,
-                      ids + (int64_t)t * k, gates + (int64_t)t * k, &sc[w]);
+                      ids + (int64_t)t * k, gates + (int64_t)t * k);
 }
 
 template <int XDT, int WDT>

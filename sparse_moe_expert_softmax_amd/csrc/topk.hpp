@@ -14,28 +14,52 @@ __device__ __forceinline__ uint64_t dkey(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// Top-k of one token's E <= 64*PER scores by one wave, without a serial
-// chain of cross-lane shuffles: a radix select over the orderable 64-bit
-// keys (one ballot per held value and bit, most significant bit first,
-// stopping as soon as the candidate set is exactly the number still needed),
-// then the k winners are ranked by (score desc, id asc) through LDS.
-// Equal scores at the boundary go to the lowest ids.  Scratch: 32 entries
-// per wave in LDS.
-struct TopkScratch {
-  uint64_t key[32];
-  double l[32];
-  double ex[32];
-  int id[32];
-};
+// Top-k of one token's E <= 64*PER scores by one wave: k rounds of a
+// wave-wide maximum over the orderable 64-bit keys of the experts not yet
+// taken (the high halves; the low halves only where several keys share the
+// highest high half), the lowest expert id winning among equal keys.  Round j
+// yields the expert of rank j, so the order is (score desc, id asc) by
+// construction.  Keys are stored plus one, so 0 marks an expert that is
+// taken or does not exist while a NaN score (key 0) stays selectable, below
+// every number.  The gates are formed afterwards with the softmax
+// denominator summed over the winners in ascending id order.  No LDS is used.
+
+// wave-wide unsigned 32-bit maximum, returned as a uniform value: six DPP
+// steps (quads, rows of 16, then across rows), the result in lane 63; each
+// step waits the two wait states a DPP read of a just-written VGPR needs
+__device__ __forceinline__ uint32_t tk_wave_max_u32(uint32_t v) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "+v"(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ double tk_readlane_f64(double v, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 
 template <int PER>
 __device__ void topk_one_token(const double* __restrict__ lt, const float* __restrict__ bias_t, int E, int k,
-                               int renormalize, int32_t* __restrict__ ids_t, float* __restrict__ gates_t,
-                               TopkScratch* sc) {
+                               int renormalize, int32_t* __restrict__ ids_t, float* __restrict__ gates_t) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[PER];
+  uint32_t khi[PER], klo[PER];  // key + 1 of the experts not yet taken, else 0
+  int rank[PER];
   double lv[PER];
-  bool cand[PER], sel[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
@@ -43,100 +67,84 @@ __device__ void topk_one_token(const double* __restrict__ lt, const float* __res
     lv[i] = ok ? lt[e] : 0.0;
     double s = lv[i];
     if (ok && bias_t) s += (double)bias_t[e];
-    key[i] = ok ? dkey(s) : 0ull;
-    cand[i] = ok;
-    sel[i] = false;
+    const uint64_t key = ok ? dkey(s) + 1ull : 0ull;  // dkey <= dkey(+inf) < 2^64 - 1
+    khi[i] = (uint32_t)(key >> 32);
+    klo[i] = (uint32_t)key;
+    rank[i] = 0;
   }
-  int need = k;
-  for (int b = 63; b >= 0 && need > 0; --b) {
-    int n_cand = 0, c1 = 0;
-    uint64_t m1[PER];
+  double mx = -__builtin_inf();  // largest logit among the winners
+  for (int j = 0; j < k; ++j) {
+    uint32_t h = khi[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i) h = max(h, khi[i]);
+    const uint32_t mh = tk_wave_max_u32(h);
+    // experts holding that high half; the low halves decide only among several
+    uint64_t mt[PER];
+    int nt = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const bool one = cand[i] && ((key[i] >> b) & 1ull);
-      m1[i] = __ballot(one);
-      c1 += __popcll(m1[i]);
-      n_cand += __popcll(__ballot(cand[i]));
+      mt[i] = __ballot(khi[i] == mh && (khi[i] | klo[i]) != 0u);
+      nt += __popcll(mt[i]);
     }
-    if (n_cand == need) break;  // every candidate is selected
-    const bool take_ones = c1 >= need;
+    if (nt > 1) {
+      uint32_t l = 0u;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const bool one = (m1[i] >> lane) & 1ull;
-      if (take_ones) {
-        cand[i] = cand[i] && one;
-      } else {
-        if (cand[i] && one) sel[i] = true;  // strictly above the threshold
-        cand[i] = cand[i] && !one;
+      for (int i = 0; i < PER; ++i)
+        if ((mt[i] >> lane) & 1ull) l = max(l, klo[i]);
+      const uint32_t ml = tk_wave_max_u32(l);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) mt[i] = __ballot(((mt[i] >> lane) & 1ull) && klo[i] == ml);
+    }
+    int w = -1, iw = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (w < 0 && mt[i] != 0ull) { w = __builtin_ctzll(mt[i]); iw = i; }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (i == iw) {
+        if (lane == w) { rank[i] = j; khi[i] = 0u; klo[i] = 0u; }
+        // without a selection bias the first winner holds the largest logit
+        if (j == 0 || bias_t) mx = fmax(mx, tk_readlane_f64(lv[i], w));
+      }
+  }
+  // winners: the experts that exist and were taken
+  uint64_t sel[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sel[i] = __ballot(lane + 64 * i < E && (khi[i] | klo[i]) == 0u);
+  if (renormalize) {
+    double ex[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) ex[i] = ((sel[i] >> lane) & 1ull) ? exp(lv[i] - mx) : 0.0;
+    double den = 0.0;
+#pragma unroll
+    for (int iw = 0; iw < PER; ++iw) {
+      uint64_t m = sel[iw];
+      while (m) {
+        const int lw = __builtin_ctzll(m);
+        m &= m - 1;
+        den += tk_readlane_f64(ex[iw], lw);
       }
     }
-    if (!take_ones) need -= c1;
-  }
-  // remaining candidates share the threshold key (or fit exactly): take the
-  // `need` lowest ids, i.e. first in (i, lane) order
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const uint64_t m = __ballot(cand[i]);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int before = __popcll(m & below);
-    if (cand[i] && before < need) sel[i] = true;
-    need -= __popcll(m);
-    if (need < 0) need = 0;
-  }
-  // compact the winners into LDS in (i, lane) = ascending id order
-  int base = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const uint64_t m = __ballot(sel[i]);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if (sel[i]) {
-      const int pos = base + __popcll(m & below);
-      sc->key[pos] = key[i];
-      sc->l[pos] = lv[i];
-      sc->id[pos] = lane + 64 * i;
-    }
-    base += __popcll(m);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  const bool mine = lane < k;
-  uint64_t kk = 0ull;
-  int id = 0;
-  double l = 0.0;
-  int rank = 0;
-  if (mine) {
-    kk = sc->key[lane];
-    id = sc->id[lane];
-    l = sc->l[lane];
-    for (int m = 0; m < k; ++m) {
-      const uint64_t km = sc->key[m];
-      rank += (km > kk || (km == kk && sc->id[m] < id)) ? 1 : 0;
-    }
-  }
-  double g = 0.0;
-  if (renormalize) {
-    double mx = -__builtin_inf();
-    for (int m = 0; m < k; ++m) mx = fmax(mx, sc->l[m]);
-    const double ex = mine ? exp(l - mx) : 0.0;
-    if (mine) sc->ex[lane] = ex;
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    double den = 0.0;
-    for (int m = 0; m < k; ++m) den += sc->ex[m];
-    g = ex / den;
+    for (int i = 0; i < PER; ++i)
+      if ((sel[i] >> lane) & 1ull) {
+        ids_t[rank[i]] = lane + 64 * i;
+        gates_t[rank[i]] = (float)(ex[i] / den);
+      }
   } else {
-    double mx = -__builtin_inf();
-    for (int e = lane; e < E; e += 64) mx = fmax(mx, lt[e]);
+    double mxa = -__builtin_inf();
+    for (int e = lane; e < E; e += 64) mxa = fmax(mxa, lt[e]);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+    for (int o = 32; o >= 1; o >>= 1) mxa = fmax(mxa, __shfl_xor(mxa, o, 64));
     double part = 0.0;
-    for (int e = lane; e < E; e += 64) part += exp(lt[e] - mx);
+    for (int e = lane; e < E; e += 64) part += exp(lt[e] - mxa);
     const double den = wave_sum(part);
-    g = mine ? exp(l - mx) / den : 0.0;
-  }
-  if (mine) {
-    ids_t[rank] = id;
-    gates_t[rank] = (float)g;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if ((sel[i] >> lane) & 1ull) {
+        ids_t[rank[i]] = lane + 64 * i;
+        gates_t[rank[i]] = (float)(exp(lv[i] - mxa) / den);
+      }
   }
 }
 

@@ -96,7 +96,12 @@ size_t ft_record_bytes(int32_t hidden, int32_t inter, int32_t w_dtype) {
 
 size_t ft_route_workspace_bytes(const ft_moe_desc* desc, int32_t n_tokens) {
   if (!desc || n_tokens < 0) return 0;
-  return 256 + align256(sizeof(double) * (size_t)n_tokens * desc->n_experts);
+  // fp64 logits [T, E]; also room for the bounded prefill path's fp32
+  // approximate logits [T, E] and fp64 squared norms [T] and [E]
+  const size_t te = (size_t)n_tokens * desc->n_experts;
+  const size_t a = sizeof(double) * te;
+  const size_t b = sizeof(float) * (te + 64) + sizeof(double) * ((size_t)n_tokens + 32 + desc->n_experts);
+  return 256 + align256(a > b ? a : b);
 }
 
 int ft_moe_route(const ft_moe_desc* desc, const void* x, int32_t n_tokens, const void* w_router,
@@ -116,7 +121,8 @@ int ft_moe_route(const ft_moe_desc* desc, const void* x, int32_t n_tokens, const
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = (n_tokens <= ft::ROUTE_DECODE_MAX_T)
                      ? ft::launch_route_decode(*desc, x, n_tokens, w_router, sel_bias, topk_ids, topk_gates, lg, st)
-                     : ft::launch_route(*desc, x, n_tokens, w_router, sel_bias, topk_ids, topk_gates, lg, st);
+                     : ft::launch_route(*desc, x, n_tokens, w_router, sel_bias, topk_ids, topk_gates, lg,
+                                        logits != nullptr, st);
   if (e != hipSuccess) return hip_fail(e, "ft_moe_route launch");
   return FT_OK;
 }

@@ -9,8 +9,10 @@
 namespace ft {
 
 // router
+// logits: [T, E] fp64 (the caller's when want_logits, else workspace, which
+// the bounded prefill path also uses for its own arrays)
 hipError_t launch_route(const ft_moe_desc& d, const void* x, int T, const void* wr, const float* sel_bias,
-                        int32_t* ids, float* gates, double* logits, hipStream_t st);
+                        int32_t* ids, float* gates, double* logits, bool want_logits, hipStream_t st);
 constexpr int ROUTE_DECODE_MAX_T = 16;
 hipError_t launch_route_decode(const ft_moe_desc& d, const void* x, int T, const void* wr, const float* sel_bias,
                                int32_t* ids, float* gates, double* logits, hipStream_t st);

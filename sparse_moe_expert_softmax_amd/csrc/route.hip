@@ -339,11 +339,237 @@ __global__ void __launch_bounds__(256) route_logits_mfma_kernel(const void* __re
     }
 }
 
+// ------------------------------------------------ prefill, bounded path --
+// Many tokens with bf16 x and W_r: the fp64 logits of every (token, expert)
+// are more work than the selection needs.  Approximate logits L~ come from
+// bf16 matrix cores with fp32 accumulation; every product of two bf16
+// values is exact in fp32, and any fp32 summation of the H products (each
+// addition faithfully rounded or better, plus one accumulator addition per
+// 32 products) is within 2^-23 * (H + H/32) * sum|x_h w_eh| of the exact
+// logit, and sum|x_h w_eh| <= |x| |w| (Cauchy-Schwarz).  So with
+// B = 2^-23 * 1.125 H * sqrt(|x|^2 |w|^2) (squared norms in fp64) the exact
+// score lies in [s~ - B, s~ + B].  Experts whose upper end lies below the
+// k-th largest lower end cannot be selected; the rest (the k certain ones and
+// the few near the boundary) get their logits recomputed exactly in fp64, and
+// the selection and the gates are taken on those exact values.  Non-finite
+// bounds (non-finite inputs) recompute every expert.
+constexpr int RA_T = 64;   // tokens per workgroup
+constexpr int RA_E = 128;  // experts per workgroup
+constexpr int RA_K = 64;   // K per LDS stage
+
+typedef __bf16 ra_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float ra_f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ ra_bf16x8_t ra_as_bf16x8(uint4 v) {
+  ra_bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__device__ __forceinline__ double ra_sq8(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double a = bf16_lo(w[j]), b = bf16_hi(w[j]);
+    s = fma(a, a, s);
+    s = fma(b, b, s);
+  }
+  return s;
+}
+
+// L~ [T, E] fp32, |x_t|^2 [T] and |w_e|^2 [E] in fp64.  Grid (T/64, E/128);
+// four waves of 16 tokens x 128 experts (8 blocks of 16, v_mfma_f32_16x16x32_bf16).
+// W_r goes through double-buffered LDS in 64-K stages, rows of 128 bytes with
+// 16-byte chunks XOR-swizzled by (row >> 1) & 7.
+__global__ void __launch_bounds__(256) route_approx_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wr, float* __restrict__ la,
+                                                           double* __restrict__ nx, double* __restrict__ nw, int T,
+                                                           int H, int E) {
+  __shared__ __attribute__((aligned(16))) uint8_t ws[2][RA_E * RA_K * 2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int t0 = blockIdx.x * RA_T, e0 = blockIdx.y * RA_E;
+  const int ta = t0 + 16 * wv + c16;
+  const bool tok_ok = ta < T;
+  const uint16_t* xr = x + (int64_t)(tok_ok ? ta : T - 1) * H;
+  // stage pieces: p = tid + 256 j -> expert e0 + p/8, chunk p%8 (8 bf16)
+  auto gload = [&](int k0, uint4 (&r)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = tid + 256 * j, e = e0 + p / 8;
+      r[j] = (e < E) ? *reinterpret_cast<const uint4*>(wr + (int64_t)e * H + k0 + (p % 8) * 8)
+                     : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf, const uint4 (&r)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = tid + 256 * j, row = p / 8, c = p % 8;
+      *reinterpret_cast<uint4*>(&ws[buf][row * 128 + 16 * (c ^ ((row >> 1) & 7))]) = r[j];
+    }
+  };
+  ra_f32x4_t acc[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) acc[b] = (ra_f32x4_t){0.f, 0.f, 0.f, 0.f};
+  double nxa = 0.0, nwa[4] = {0.0, 0.0, 0.0, 0.0};
+  const bool do_nw = blockIdx.x == 0;
+  const int nkc = H / RA_K;
+  uint4 r[4];
+  gload(0, r);
+  if (do_nw) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nwa[j] += ra_sq8(r[j]);
+  }
+  lstore(0, r);
+  __syncthreads();
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int cur = kc & 1;
+    if (kc + 1 < nkc) {
+      gload((kc + 1) * RA_K, r);
+      if (do_nw) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nwa[j] += ra_sq8(r[j]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 a = tok_ok ? *reinterpret_cast<const uint4*>(xr + kc * RA_K + ks * 32 + 8 * g)
+                             : make_uint4(0, 0, 0, 0);
+      nxa += ra_sq8(a);
+      const ra_bf16x8_t av = ra_as_bf16x8(a);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int row = 16 * b + c16;
+        const uint4 bv = *reinterpret_cast<const uint4*>(&ws[cur][row * 128 + 16 * ((4 * ks + g) ^ ((row >> 1) & 7))]);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ra_as_bf16x8(bv), acc[b], 0, 0, 0);
+      }
+    }
+    if (kc + 1 < nkc) lstore(cur ^ 1, r);
+    __syncthreads();
+  }
+  // D[4 g + i][c16]: token t0 + 16 wv + 4 g + i, expert e0 + 16 b + c16
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int e = e0 + 16 * b + c16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * wv + 4 * g + i;
+      if (t < T && e < E) la[(int64_t)t * E + e] = acc[b][i];
+    }
+  }
+  // |x|^2: the four lane groups of a token hold disjoint K pieces
+  nxa += __shfl_xor(nxa, 16, 64);
+  nxa += __shfl_xor(nxa, 32, 64);
+  if (blockIdx.y == 0 && g == 0 && tok_ok) nx[ta] = nxa;
+  if (do_nw) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      double v = nwa[j];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      const int e = e0 + (tid + 256 * j) / 8;
+      if ((tid & 7) == 0 && e < E) nw[e] = v;
+    }
+  }
+}
+
+// One wave per token: bounds, candidates, exact fp64 logits of the
+// candidates (fixed per-lane order, then a fixed butterfly), selection and gates.
+template <int PER>
+__global__ void __launch_bounds__(256) route_refine_kernel(const float* __restrict__ la, const double* __restrict__ nx,
+                                                           const double* __restrict__ nw,
+                                                           const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wr,
+                                                           const float* __restrict__ sel_bias,
+                                                           int32_t* __restrict__ ids, float* __restrict__ gates, int T,
+                                                           int H, int E, int k) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const double cB = 1.125 * (double)H * 0x1p-23;
+  const double nxt = nx[t];
+  uint32_t lhi[PER], llo[PER];
+  double ub[PER];
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    const bool ok = e < E;
+    double s = ok ? (double)la[(int64_t)t * E + e] : 0.0;
+    if (ok && sel_bias) s += (double)sel_bias[(int64_t)t * E + e];
+    const double bnd = ok ? cB * sqrt(nxt * nw[e]) * (1.0 + 1e-12) + 1e-30 + fabs(s) * 1e-15 : 0.0;
+    if (ok && !(fabs(s) <= 1e300 && bnd <= 1e300)) bad = true;
+    const uint64_t lk = ok ? dkey(s - bnd) + 1ull : 0ull;
+    lhi[i] = (uint32_t)(lk >> 32);
+    llo[i] = (uint32_t)lk;
+    ub[i] = s + bnd;
+  }
+  const bool full = __ballot(bad) != 0ull;
+  uint64_t cand[PER];
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) cand[i] = __ballot(lane + 64 * i < E);
+  } else {
+    const uint64_t kth = tk_kth_largest<PER>(lhi, llo, k);  // k-th largest lower end (key + 1)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) cand[i] = __ballot(lane + 64 * i < E && dkey(ub[i]) + 1ull >= kth);
+  }
+  // exact logits of the candidates; everything else cannot win
+  double lv[PER], sv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) { lv[i] = -__builtin_inf(); sv[i] = -__builtin_inf(); }
+  const uint16_t* xr = x + (int64_t)t * H;
+#pragma unroll
+  for (int iw = 0; iw < PER; ++iw) {
+    uint64_t m = cand[iw];
+    while (m) {
+      const int lw = __builtin_ctzll(m);
+      m &= m - 1;
+      const int e = lw + 64 * iw;
+      const uint16_t* wrow = wr + (int64_t)e * H;
+      double acc = 0.0;
+      for (int h = 8 * lane; h < H; h += 512) {
+        double xv[8], wv8[8];
+        load8_f64<FT_BF16>(xr, h, xv);
+        load8_f64<FT_BF16>(wrow, h, wv8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = fma(xv[j], wv8[j], acc);
+      }
+      const double l = wave_sum(acc);
+      if (lane == lw) {
+        lv[iw] = l;
+        sv[iw] = sel_bias ? l + (double)sel_bias[(int64_t)t * E + e] : l;
+      }
+    }
+  }
+  topk_core<PER>(lv, sv, sel_bias != nullptr, E, k, 1, ids + (int64_t)t * k, gates + (int64_t)t * k);
+}
+
 hipError_t launch_route(const ft_moe_desc& d, const void* x, int T, const void* wr,
                         const float* sel_bias, int32_t* ids, float* gates, double* logits,
-                        hipStream_t st) {
+                        bool want_logits, hipStream_t st) {
   dim3 grid((T + RL_TT - 1) / RL_TT, (d.n_experts + RL_TE - 1) / RL_TE);
   const int xd = d.act_dtype, wd = d.router_dtype, H = d.hidden, E = d.n_experts;
+  if (xd == FT_BF16 && wd == FT_BF16 && !want_logits && d.renormalize && H % RA_K == 0 && E <= 1024) {
+    // bounded path; the logits buffer [T, E] fp64 holds L~ [T, E] fp32, then |x|^2, |w|^2
+    float* la = reinterpret_cast<float*>(logits);
+    double* nx = reinterpret_cast<double*>(la + (((int64_t)T * E + 63) / 64) * 64);
+    double* nw = nx + ((T + 31) / 32) * 32;
+    route_approx_kernel<<<dim3((T + RA_T - 1) / RA_T, (E + RA_E - 1) / RA_E), 256, 0, st>>>(
+        reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(wr), la, nx, nw, T, H, E);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int nb = (T + 3) / 4, k = d.top_k;
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+    const uint16_t* wb = reinterpret_cast<const uint16_t*>(wr);
+    if (E <= 64) route_refine_kernel<1><<<nb, 256, 0, st>>>(la, nx, nw, xb, wb, sel_bias, ids, gates, T, H, E, k);
+    else if (E <= 128) route_refine_kernel<2><<<nb, 256, 0, st>>>(la, nx, nw, xb, wb, sel_bias, ids, gates, T, H, E, k);
+    else if (E <= 256) route_refine_kernel<4><<<nb, 256, 0, st>>>(la, nx, nw, xb, wb, sel_bias, ids, gates, T, H, E, k);
+    else if (E <= 512) route_refine_kernel<8><<<nb, 256, 0, st>>>(la, nx, nw, xb, wb, sel_bias, ids, gates, T, H, E, k);
+    else route_refine_kernel<16><<<nb, 256, 0, st>>>(la, nx, nw, xb, wb, sel_bias, ids, gates, T, H, E, k);
+    return hipGetLastError();
+  }
   dim3 mgrid((T + RM_T - 1) / RM_T, (E + RM_E - 1) / RM_E);
   if (H % 32 == 0) {  // matrix-core path
     if (xd == FT_BF16 && wd == FT_BF16)

@@ -53,21 +53,18 @@ __device__ __forceinline__ double tk_readlane_f64(double v, int l) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// The selection from values in registers: lane l holds expert l + 64 i as
+// logit lv[i] and score sv[i] (logit plus any selection bias).
 template <int PER>
-__device__ void topk_one_token(const double* __restrict__ lt, const float* __restrict__ bias_t, int E, int k,
-                               int renormalize, int32_t* __restrict__ ids_t, float* __restrict__ gates_t) {
+__device__ void topk_core(const double (&lv)[PER], const double (&sv)[PER], bool has_bias, int E, int k,
+                          int renormalize, int32_t* __restrict__ ids_t, float* __restrict__ gates_t) {
   const int lane = threadIdx.x & 63;
   uint32_t khi[PER], klo[PER];  // key + 1 of the experts not yet taken, else 0
   int rank[PER];
-  double lv[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    const bool ok = e < E;
-    lv[i] = ok ? lt[e] : 0.0;
-    double s = lv[i];
-    if (ok && bias_t) s += (double)bias_t[e];
-    const uint64_t key = ok ? dkey(s) + 1ull : 0ull;  // dkey <= dkey(+inf) < 2^64 - 1
+    const bool ok = lane + 64 * i < E;
+    const uint64_t key = ok ? dkey(sv[i]) + 1ull : 0ull;  // dkey <= dkey(+inf) < 2^64 - 1
     khi[i] = (uint32_t)(key >> 32);
     klo[i] = (uint32_t)key;
     rank[i] = 0;
@@ -104,7 +101,7 @@ __device__ void topk_one_token(const double* __restrict__ lt, const float* __res
       if (i == iw) {
         if (lane == w) { rank[i] = j; khi[i] = 0u; klo[i] = 0u; }
         // without a selection bias the first winner holds the largest logit
-        if (j == 0 || bias_t) mx = fmax(mx, tk_readlane_f64(lv[i], w));
+        if (j == 0 || has_bias) mx = fmax(mx, tk_readlane_f64(lv[i], w));
       }
   }
   // winners: the experts that exist and were taken
@@ -133,11 +130,15 @@ __device__ void topk_one_token(const double* __restrict__ lt, const float* __res
       }
   } else {
     double mxa = -__builtin_inf();
-    for (int e = lane; e < E; e += 64) mxa = fmax(mxa, lt[e]);
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i < E) mxa = fmax(mxa, lv[i]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) mxa = fmax(mxa, __shfl_xor(mxa, o, 64));
     double part = 0.0;
-    for (int e = lane; e < E; e += 64) part += exp(lt[e] - mxa);
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i < E) part += exp(lv[i] - mxa);
     const double den = wave_sum(part);
 #pragma unroll
     for (int i = 0; i < PER; ++i)
@@ -146,6 +147,68 @@ __device__ void topk_one_token(const double* __restrict__ lt, const float* __res
         gates_t[rank[i]] = (float)(exp(lv[i] - mxa) / den);
       }
   }
+}
+
+template <int PER>
+__device__ void topk_one_token(const double* __restrict__ lt, const float* __restrict__ bias_t, int E, int k,
+                               int renormalize, int32_t* __restrict__ ids_t, float* __restrict__ gates_t) {
+  const int lane = threadIdx.x & 63;
+  double lv[PER], sv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    const bool ok = e < E;
+    lv[i] = ok ? lt[e] : 0.0;
+    sv[i] = lv[i];
+    if (ok && bias_t) sv[i] += (double)bias_t[e];
+  }
+  topk_core<PER>(lv, sv, bias_t != nullptr, E, k, renormalize, ids_t, gates_t);
+}
+
+// The k-th largest of the wave's keys (key + 1 per expert, 0 = absent),
+// by the same rounds of wave maxima.
+template <int PER>
+__device__ uint64_t tk_kth_largest(uint32_t (&khi)[PER], uint32_t (&klo)[PER], int k) {
+  const int lane = threadIdx.x & 63;
+  uint64_t last = 0ull;
+  for (int j = 0; j < k; ++j) {
+    uint32_t h = khi[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i) h = max(h, khi[i]);
+    const uint32_t mh = tk_wave_max_u32(h);
+    uint64_t mt[PER];
+    int nt = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      mt[i] = __ballot(khi[i] == mh && (khi[i] | klo[i]) != 0u);
+      nt += __popcll(mt[i]);
+    }
+    uint32_t ml;
+    {
+      uint32_t l = 0u;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if ((mt[i] >> lane) & 1ull) l = max(l, klo[i]);
+      ml = (nt > 1) ? tk_wave_max_u32(l) : (uint32_t)0;
+      if (nt == 1) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          if (mt[i]) ml = (uint32_t)__builtin_amdgcn_readlane((int)klo[i], __builtin_ctzll(mt[i]));
+      }
+    }
+    last = ((uint64_t)mh << 32) | ml;
+    // remove one expert holding that key (the lowest id; which one does not matter)
+    int w = -1, iw = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint64_t m = __ballot(((mt[i] >> lane) & 1ull) && klo[i] == ml);
+      if (w < 0 && m != 0ull) { w = __builtin_ctzll(m); iw = i; }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (i == iw && lane == w) { khi[i] = 0u; klo[i] = 0u; }
+  }
+  return last;
 }
 
 }  // namespace ft

@@ -347,18 +347,30 @@ __global__ void __launch_bounds__(256) route_logits_mfma_kernel(const void* __re
 // addition faithfully rounded or better, plus one accumulator addition per
 // 32 products) is within 2^-23 * (H + H/32) * sum|x_h w_eh| of the exact
 // logit, and sum|x_h w_eh| <= |x| |w| (Cauchy-Schwarz).  So with
-// B = 2^-23 * 1.125 H * sqrt(|x|^2 |w|^2) (squared norms in fp64) the exact
-// score lies in [s~ - B, s~ + B].  Experts whose upper end lies below the
+// B = 2^-23 * 1.125 H * |x| |w| (each norm replaced by an upper bound taken
+// from an fp32 sum of squares, ra_norm_upper) the exact score lies in
+// [s~ - B, s~ + B]; the two K halves of the matrix-core sum add one more
+// rounding, inside the slack of 1.125 H.  Experts whose upper end lies below the
 // k-th largest lower end cannot be selected; the rest (the k certain ones and
 // the few near the boundary) get their logits recomputed exactly in fp64, and
 // the selection and the gates are taken on those exact values.  Non-finite
 // bounds (non-finite inputs) recompute every expert.
 constexpr int RA_T = 64;   // tokens per workgroup
 constexpr int RA_E = 128;  // experts per workgroup
-constexpr int RA_K = 64;   // K per LDS stage
+constexpr int RA_K = 128;  // K per LDS stage (two halves of 64, one per wave group)
+constexpr int RF_Q = 8;    // refine: 16-byte pieces per lane held in registers (H <= 4096)
 
 typedef __bf16 ra_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 ra_bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float ra_f32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes from a valid address, zeroed where ok is false (an unconditional
+// load and a select: no branch around the load)
+__device__ __forceinline__ uint4 ra_ld16(const uint16_t* p, bool ok) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t m = 0u - (uint32_t)ok;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
 
 __device__ __forceinline__ ra_bf16x8_t ra_as_bf16x8(uint4 v) {
   ra_bf16x8_t r;
@@ -366,119 +378,167 @@ __device__ __forceinline__ ra_bf16x8_t ra_as_bf16x8(uint4 v) {
   return r;
 }
 
-__device__ __forceinline__ double ra_sq8(uint4 v) {
+// s + the squares of the eight bf16 values in v, fp32 (v_dot2c_f32_bf16)
+__device__ __forceinline__ float ra_sq8(uint4 v, float s) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  double s = 0.0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const double a = bf16_lo(w[j]), b = bf16_hi(w[j]);
-    s = fma(a, a, s);
-    s = fma(b, b, s);
+    ra_bf16x2_t p;
+    __builtin_memcpy(&p, &w[j], 4);
+    s = __builtin_amdgcn_fdot2_f32_bf16(p, p, s, false);
   }
   return s;
 }
 
-// L~ [T, E] fp32, |x_t|^2 [T] and |w_e|^2 [E] in fp64.  Grid (T/64, E/128);
-// four waves of 16 tokens x 128 experts (8 blocks of 16, v_mfma_f32_16x16x32_bf16).
-// W_r goes through double-buffered LDS in 64-K stages, rows of 128 bytes with
-// 16-byte chunks XOR-swizzled by (row >> 1) & 7.
-__global__ void __launch_bounds__(256) route_approx_kernel(const uint16_t* __restrict__ x,
+// Upper bound on sqrt(sum of squares) from its fp32 accumulation over n
+// terms: every square of a bf16 value is exact in fp32, each two-term step
+// rounds at most twice (relative error below 2^-23 per step even for a
+// directed rounding), so the exact sum is below q (1 + n 2^-21); squares
+// flushed below the normal range add at most n 2^-126.
+__device__ __forceinline__ double ra_norm_upper(float q, int n) {
+  return sqrt((double)q * (1.0 + (double)n * 0x1p-21) + (double)n * 0x1p-120) * (1.0 + 0x1p-50);
+}
+
+// L~ [T, E] fp32 and |w_e| [E] (an upper bound, fp64).  Grid (T/64, E/128),
+// eight waves: wave (wt, kh) takes tokens 16 wt .. 16 wt + 15 and all 128
+// experts of the tile (8 blocks of v_mfma_f32_16x16x32_bf16) over the K half
+// kh of every 128-K stage; the two halves are added once at the end in a
+// fixed order.  W_r goes through double-buffered LDS, one 128 x 64
+// sub-buffer per K half, rows of 128 bytes with 16-byte chunks XOR-swizzled
+// by (row >> 1) & 7; x goes straight to registers, four stages ahead.
+// |w_e|^2 is summed by one wave per group of rows, in the first eight
+// workgroups of a column only.  (A 2 x 4 block per wave, which halves the
+// LDS reads per product, measured slower: it doubles the x loads.)
+__global__ void __launch_bounds__(512) route_approx_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ wr, float* __restrict__ la,
-                                                           double* __restrict__ nx, double* __restrict__ nw, int T,
+                                                           double* __restrict__ rw, int T,
                                                            int H, int E) {
-  __shared__ __attribute__((aligned(16))) uint8_t ws[2][RA_E * RA_K * 2];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  constexpr int HALF = RA_E * 64 * 2;  // bytes of one K-half sub-buffer
+  __shared__ __attribute__((aligned(16))) uint8_t ws[2][2 * HALF];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wt = wv & 3, kh = wv >> 2;
+  const int g = lane >> 4, c16 = lane & 15;
   const int t0 = blockIdx.x * RA_T, e0 = blockIdx.y * RA_E;
-  const int ta = t0 + 16 * wv + c16;
+  const int ta = t0 + 16 * wt + c16;
   const bool tok_ok = ta < T;
-  const uint16_t* xr = x + (int64_t)(tok_ok ? ta : T - 1) * H;
-  // stage pieces: p = tid + 256 j -> expert e0 + p/8, chunk p%8 (8 bf16)
-  auto gload = [&](int k0, uint4 (&r)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = tid + 256 * j, e = e0 + p / 8;
-      r[j] = (e < E) ? *reinterpret_cast<const uint4*>(wr + (int64_t)e * H + k0 + (p % 8) * 8)
-                     : make_uint4(0, 0, 0, 0);
-    }
+  const uint16_t* xr = x + (int64_t)(tok_ok ? ta : T - 1) * H + 64 * kh + 8 * g;
+  // stage pieces j < 4: K half j / 2, row (tid >> 3) + 64 (j & 1), chunk tid & 7
+  const int prow = tid >> 3, pc = tid & 7;
+  const uint16_t* wa = wr + (int64_t)min(e0 + prow, E - 1) * H + 8 * pc;
+  const uint16_t* wb = wr + (int64_t)min(e0 + prow + 64, E - 1) * H + 8 * pc;
+  const bool oka = e0 + prow < E, okb = e0 + prow + 64 < E;
+  const int gx = gridDim.x;
+  const bool do_nw = (gx >= 8) ? ((int)blockIdx.x == wv) : (wv % gx == (int)blockIdx.x);
+  // Rows past T or E, and stages past the last one, are read at a clamped
+  // (valid) place and zeroed after the load, so the loop below has no
+  // branches: it runs a multiple of four stages, the extra ones all zeros
+  // (both operands zero: they add exactly +0).
+  const int nkc = H / RA_K, nkc4 = (nkc + 3) & ~3;
+  auto wload = [&](int kc, uint4 (&r)[4]) {
+    const int k0 = min(kc, nkc - 1) * RA_K;
+    const bool ks = kc < nkc;
+    r[0] = ra_ld16(wa + k0, oka && ks);
+    r[1] = ra_ld16(wb + k0, okb && ks);
+    r[2] = ra_ld16(wa + k0 + 64, oka && ks);
+    r[3] = ra_ld16(wb + k0 + 64, okb && ks);
   };
+  auto xload = [&](int kc, uint4 (&xa)[2]) {
+    const int k0 = min(kc, nkc - 1) * RA_K;
+    const bool ks = kc < nkc;
+    xa[0] = ra_ld16(xr + k0, tok_ok && ks);
+    xa[1] = ra_ld16(xr + k0 + 32, tok_ok && ks);
+  };
+  float nwa = 0.f, nwb = 0.f;
+  // |w|^2 of the stage in r, then r into LDS buffer buf
   auto lstore = [&](int buf, const uint4 (&r)[4]) {
+    if (do_nw) {
+      nwa = ra_sq8(r[0], nwa);
+      nwb = ra_sq8(r[1], nwb);
+      nwa = ra_sq8(r[2], nwa);
+      nwb = ra_sq8(r[3], nwb);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int p = tid + 256 * j, row = p / 8, c = p % 8;
-      *reinterpret_cast<uint4*>(&ws[buf][row * 128 + 16 * (c ^ ((row >> 1) & 7))]) = r[j];
+      const int row = prow + 64 * (j & 1);
+      *reinterpret_cast<uint4*>(&ws[buf][(j >> 1) * HALF + row * 128 + 16 * (pc ^ ((row >> 1) & 7))]) = r[j];
     }
   };
   ra_f32x4_t acc[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) acc[b] = (ra_f32x4_t){0.f, 0.f, 0.f, 0.f};
-  double nxa = 0.0, nwa[4] = {0.0, 0.0, 0.0, 0.0};
-  const bool do_nw = blockIdx.x == 0;
-  const int nkc = H / RA_K;
-  uint4 r[4];
-  gload(0, r);
-  if (do_nw) {
+  // x of stages kc .. kc + 3 in flight in xs[kc % 4]; W of stage kc + 1 in wq[(kc + 1) % 2]
+  uint4 xs[4][2], wq[2][4];
+  wload(0, wq[0]);
+  wload(1, wq[1]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) nwa[j] += ra_sq8(r[j]);
-  }
-  lstore(0, r);
+  for (int u = 0; u < 4; ++u) xload(u, xs[u]);
+  lstore(0, wq[0]);
   __syncthreads();
-  for (int kc = 0; kc < nkc; ++kc) {
-    const int cur = kc & 1;
-    if (kc + 1 < nkc) {
-      gload((kc + 1) * RA_K, r);
-      if (do_nw) {
+  for (int kc4 = 0; kc4 < nkc4; kc4 += 4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) nwa[j] += ra_sq8(r[j]);
+    for (int u = 0; u < 4; ++u) {
+      const int kc = kc4 + u;
+      wload(kc + 2, wq[u & 1]);
+      const uint8_t* wsb = &ws[u & 1][kh * HALF];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 bv[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const int row = 16 * b + c16;
+          bv[b] = *reinterpret_cast<const uint4*>(&wsb[row * 128 + 16 * ((4 * ks + g) ^ ((row >> 1) & 7))]);
+        }
+        const ra_bf16x8_t av = ra_as_bf16x8(xs[u][ks]);
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ra_as_bf16x8(bv[b]), acc[b], 0, 0, 0);
       }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint4 a = tok_ok ? *reinterpret_cast<const uint4*>(xr + kc * RA_K + ks * 32 + 8 * g)
-                             : make_uint4(0, 0, 0, 0);
-      nxa += ra_sq8(a);
-      const ra_bf16x8_t av = ra_as_bf16x8(a);
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int row = 16 * b + c16;
-        const uint4 bv = *reinterpret_cast<const uint4*>(&ws[cur][row * 128 + 16 * ((4 * ks + g) ^ ((row >> 1) & 7))]);
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ra_as_bf16x8(bv), acc[b], 0, 0, 0);
-      }
-    }
-    if (kc + 1 < nkc) lstore(cur ^ 1, r);
-    __syncthreads();
-  }
-  // D[4 g + i][c16]: token t0 + 16 wv + 4 g + i, expert e0 + 16 b + c16
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int e = e0 + 16 * b + c16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * wv + 4 * g + i;
-      if (t < T && e < E) la[(int64_t)t * E + e] = acc[b][i];
+      xload(kc + 4, xs[u]);
+      lstore((u + 1) & 1, wq[(u + 1) & 1]);
+      __syncthreads();
     }
   }
-  // |x|^2: the four lane groups of a token hold disjoint K pieces
-  nxa += __shfl_xor(nxa, 16, 64);
-  nxa += __shfl_xor(nxa, 32, 64);
-  if (blockIdx.y == 0 && g == 0 && tok_ok) nx[ta] = nxa;
-  if (do_nw) {
+  // the K half 1 waves hand their partial sums over through LDS
+  float* red = reinterpret_cast<float*>(&ws[0][0]);  // [4 wt][8 b][4 i][64 lanes], then nx [4 wt][64]
+  if (kh == 1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      double v = nwa[j];
-      v += __shfl_xor(v, 1, 64);
-      v += __shfl_xor(v, 2, 64);
-      v += __shfl_xor(v, 4, 64);
-      const int e = e0 + (tid + 256 * j) / 8;
-      if ((tid & 7) == 0 && e < E) nw[e] = v;
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[((wt * 8 + b) * 4 + i) * 64 + lane] = acc[b][i];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    // D[4 g + i][c16]: token t0 + 16 wt + 4 g + i, expert e0 + 16 b + c16
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int e = e0 + 16 * b + c16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * wt + 4 * g + i;
+        const float v = acc[b][i] + red[((wt * 8 + b) * 4 + i) * 64 + lane];
+        if (t < T && e < E) la[(int64_t)t * E + e] = v;
+      }
     }
+  }
+  // |w|: the eight lanes of a row hold disjoint chunks of every stage
+  nwa += __shfl_xor(nwa, 1, 64);
+  nwa += __shfl_xor(nwa, 2, 64);
+  nwa += __shfl_xor(nwa, 4, 64);
+  nwb += __shfl_xor(nwb, 1, 64);
+  nwb += __shfl_xor(nwb, 2, 64);
+  nwb += __shfl_xor(nwb, 4, 64);
+  if (do_nw && pc == 0) {
+    if (oka) rw[e0 + prow] = ra_norm_upper(nwa, H + 8);
+    if (okb) rw[e0 + prow + 64] = ra_norm_upper(nwb, H + 8);
   }
 }
 
-// One wave per token: bounds, candidates, exact fp64 logits of the
-// candidates (fixed per-lane order, then a fixed butterfly), selection and gates.
-template <int PER>
-__global__ void __launch_bounds__(256) route_refine_kernel(const float* __restrict__ la, const double* __restrict__ nx,
-                                                           const double* __restrict__ nw,
+// One wave per token: |x_t|, bounds, candidates, exact fp64 logits of the
+// candidates, selection and gates.  Lane l owns the 16-byte pieces of a row
+// at elements 8 l + 512 q.  Short rows (H <= 512 RF_Q, LONG false) keep the
+// x row in registers; long rows go through it in chunks of 512 RF_Q.
+template <int PER, bool LONG>
+__global__ void __launch_bounds__(256) route_refine_kernel(const float* __restrict__ la,
+                                                           const double* __restrict__ rw,
                                                            const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ wr,
                                                            const float* __restrict__ sel_bias,
@@ -487,18 +547,36 @@ __global__ void __launch_bounds__(256) route_refine_kernel(const float* __restri
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  auto load_row = [&](const uint16_t* row, int q0, uint4 (&r)[RF_Q]) {  // row points at element 8 lane
+#pragma unroll
+    for (int q = 0; q < RF_Q; ++q) {
+      const int off = 512 * (q0 + q), ok = 8 * lane + off < H;
+      r[q] = ra_ld16(row + (ok ? off : -8 * lane), ok);  // pieces past H read the row's start
+    }
+  };
+  const uint16_t* xr = x + (int64_t)t * H + 8 * lane;
+  uint4 xq[RF_Q], wq[RF_Q];
+  // |x_t|^2: fp32 partial sums per lane, then a fixed butterfly (H + 64 roundings at most)
+  float q2 = 0.f;
+  for (int q0 = 0; q0 == 0 || (LONG && 512 * q0 < H); q0 += RF_Q) {
+    load_row(xr, q0, xq);
+#pragma unroll
+    for (int q = 0; q < RF_Q; ++q) q2 = ra_sq8(xq[q], q2);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) q2 += __shfl_xor(q2, o, 64);
+  const double rxt = ra_norm_upper(q2, H + 64);
   const double cB = 1.125 * (double)H * 0x1p-23;
-  const double nxt = nx[t];
   uint32_t lhi[PER], llo[PER];
   double ub[PER];
   bool bad = false;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
+    const int e = lane + 64 * i, ec = min(e, E - 1);  // lanes past E read expert E - 1, then drop it
     const bool ok = e < E;
-    double s = ok ? (double)la[(int64_t)t * E + e] : 0.0;
-    if (ok && sel_bias) s += (double)sel_bias[(int64_t)t * E + e];
-    const double bnd = ok ? cB * sqrt(nxt * nw[e]) * (1.0 + 1e-12) + 1e-30 + fabs(s) * 1e-15 : 0.0;
+    double s = (double)la[(int64_t)t * E + ec];
+    if (sel_bias) s += (double)sel_bias[(int64_t)t * E + ec];
+    const double bnd = cB * (rxt * rw[ec]) * (1.0 + 1e-12) + 1e-30 + fabs(s) * 1e-15;
     if (ok && !(fabs(s) <= 1e300 && bnd <= 1e300)) bad = true;
     const uint64_t lk = ok ? dkey(s - bnd) + 1ull : 0ull;
     lhi[i] = (uint32_t)(lk >> 32);
@@ -515,35 +593,86 @@ __global__ void __launch_bounds__(256) route_refine_kernel(const float* __restri
 #pragma unroll
     for (int i = 0; i < PER; ++i) cand[i] = __ballot(lane + 64 * i < E && dkey(ub[i]) + 1ull >= kth);
   }
-  // exact logits of the candidates; everything else cannot win
+  // exact logits of the candidates (lowest id first); everything else cannot
+  // win.  Sixteen independent fp64 chains per lane (piece parity x element
+  // slot), folded in a fixed order, then the wave's fixed tree.
   double lv[PER], sv[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) { lv[i] = -__builtin_inf(); sv[i] = -__builtin_inf(); }
-  const uint16_t* xr = x + (int64_t)t * H;
+  auto next_cand = [&]() -> int {  // lowest remaining candidate, removed; -1 when none
+    int e = -1;
 #pragma unroll
-  for (int iw = 0; iw < PER; ++iw) {
-    uint64_t m = cand[iw];
-    while (m) {
-      const int lw = __builtin_ctzll(m);
-      m &= m - 1;
-      const int e = lw + 64 * iw;
-      const uint16_t* wrow = wr + (int64_t)e * H;
-      double acc = 0.0;
-      for (int h = 8 * lane; h < H; h += 512) {
-        double xv[8], wv8[8];
-        load8_f64<FT_BF16>(xr, h, xv);
-        load8_f64<FT_BF16>(wrow, h, wv8);
+    for (int i = 0; i < PER; ++i)
+      if (e < 0 && cand[i] != 0ull) {
+        e = 64 * i + __builtin_ctzll(cand[i]);
+        cand[i] &= cand[i] - 1;
+      }
+    return e;
+  };
+  auto dot = [](const uint4 (&a)[RF_Q], const uint4 (&b)[RF_Q], double (&acc)[16]) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc = fma(xv[j], wv8[j], acc);
+    for (int q = 0; q < RF_Q; ++q) {
+      const uint32_t xa[4] = {a[q].x, a[q].y, a[q].z, a[q].w};
+      const uint32_t wa[4] = {b[q].x, b[q].y, b[q].z, b[q].w};
+      const int c = 8 * (q & 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[c + j] = fma((double)bf16_lo(xa[j]), (double)bf16_lo(wa[j]), acc[c + j]);
+        acc[c + 4 + j] = fma((double)bf16_hi(xa[j]), (double)bf16_hi(wa[j]), acc[c + 4 + j]);
       }
-      const double l = wave_sum(acc);
-      if (lane == lw) {
-        lv[iw] = l;
-        sv[iw] = sel_bias ? l + (double)sel_bias[(int64_t)t * E + e] : l;
+    }
+  };
+  auto record = [&](int e, const double (&acc)[16]) {
+    double f[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) f[c] = acc[c] + acc[c + 8];
+    const double l = tk_wave_sum_f64(((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7])));
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (e == lane + 64 * i) {
+        lv[i] = l;
+        sv[i] = sel_bias ? l + (double)sel_bias[(int64_t)t * E + e] : l;
       }
+  };
+  if (!LONG) {
+    for (int e = next_cand(); e >= 0; e = next_cand()) {
+      double acc[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[c] = 0.0;
+      load_row(wr + (int64_t)e * H + 8 * lane, 0, wq);
+      // keep the x row packed: converting it once outside this loop would
+      // take 128 more registers per lane
+#pragma unroll
+      for (int q = 0; q < RF_Q; ++q) asm volatile("" : "+v"(xq[q].x), "+v"(xq[q].y), "+v"(xq[q].z), "+v"(xq[q].w));
+      dot(xq, wq, acc);
+      record(e, acc);
+    }
+  } else {
+    for (int e = next_cand(); e >= 0; e = next_cand()) {
+      const uint16_t* wrow = wr + (int64_t)e * H + 8 * lane;
+      double acc[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[c] = 0.0;
+      for (int q0 = 0; 512 * q0 < H; q0 += RF_Q) {
+        load_row(xr, q0, xq);
+        load_row(wrow, q0, wq);
+        dot(xq, wq, acc);
+      }
+      record(e, acc);
     }
   }
   topk_core<PER>(lv, sv, sel_bias != nullptr, E, k, 1, ids + (int64_t)t * k, gates + (int64_t)t * k);
+}
+
+template <bool LONG>
+static void launch_refine(int nb, hipStream_t st, const float* la, const double* rw, const uint16_t* x,
+                          const uint16_t* wr, const float* sel_bias, int32_t* ids, float* gates, int T, int H, int E,
+                          int k) {
+  if (E <= 64) route_refine_kernel<1, LONG><<<nb, 256, 0, st>>>(la, rw, x, wr, sel_bias, ids, gates, T, H, E, k);
+  else if (E <= 128) route_refine_kernel<2, LONG><<<nb, 256, 0, st>>>(la, rw, x, wr, sel_bias, ids, gates, T, H, E, k);
+  else if (E <= 256) route_refine_kernel<4, LONG><<<nb, 256, 0, st>>>(la, rw, x, wr, sel_bias, ids, gates, T, H, E, k);
+  else if (E <= 512) route_refine_kernel<8, LONG><<<nb, 256, 0, st>>>(la, rw, x, wr, sel_bias, ids, gates, T, H, E, k);
+  else route_refine_kernel<16, LONG><<<nb, 256, 0, st>>>(la, rw, x, wr, sel_bias, ids, gates, T, H, E, k);
 }
 
 hipError_t launch_route(const ft_moe_desc& d, const void* x, int T, const void* wr,
@@ -552,22 +681,18 @@ hipError_t launch_route(const ft_moe_desc& d, const void* x, int T, const void* 
   dim3 grid((T + RL_TT - 1) / RL_TT, (d.n_experts + RL_TE - 1) / RL_TE);
   const int xd = d.act_dtype, wd = d.router_dtype, H = d.hidden, E = d.n_experts;
   if (xd == FT_BF16 && wd == FT_BF16 && !want_logits && d.renormalize && H % RA_K == 0 && E <= 1024) {
-    // bounded path; the logits buffer [T, E] fp64 holds L~ [T, E] fp32, then |x|^2, |w|^2
+    // bounded path; the logits buffer [T, E] fp64 holds L~ [T, E] fp32, then |w| [E] fp64
     float* la = reinterpret_cast<float*>(logits);
-    double* nx = reinterpret_cast<double*>(la + (((int64_t)T * E + 63) / 64) * 64);
-    double* nw = nx + ((T + 31) / 32) * 32;
-    route_approx_kernel<<<dim3((T + RA_T - 1) / RA_T, (E + RA_E - 1) / RA_E), 256, 0, st>>>(
-        reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(wr), la, nx, nw, T, H, E);
+    double* rw = reinterpret_cast<double*>(la + (((int64_t)T * E + 63) / 64) * 64);
+    route_approx_kernel<<<dim3((T + RA_T - 1) / RA_T, (E + RA_E - 1) / RA_E), 512, 0, st>>>(
+        reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(wr), la, rw, T, H, E);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int nb = (T + 3) / 4, k = d.top_k;
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
     const uint16_t* wb = reinterpret_cast<const uint16_t*>(wr);
-    if (E <= 64) route_refine_kernel<1><<<nb, 256, 0, st>>>(la, nx, nw, xb, wb, sel_bias, ids, gates, T, H, E, k);
-    else if (E <= 128) route_refine_kernel<2><<<nb, 256, 0, st>>>(la, nx, nw, xb, wb, sel_bias, ids, gates, T, H, E, k);
-    else if (E <= 256) route_refine_kernel<4><<<nb, 256, 0, st>>>(la, nx, nw, xb, wb, sel_bias, ids, gates, T, H, E, k);
-    else if (E <= 512) route_refine_kernel<8><<<nb, 256, 0, st>>>(la, nx, nw, xb, wb, sel_bias, ids, gates, T, H, E, k);
-    else route_refine_kernel<16><<<nb, 256, 0, st>>>(la, nx, nw, xb, wb, sel_bias, ids, gates, T, H, E, k);
+    if (H <= 512 * RF_Q) launch_refine<false>(nb, st, la, rw, xb, wb, sel_bias, ids, gates, T, H, E, k);
+    else launch_refine<true>(nb, st, la, rw, xb, wb, sel_bias, ids, gates, T, H, E, k);
     return hipGetLastError();
   }
   dim3 mgrid((T + RM_T - 1) / RM_T, (E + RM_E - 1) / RM_E);

@@ -46,6 +46,30 @@ __device__ __forceinline__ uint32_t tk_wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// one DPP step of a wave-wide fp64 sum: a + (a moved by the DPP control)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double tk_dpp_add_f64(double a) {
+  const uint64_t u = (uint64_t)__double_as_longlong(a);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xF, false);
+  return a + __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// wave-wide fp64 sum in a fixed order (quads, rows, then across rows; the
+// total lands in lane 63), returned as a uniform value
+__device__ __forceinline__ double tk_wave_sum_f64(double v) {
+  v = tk_dpp_add_f64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = tk_dpp_add_f64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = tk_dpp_add_f64<0x124, 0xF>(v);  // row_ror:4
+  v = tk_dpp_add_f64<0x128, 0xF>(v);  // row_ror:8
+  v = tk_dpp_add_f64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = tk_dpp_add_f64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 __device__ __forceinline__ double tk_readlane_f64(double v, int l) {
   const uint64_t u = (uint64_t)__double_as_longlong(v);
   const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);

@@ -85,6 +85,10 @@ size_t ft_record_bytes(int32_t hidden, int32_t inter, int32_t w_dtype);
  * topk_gates[t,j] = softmax of the selected l (renormalize=1) or the full
  * softmax probability (renormalize=0), computed in fp64, stored fp32.
  * logits (nullable): l as fp64 [T, E].
+ * With more than 16 tokens, bf16 x and W_r, renormalize = 1 and logits
+ * NULL, l is computed in fp64 only for the experts that a rounding bound on
+ * bf16 matrix-core scores cannot rule out; ids and gates are the same as
+ * above (the excluded experts provably score below the k-th).
  * workspace: ft_route_workspace_bytes(desc, T) bytes, 256-byte aligned
  * (holds the logits when `logits` is NULL; calls sharing it must not overlap).
  * Errors: FT_EINVAL on null x/w_router/outputs, n_tokens < 0, k > E,

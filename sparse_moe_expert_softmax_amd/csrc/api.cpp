@@ -97,7 +97,8 @@ size_t ft_record_bytes(int32_t hidden, int32_t inter, int32_t w_dtype) {
 size_t ft_route_workspace_bytes(const ft_moe_desc* desc, int32_t n_tokens) {
   if (!desc || n_tokens < 0) return 0;
   // fp64 logits [T, E]; also room for the bounded prefill path's fp32
-  // approximate logits [T, E] and fp64 squared norms [T] and [E]
+  // approximate logits [T, E] and its fp64 norm bounds (|w| [E], with room
+  // for [T] more)
   const size_t te = (size_t)n_tokens * desc->n_experts;
   const size_t a = sizeof(double) * te;
   const size_t b = sizeof(float) * (te + 64) + sizeof(double) * ((size_t)n_tokens + 32 + desc->n_experts);

@@ -140,9 +140,8 @@ __device__ __forceinline__ void load_raw(const WMat& w, int row, int c, int g, R
     r.q = *reinterpret_cast<const uint4*>(w.codes + ((int64_t)row * w.K + k0) / 2);
     if constexpr (WD == FT_MXFP4) {
       r.s = w.scales[(int64_t)row * (w.K / 32) + k0 / 32];
-    } else {  // two E4M3 block scales, blocks of 16
-      const uint8_t* sp = w.scales + (int64_t)row * (w.K / 16) + k0 / 16;
-      r.s = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+    } else {  // two E4M3 block scales, blocks of 16 (adjacent, 2-byte aligned: one 16-bit load)
+      r.s = *reinterpret_cast<const uint16_t*>(w.scales + (int64_t)row * (w.K / 16) + k0 / 16);
     }
   }
 }
@@ -466,7 +465,11 @@ __device__ __forceinline__ void dd_group_all(const int32_t* __restrict__ ids, co
   if (lane == 0) di->n_distinct = n;
 }
 
-template <int WD, int UNROLL>
+// PACK (T <= 8): the MFMA's 16 token columns carry h's hi terms in columns
+// 0 .. T-1 and its lo terms in columns T .. 2T-1, so one product per K slice
+// covers both (and every h load fills twice the lanes); the two column
+// groups are added once at the end.  Otherwise hi and lo take a product each.
+template <int WD, int UNROLL, bool PACK>
 __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
     const uint16_t* __restrict__ hbuf, const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P,
     int k, const void* __restrict__ pool, int64_t stride, const int32_t* __restrict__ slot_ids,
@@ -498,7 +501,9 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
       if (job < njobs) {
         const int d = half + 2 * (job / nchunk), c = job % nchunk;
         const int slot = di.slot[d];
-        const int p = (col < T) ? di.pair[d][col] : -1;
+        // this lane's B column: token col (hi), or token col - T (lo) when packed
+        const int tk = (PACK && col >= T) ? col - T : col;
+        const int p = (tk < T && col < (PACK ? 2 * T : T)) ? di.pair[d][tk] : -1;
         if (slot < 0) {
           poisoned = true;
         } else {
@@ -507,12 +512,12 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
           ts[u] = Dm.tscale;
           load_raw<WD>(Dm, row, c, g, rw[u]);
         }
-        const uint16_t* hh = hbuf + (int64_t)(p < 0 ? 0 : p) * 2 * I;
+        const uint16_t* hh = hbuf + (int64_t)(p < 0 ? 0 : p) * 2 * I + ((PACK && col >= T) ? I : 0);
 #pragma unroll
         for (int jj = 0; jj < NM; ++jj) {
           const int ko = kofs<WD>(c, jj, g);
           bh[u][jj] = p >= 0 ? *reinterpret_cast<const uint4*>(hh + ko) : make_uint4(0, 0, 0, 0);
-          bl[u][jj] = p >= 0 ? *reinterpret_cast<const uint4*>(hh + I + ko) : make_uint4(0, 0, 0, 0);
+          if constexpr (!PACK) bl[u][jj] = p >= 0 ? *reinterpret_cast<const uint4*>(hh + I + ko) : make_uint4(0, 0, 0, 0);
         }
       }
     }
@@ -524,7 +529,7 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
         for (int jj = 0; jj < NM; ++jj) {
           const bf16x8_t a = decode_a<WD>(rw[u], jj);
           part = mfma(a, as_bf16x8(bh[u][jj]), part);
-          part = mfma(a, as_bf16x8(bl[u][jj]), part);
+          if constexpr (!PACK) part = mfma(a, as_bf16x8(bl[u][jj]), part);
         }
         if constexpr (WD == FT_NVFP4) acc += part * ts[u];
         else acc += part;
@@ -534,15 +539,22 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
   if (poisoned) acc = acc * __builtin_nanf("");
   red[wv][lane] = acc;
   __syncthreads();
-  if (wv == 0 && col < T) {
+  if (wv == 0) {
     f32x4_t s = red[0][lane];
 #pragma unroll
     for (int w = 1; w < DD_WAVES; ++w) s += red[w][lane];
-    // exactly two addends land on each zeroed output element, and
-    // (0 + a) + b == (0 + b) + a in IEEE arithmetic: the sum is deterministic
-    float* o = out + (int64_t)col * H + rt * 16 + 4 * g;
+    if constexpr (PACK) {  // add the lo column group (col + T of the same 16-lane row group)
+      const int src = (lane & ~15) | ((col + T) & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) unsafeAtomicAdd(o + i, s[i]);
+      for (int i = 0; i < 4; ++i) s[i] += __shfl(s[i], src, 64);
+    }
+    if (col < T) {
+      // exactly two addends land on each zeroed output element, and
+      // (0 + a) + b == (0 + b) + a in IEEE arithmetic: the sum is deterministic
+      float* o = out + (int64_t)col * H + rt * 16 + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) unsafeAtomicAdd(o + i, s[i]);
+    }
   }
 }
 
@@ -586,8 +598,13 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int32_t* ids_down = route.logits ? route.ids_out : ids;  // the selection the gate/up kernel stored
-  dec_down_kernel<WD, (WD == FT_BF16) ? 3 : 2><<<(H / 16) * 2, DD_THREADS, 0, st>>>(hbuf, ids_down, mask, pl.P, k, pool, d.expert_stride, slot_ids,
-                                                        out, pl.T, H, I, E);
+  constexpr int DU = (WD == FT_BF16) ? 3 : 2;
+  if (pl.T <= 8)
+    dec_down_kernel<WD, DU, true><<<(H / 16) * 2, DD_THREADS, 0, st>>>(hbuf, ids_down, mask, pl.P, k, pool,
+                                                                        d.expert_stride, slot_ids, out, pl.T, H, I, E);
+  else
+    dec_down_kernel<WD, DU, false><<<(H / 16) * 2, DD_THREADS, 0, st>>>(hbuf, ids_down, mask, pl.P, k, pool,
+                                                                         d.expert_stride, slot_ids, out, pl.T, H, I, E);
   return hipGetLastError();
 }
 

@@ -132,12 +132,14 @@ def test_forward_mxfp4_decode():
         run_layer(cfg, 5, 3, b)
 
 
-@pytest.mark.parametrize("cfg,T", [(C3, 8), (C5, 6), (C5, 1)])
+@pytest.mark.parametrize("cfg,T", [(C3, 8), (C5, 6), (C5, 1), (C3, 10)])
 def test_forward_fp4_decode_both_gate_up_paths(cfg, T):
     """fp4 gate/up has two loops: activations staged in LDS with block scales
     loaded four chunks at a time (when the token group's rows fit in 56 KB),
     and the per-chunk register loop otherwise. H4096 at 8 tokens and H6144
-    at 6 tokens take the second; one token takes the first."""
+    at 6 tokens take the second; one token takes the first.  The down
+    projection packs h's hi and lo terms into one product up to 8 tokens and
+    takes a product each above (10 tokens x top-6 = 60 pairs)."""
     print(f"fp4 decode {cfg.name} T={T}", flush=True)
     run_layer(cfg, 2, 4, T)
 

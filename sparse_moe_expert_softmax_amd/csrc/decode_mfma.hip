@@ -428,6 +428,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
 constexpr int DD_WAVES = 16;
 constexpr int DD_THREADS = DD_WAVES * 64;
 constexpr int DD_MAXT = 16;  // token columns of the accumulator
+constexpr int DD_MAX_GRID = 256;  // down-projection workgroups at most (one per CU)
 
 struct DownInfo {
   int n_distinct;
@@ -477,84 +478,89 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
   __shared__ DownInfo di;
   __shared__ f32x4_t red[DD_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
-  // two workgroups per 16-row tile: half s takes the distinct experts d = s, s+2, ...
-  const int rt = blockIdx.x >> 1, half = blockIdx.x & 1;
   if (wv == 0) dd_group_all(ids, mask, slot_ids, P, k, E, &di);
   __syncthreads();
   const int nd = di.n_distinct;
-  const int ndh = (nd - half + 1) / 2;  // experts of this half
-  const int row = rt * 16 + col;
   constexpr int CK = Chunk<WD>::K, NM = Chunk<WD>::NM;
   const int nchunk = I / CK;
-  const int njobs = ndh * nchunk;
   const RecordLayout L = record_layout(H, I, WD);
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  bool poisoned = false;
-  for (int j0 = wv; j0 < njobs; j0 += DD_WAVES * UNROLL) {
-    RawW<WD> rw[UNROLL];
-    uint4 bh[UNROLL][NM], bl[UNROLL][NM];
-    float ts[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int job = j0 + u * DD_WAVES;
-      ts[u] = 0.f;
-      if (job < njobs) {
-        const int d = half + 2 * (job / nchunk), c = job % nchunk;
-        const int slot = di.slot[d];
-        // this lane's B column: token col (hi), or token col - T (lo) when packed
-        const int tk = (PACK && col >= T) ? col - T : col;
-        const int p = (tk < T && col < (PACK ? 2 * T : T)) ? di.pair[d][tk] : -1;
-        if (slot < 0) {
-          poisoned = true;
-        } else {
-          const uint8_t* rec = reinterpret_cast<const uint8_t*>(pool) + (int64_t)slot * stride;
-          const WMat Dm = wmat<WD>(rec, L, 2, I);
-          ts[u] = Dm.tscale;
-          load_raw<WD>(Dm, row, c, g, rw[u]);
+  // work items: (16-row tile rt, half) with half s taking the distinct experts
+  // d = s, s+2, ...; a workgroup takes items blockIdx.x, + gridDim.x, ... (the
+  // grid is capped, so the grouping above is done once per workgroup)
+  for (int item = blockIdx.x; item < (H / 16) * 2; item += gridDim.x) {
+    const int rt = item >> 1, half = item & 1;
+    const int ndh = (nd - half + 1) / 2;  // experts of this half
+    const int row = rt * 16 + col;
+    const int njobs = ndh * nchunk;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    bool poisoned = false;
+    for (int j0 = wv; j0 < njobs; j0 += DD_WAVES * UNROLL) {
+      RawW<WD> rw[UNROLL];
+      uint4 bh[UNROLL][NM], bl[UNROLL][NM];
+      float ts[UNROLL];
+  #pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int job = j0 + u * DD_WAVES;
+        ts[u] = 0.f;
+        if (job < njobs) {
+          const int d = half + 2 * (job / nchunk), c = job % nchunk;
+          const int slot = di.slot[d];
+          // this lane's B column: token col (hi), or token col - T (lo) when packed
+          const int tk = (PACK && col >= T) ? col - T : col;
+          const int p = (tk < T && col < (PACK ? 2 * T : T)) ? di.pair[d][tk] : -1;
+          if (slot < 0) {
+            poisoned = true;
+          } else {
+            const uint8_t* rec = reinterpret_cast<const uint8_t*>(pool) + (int64_t)slot * stride;
+            const WMat Dm = wmat<WD>(rec, L, 2, I);
+            ts[u] = Dm.tscale;
+            load_raw<WD>(Dm, row, c, g, rw[u]);
+          }
+          const uint16_t* hh = hbuf + (int64_t)(p < 0 ? 0 : p) * 2 * I + ((PACK && col >= T) ? I : 0);
+  #pragma unroll
+          for (int jj = 0; jj < NM; ++jj) {
+            const int ko = kofs<WD>(c, jj, g);
+            bh[u][jj] = p >= 0 ? *reinterpret_cast<const uint4*>(hh + ko) : make_uint4(0, 0, 0, 0);
+            if constexpr (!PACK) bl[u][jj] = p >= 0 ? *reinterpret_cast<const uint4*>(hh + I + ko) : make_uint4(0, 0, 0, 0);
+          }
         }
-        const uint16_t* hh = hbuf + (int64_t)(p < 0 ? 0 : p) * 2 * I + ((PACK && col >= T) ? I : 0);
-#pragma unroll
-        for (int jj = 0; jj < NM; ++jj) {
-          const int ko = kofs<WD>(c, jj, g);
-          bh[u][jj] = p >= 0 ? *reinterpret_cast<const uint4*>(hh + ko) : make_uint4(0, 0, 0, 0);
-          if constexpr (!PACK) bl[u][jj] = p >= 0 ? *reinterpret_cast<const uint4*>(hh + I + ko) : make_uint4(0, 0, 0, 0);
+      }
+  #pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        if (ts[u] != 0.f) {
+          f32x4_t part = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int jj = 0; jj < NM; ++jj) {
+            const bf16x8_t a = decode_a<WD>(rw[u], jj);
+            part = mfma(a, as_bf16x8(bh[u][jj]), part);
+            if constexpr (!PACK) part = mfma(a, as_bf16x8(bl[u][jj]), part);
+          }
+          if constexpr (WD == FT_NVFP4) acc += part * ts[u];
+          else acc += part;
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      if (ts[u] != 0.f) {
-        f32x4_t part = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int jj = 0; jj < NM; ++jj) {
-          const bf16x8_t a = decode_a<WD>(rw[u], jj);
-          part = mfma(a, as_bf16x8(bh[u][jj]), part);
-          if constexpr (!PACK) part = mfma(a, as_bf16x8(bl[u][jj]), part);
-        }
-        if constexpr (WD == FT_NVFP4) acc += part * ts[u];
-        else acc += part;
+    if (poisoned) acc = acc * __builtin_nanf("");
+    red[wv][lane] = acc;
+    __syncthreads();
+    if (wv == 0) {
+      f32x4_t s = red[0][lane];
+  #pragma unroll
+      for (int w = 1; w < DD_WAVES; ++w) s += red[w][lane];
+      if constexpr (PACK) {  // add the lo column group (col + T of the same 16-lane row group)
+        const int src = (lane & ~15) | ((col + T) & 15);
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] += __shfl(s[i], src, 64);
+      }
+      if (col < T) {
+        // exactly two addends land on each zeroed output element, and
+        // (0 + a) + b == (0 + b) + a in IEEE arithmetic: the sum is deterministic
+        float* o = out + (int64_t)col * H + rt * 16 + 4 * g;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(o + i, s[i]);
       }
     }
-  }
-  if (poisoned) acc = acc * __builtin_nanf("");
-  red[wv][lane] = acc;
-  __syncthreads();
-  if (wv == 0) {
-    f32x4_t s = red[0][lane];
-#pragma unroll
-    for (int w = 1; w < DD_WAVES; ++w) s += red[w][lane];
-    if constexpr (PACK) {  // add the lo column group (col + T of the same 16-lane row group)
-      const int src = (lane & ~15) | ((col + T) & 15);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] += __shfl(s[i], src, 64);
-    }
-    if (col < T) {
-      // exactly two addends land on each zeroed output element, and
-      // (0 + a) + b == (0 + b) + a in IEEE arithmetic: the sum is deterministic
-      float* o = out + (int64_t)col * H + rt * 16 + 4 * g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) unsafeAtomicAdd(o + i, s[i]);
-    }
+    __syncthreads();  // red is reused by the next item
   }
 }
 
@@ -599,12 +605,15 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
   if (err != hipSuccess) return err;
   const int32_t* ids_down = route.logits ? route.ids_out : ids;  // the selection the gate/up kernel stored
   constexpr int DU = (WD == FT_BF16) ? 3 : 2;
+  // one workgroup of 16 waves per CU: cap the grid at the CU count and let
+  // each workgroup loop over its (tile, half) items
+  const unsigned dgrid = (H / 16) * 2 < DD_MAX_GRID ? (H / 16) * 2 : DD_MAX_GRID;
   if (pl.T <= 8)
-    dec_down_kernel<WD, DU, true><<<(H / 16) * 2, DD_THREADS, 0, st>>>(hbuf, ids_down, mask, pl.P, k, pool,
-                                                                        d.expert_stride, slot_ids, out, pl.T, H, I, E);
+    dec_down_kernel<WD, DU, true><<<dgrid, DD_THREADS, 0, st>>>(hbuf, ids_down, mask, pl.P, k, pool, d.expert_stride,
+                                                                 slot_ids, out, pl.T, H, I, E);
   else
-    dec_down_kernel<WD, DU, false><<<(H / 16) * 2, DD_THREADS, 0, st>>>(hbuf, ids_down, mask, pl.P, k, pool,
-                                                                         d.expert_stride, slot_ids, out, pl.T, H, I, E);
+    dec_down_kernel<WD, DU, false><<<dgrid, DD_THREADS, 0, st>>>(hbuf, ids_down, mask, pl.P, k, pool, d.expert_stride,
+                                                                  slot_ids, out, pl.T, H, I, E);
   return hipGetLastError();
 }
 

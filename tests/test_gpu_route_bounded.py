@@ -102,3 +102,10 @@ def test_bounded_router_with_selection_bias():
     T = 96
     bias = np.random.default_rng(21).normal(0.0, 0.05, (T, cfg.n_experts))
     check(LayerData(cfg, 1, 3, T), bias=bias)
+
+
+def test_bounded_router_full_prefill_chunk():
+    """The 8,192-token prefill chunk the benchmark routes (no logits output):
+    every token's ids against the oracle and the fp64 path."""
+    print("bounded route prefill chunk T=8192", flush=True)
+    check(LayerData(C4, 0, 0, 8192))

@@ -92,6 +92,7 @@ __global__ void __launch_bounds__(SLOT_THREADS) slot_lookup_kernel(
   __shared__ int32_t n_u, n_hit, n_mis;
   __shared__ uint64_t wave_best[SLOT_THREADS / 64];
   __shared__ int32_t victims[SLOT_THREADS];
+  __shared__ int32_t vold[SLOT_THREADS];         // key held by each victim before this call
 
   TableView tv = table_view(table);
   const int tid = threadIdx.x;
@@ -111,19 +112,30 @@ __global__ void __launch_bounds__(SLOT_THREADS) slot_lookup_kernel(
     if (e >= 0 && e < E) present[e] = 1;
   }
   __syncthreads();
-  // distinct ids in ascending order (serial compaction by one wave is plenty
-  // for E <= 4096; done by thread 0 to keep the order trivially right)
-  if (tid == 0) {
+  // current slot of every selected expert (-1: absent), fetched in parallel
+  // so that the serial steps below read only LDS
+  for (int e = tid; e < E; e += SLOT_THREADS)
+    if (present[e]) uslot[e] = ks_layer[e];
+  __syncthreads();
+  // distinct ids in ascending order: wave 0 compacts 64 experts per step
+  // (a ballot of the present flags, each lane's place from the set bits below it)
+  if (tid < 64) {
     int n = 0, h = 0;
-    for (int e = 0; e < E; ++e) {
-      if (present[e]) {
-        ulist[n++] = e;
-        if (ks_layer[e] >= 0) ++h;
-      }
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + tid, ec = e < E ? e : E - 1;  // lanes past E read a valid entry and drop it
+      const bool pr = e < E && present[ec];
+      const bool hit = pr && uslot[ec] >= 0;
+      const uint64_t m = __ballot(pr);
+      const uint64_t below = (tid == 0) ? 0ull : (~0ull >> (64 - tid));
+      if (pr) ulist[n + __popcll(m & below)] = e;
+      n += __popcll(m);
+      h += __popcll(__ballot(hit));
     }
-    n_u = n;
-    n_hit = h;
-    n_mis = n - h;
+    if (tid == 0) {
+      n_u = n;
+      n_hit = h;
+      n_mis = n - h;
+    }
   }
   __syncthreads();
   const int nu = n_u, nm = n_mis, nh = n_hit;
@@ -137,9 +149,8 @@ __global__ void __launch_bounds__(SLOT_THREADS) slot_lookup_kernel(
   __syncthreads();
   // stamp hits (in the LDS copy and in the table)
   for (int i = tid; i < nu; i += SLOT_THREADS) {
-    const int e = ulist[i];
-    const int s = ks_layer[e];
-    if (s >= 0) { tv.last_use[s] = tick; lu_s[s] = tick; uslot[e] = s; }
+    const int s = uslot[ulist[i]];
+    if (s >= 0) { tv.last_use[s] = tick; lu_s[s] = tick; }
   }
   __syncthreads();
   // pick nm victims, smallest (last_use, slot) among slots with last_use < tick
@@ -160,24 +171,34 @@ __global__ void __launch_bounds__(SLOT_THREADS) slot_lookup_kernel(
     }
     if (lane == 0) wave_best[wv] = best;
     __syncthreads();
-    if (tid == 0) {
-      uint64_t b = ~0ull;
-      for (int w = 0; w < SLOT_THREADS / 64; ++w) b = wave_best[w] < b ? wave_best[w] : b;
-      const int s = (int)(uint32_t)(b & 0xFFFFFFFFu);
-      victims[r] = s;
-      lu_s[s] = tick;  // now stamped by this call
+    if (tid < 64) {  // the minimum of the wave minima, in wave 0
+      uint64_t b = (tid < SLOT_THREADS / 64) ? wave_best[tid] : ~0ull;
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) {
+        const uint64_t ob = __shfl_xor(b, o, 64);
+        b = ob < b ? ob : b;
+      }
+      if (tid == 0) {
+        const int s = (int)(uint32_t)(b & 0xFFFFFFFFu);
+        victims[r] = s;
+        lu_s[s] = tick;  // now stamped by this call
+      }
     }
     __syncthreads();
   }
-  // assign misses (ascending id) to victims in order; sequential by thread 0
-  // because an eviction may clear a key of this same layer
+  // the victims' current keys, fetched in parallel.  A victim was not
+  // stamped by this call, so its key is none of this call's ids: the
+  // evictions below cannot touch a key that this call reads.
+  for (int r = tid; r < nm; r += SLOT_THREADS) vold[r] = tv.slot_key[victims[r]];
+  __syncthreads();
+  // assign misses (ascending id) to victims in order (thread 0; LDS reads only)
   if (tid == 0) {
     int r = 0;
     for (int i = 0; i < nu; ++i) {
       const int e = ulist[i];
-      if (ks_layer[e] >= 0) continue;
+      if (uslot[e] >= 0) continue;
       const int s = victims[r];
-      const int old = tv.slot_key[s];
+      const int old = vold[r];
       if (old >= 0) tv.key_slot[old] = -1;
       tv.slot_key[s] = layer * E + e;
       tv.key_slot[(int64_t)layer * E + e] = s;

@@ -498,7 +498,7 @@ __global__ void __launch_bounds__(512) route_approx_kernel(const uint16_t* __res
     }
   }
   // the K half 1 waves hand their partial sums over through LDS
-  float* red = reinterpret_cast<float*>(&ws[0][0]);  // [4 wt][8 b][4 i][64 lanes], then nx [4 wt][64]
+  float* red = reinterpret_cast<float*>(&ws[0][0]);  // [4 wt][8 b][4 i][64 lanes]
   if (kh == 1) {
 #pragma unroll
     for (int b = 0; b < 8; ++b)

@@ -69,10 +69,18 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(
   // per-expert totals and this block's prefix over earlier blocks (E <= 1024)
   int total = 0, before = 0;
   if (tid < E) {
-    for (int bb = 0; bb < nb; ++bb) {
-      const int c = block_hist[(int64_t)bb * E + tid];
-      total += c;
-      if (bb < b) before += c;
+    // sixteen rows in flight at a time (clamped rows, dropped after the load)
+    for (int bb0 = 0; bb0 < nb; bb0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = block_hist[(int64_t)min(bb0 + u, nb - 1) * E + tid];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int bb = bb0 + u;
+        const int cv = bb < nb ? c[u] : 0;
+        total += cv;
+        before += bb < b ? cv : 0;
+      }
     }
   }
   for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;

@@ -256,16 +256,30 @@ __global__ void __launch_bounds__(256) combine_bf16_kernel(const uint16_t* __res
   const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (t >= T || h >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int p = pos[(int64_t)t * k + j];
-    if (p < 0) continue;
-    const float g = gates[(int64_t)t * k + j];
-    const uint4 y = *reinterpret_cast<const uint4*>(ybuf + (int64_t)p * H + h);
-    const uint32_t w[4] = {y.x, y.y, y.z, y.w};
+  // up to eight pairs at a time with all their loads in flight (positions and
+  // gates first, then the y rows; a masked-out pair reads row 0 and adds 0),
+  // summed in rank order
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int pj[8];
+    float gj[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = fmaf(g, bf16_lo(w[q]), acc[2 * q]);
-      acc[2 * q + 1] = fmaf(g, bf16_hi(w[q]), acc[2 * q + 1]);
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, k - 1);
+      pj[u] = pos[(int64_t)t * k + j];
+      gj[u] = gates[(int64_t)t * k + j];
+    }
+    uint4 yj[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) yj[u] = *reinterpret_cast<const uint4*>(ybuf + (int64_t)max(pj[u], 0) * H + h);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u >= k || pj[u] < 0) continue;
+      const uint32_t w[4] = {yj[u].x, yj[u].y, yj[u].z, yj[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(gj[u], bf16_lo(w[q]), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(gj[u], bf16_hi(w[q]), acc[2 * q + 1]);
+      }
     }
   }
   float4* o = reinterpret_cast<float4*>(out + (int64_t)t * H + h);

@@ -145,7 +145,20 @@ __global__ void __launch_bounds__(SLOT_THREADS) slot_lookup_kernel(
     return;
   }
   const uint32_t tick = *tv.tick + 1u;
-  for (int s = tid; s < S; s += SLOT_THREADS) lu_s[s] = tv.last_use[s];
+  // last_use into LDS, all passes' loads in flight together (S <= 8 passes)
+  {
+    uint32_t v[SLOT_MAX_S / SLOT_THREADS];
+#pragma unroll
+    for (int u = 0; u < SLOT_MAX_S / SLOT_THREADS; ++u) {
+      const int s = tid + u * SLOT_THREADS;
+      v[u] = tv.last_use[s < S ? s : S - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < SLOT_MAX_S / SLOT_THREADS; ++u) {
+      const int s = tid + u * SLOT_THREADS;
+      if (s < S) lu_s[s] = v[u];
+    }
+  }
   __syncthreads();
   // stamp hits (in the LDS copy and in the table)
   for (int i = tid; i < nu; i += SLOT_THREADS) {

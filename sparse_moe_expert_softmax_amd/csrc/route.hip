@@ -80,16 +80,48 @@ __global__ void __launch_bounds__(256) route_decode_kernel(const void* __restric
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = 0.0;
   const int hq = H / 4;  // this wave's quarter of H (H % 32 == 0)
-  for (int h = wv * hq + lane * 8; h < (wv + 1) * hq; h += 64 * 8) {
-    double w[8];
-    load8_f64<WDT>(wr, (int64_t)e * H + h, w);
+  if (XDT == FT_BF16 && WDT == FT_BF16 && NT <= 4 && hq <= 4 * 512) {
+    // bf16, few tokens, H <= 8192: the loads of every pass are issued before
+    // any is used (passes past the quarter read its first element and are
+    // skipped); same products in the same order as the loop below
+    const int h0 = wv * hq + lane * 8, hend = (wv + 1) * hq;
+    const uint16_t* wb = reinterpret_cast<const uint16_t*>(wr) + (int64_t)e * H;
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+    uint4 wq[4], xq[4][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t < T) {
-        double xv[8];
-        load8_f64<XDT>(x, (int64_t)t * H + h, xv);
+    for (int it = 0; it < 4; ++it) {
+      const int h = h0 + 512 * it, hc = h < hend ? h : wv * hq;
+      wq[it] = *reinterpret_cast<const uint4*>(wb + hc);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[t] = fma(xv[j], w[j], acc[t]);
+      for (int t = 0; t < NT; ++t) xq[it][t] = *reinterpret_cast<const uint4*>(xb + (int64_t)(t < T ? t : 0) * H + hc);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      if (h0 + 512 * it >= hend) continue;
+      const uint32_t ww[4] = {wq[it].x, wq[it].y, wq[it].z, wq[it].w};
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t >= T) continue;
+        const uint32_t xx[4] = {xq[it][t].x, xq[it][t].y, xq[it][t].z, xq[it][t].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[t] = fma((double)bf16_lo(xx[j]), (double)bf16_lo(ww[j]), acc[t]);
+          acc[t] = fma((double)bf16_hi(xx[j]), (double)bf16_hi(ww[j]), acc[t]);
+        }
+      }
+    }
+  } else {
+    for (int h = wv * hq + lane * 8; h < (wv + 1) * hq; h += 64 * 8) {
+      double w[8];
+      load8_f64<WDT>(wr, (int64_t)e * H + h, w);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t < T) {
+          double xv[8];
+          load8_f64<XDT>(x, (int64_t)t * H + h, xv);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[t] = fma(xv[j], w[j], acc[t]);
+        }
       }
     }
   }

@@ -178,13 +178,22 @@ __device__ void topk_one_token(const double* __restrict__ lt, const float* __res
                                int renormalize, int32_t* __restrict__ ids_t, float* __restrict__ gates_t) {
   const int lane = threadIdx.x & 63;
   double lv[PER], sv[PER];
+  // unconditional loads from clamped indices (lanes past E read expert E - 1
+  // and drop it), so all of them are in flight at once
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
-    const bool ok = e < E;
-    lv[i] = ok ? lt[e] : 0.0;
+    const double l = lt[e < E ? e : E - 1];
+    lv[i] = e < E ? l : 0.0;
     sv[i] = lv[i];
-    if (ok && bias_t) sv[i] += (double)bias_t[e];
+  }
+  if (bias_t) {
+    float b[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) b[i] = bias_t[min(lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i < E) sv[i] += (double)b[i];
   }
   topk_core<PER>(lv, sv, bias_t != nullptr, E, k, renormalize, ids_t, gates_t);
 }

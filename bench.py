@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=8192, help="prefill: prompt tokens (multiples of 8192 run as chunks)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--host-layers", type=int, default=2, help="distinct pinned host layer images (aliased)")
+    ap.add_argument("--device-fetch", action="store_true",
+                    help="LRU decode: missed experts copied by ft_expert_fetch on the device (no host round trip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -565,6 +567,10 @@ def run_decode_lru(args, cfg, torch):
     misses, step_ms, fwd_ms, up_ev = [], [], [], []
     import time as _t
     xs = torch.randn((64, B, H), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    if args.device_fetch:  # the layer's host record addresses, on the device; miss counts stay there too
+        src_dev = [torch.tensor(host_ptr[h], dtype=torch.int64, device="cuda") for h in range(NH)]
+        nm_dev = torch.zeros(n_steps * L, dtype=torch.int32, device="cuda")
+        fetch_ev = []
     for s_ in range(n_steps):
         t_s = _t.perf_counter()
         for l in range(L):
@@ -573,6 +579,22 @@ def run_decode_lru(args, cfg, torch):
             bias.scatter_(1, trace_dev[s_, l], 30.0)
             ftmoe.ft_moe_route(desc, x, routers[l], ids, gates, sel_bias=bias, workspace=rws, stream=comp)
             ftmoe.ft_slot_lookup(table, l, ids, slots, flags, mlist[1:], mlist[:1], stream=comp)
+            if args.device_fetch:
+                a, b = EV(), EV()
+                a.record(comp)
+                ftmoe.ft_expert_fetch(pool, stride, rec, E, S, src_dev[l % NH], mlist[1:], mlist[:1], B * k,
+                                      stream=comp)
+                b.record(comp)
+                nm_dev[s_ * L + l].copy_(mlist[0])
+                if s_ >= args.warmup:
+                    fetch_ev.append((a, b, s_ * L + l))
+                e0, e1 = EV(), EV()
+                e0.record(comp)
+                ftmoe.ft_moe_forward(desc, x, ids, gates, pool, out, ws, slot_ids=slots, stream=comp)
+                e1.record(comp)
+                if s_ >= args.warmup:
+                    fwd_ms.append((e0, e1))
+                continue
             h_mlist.copy_(mlist, non_blocking=True)
             comp.synchronize()
             nm = int(h_mlist[0])
@@ -600,6 +622,11 @@ def run_decode_lru(args, cfg, torch):
         if s_ >= args.warmup:
             step_ms.append((_t.perf_counter() - t_s) * 1e3)
     torch.cuda.synchronize()
+    if args.device_fetch:
+        misses = nm_dev.cpu().tolist()
+        if min(misses) < 0:
+            raise RuntimeError("slot pool exhausted")
+        up_ev = [(a, b, misses[i]) for a, b, i in fetch_ev]
     # kernel-level forward time without host gaps: replay recorded calls with the queue filled ahead
     rec_calls = []
     for s_ in range(max(args.warmup, n_steps - 4), n_steps):
@@ -636,7 +663,10 @@ def run_decode_lru(args, cfg, torch):
                        {"workload": cfg.name, "batch": B, "layers": L, "hidden": H, "experts": E, "top_k": k,
                         "inter": I, "weights": "mxfp4", "pool_slots": S, "pool_gb": round(S * stride / 1e9, 1),
                         "trace": f"zipf s={cfg.zipf_s}, {n_steps} steps, cold start", "host_layer_images": NH,
-                        "launch": "eager, host-synchronous per layer (miss list read back before uploads)"}, "bf16")
+                        "launch": ("eager, misses fetched on the device (ft_expert_fetch, no host round trip)"
+                                   if args.device_fetch else
+                                   "eager, host-synchronous per layer (miss list read back before uploads)")},
+                       "bf16")
     res["steps"] = n_steps - args.warmup
     res["lru"] = {"miss_rate_per_selected_expert": round(float(miss_arr[args.warmup:].sum() / distinct.sum()), 4),
                   "misses_per_layer_call": round(float(miss_arr[args.warmup:].mean()), 3),

@@ -134,6 +134,28 @@ int ft_expert_upload(void* pool_base, int64_t expert_stride, int64_t record_byte
                      const int32_t* slots, const void* const* host_src, int32_t n,
                      void* stream, void* done_event);
 
+/* ---------------------------------------------------- device-side fetch --
+ * The copy step after ft_slot_lookup without a host round trip: the pages
+ * keep the per-layer control inside one captured graph (FreeToken blog
+ * page, architecture section); here the miss list and its count never leave
+ * the device.  Copies, for i < *n_miss, the record of expert miss_list[2i]
+ * from host memory layer_src[e] to pool_base + miss_list[2i+1] *
+ * expert_stride.  A negative *n_miss (exhausted pool) copies nothing.
+ *  layer_src: device array [n_experts] of addresses of this layer's records
+ *    in pinned host memory (hipHostMalloc, torch pin_memory), which the GPU
+ *    reads directly over the host link; 16-byte aligned.  The caller
+ *    guarantees that every address is pinned host memory (pageable memory
+ *    cannot be read by the GPU).
+ *  miss_list, n_miss: device, as ft_slot_lookup wrote them.
+ *  max_miss: upper bound on *n_miss (the lookup's n_pairs); sizes the grid.
+ *  Entries with e outside [0, n_experts) or a slot outside [0, n_slots) are
+ *  skipped.  Asynchronous on `stream`, after the lookup on the same stream.
+ * Errors: FT_EINVAL on nulls, non-positive sizes, record_bytes or stride not
+ * a multiple of 16, misaligned pool.  max_miss = 0 is a no-op. */
+int ft_expert_fetch(void* pool_base, int64_t expert_stride, int64_t record_bytes, int32_t n_experts,
+                    int32_t n_slots, const uint64_t* layer_src, const int32_t* miss_list,
+                    const int32_t* n_miss, int32_t max_miss, void* stream);
+
 /* -------------------------------------------------------------- forward --
  * out[t,:] = sum_j [expert_mask has e_tj] * topk_gates[t,j] * y_tj with
  * y_tj = D (silu(G x_t) * (U x_t)) of expert e_tj, summed over j in order.

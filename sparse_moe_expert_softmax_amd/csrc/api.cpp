@@ -188,6 +188,24 @@ int ft_expert_upload(void* pool_base, int64_t expert_stride, int64_t record_byte
   return FT_OK;
 }
 
+int ft_expert_fetch(void* pool_base, int64_t expert_stride, int64_t record_bytes, int32_t n_experts,
+                    int32_t n_slots, const uint64_t* layer_src, const int32_t* miss_list, const int32_t* n_miss,
+                    int32_t max_miss, void* stream) {
+  if (max_miss < 0) return fail(FT_EINVAL, "max_miss < 0");
+  if (max_miss == 0) return FT_OK;
+  if (!pool_base || !layer_src || !miss_list || !n_miss) return fail(FT_EINVAL, "NULL argument to ft_expert_fetch");
+  if (n_experts <= 0 || n_slots <= 0) return fail(FT_EINVAL, "n_experts and n_slots must be positive");
+  if (record_bytes <= 0 || record_bytes % 16 || expert_stride < record_bytes || expert_stride % 16)
+    return fail(FT_EINVAL, "record_bytes and expert_stride must be positive multiples of 16, stride >= record");
+  if (!aligned(pool_base, 16)) return fail(FT_EINVAL, "pool_base must be 16-byte aligned");
+  if ((int64_t)max_miss * ((record_bytes + 65535) / 65536) > (int64_t)INT32_MAX)
+    return fail(FT_EINVAL, "max_miss too large");
+  hipError_t e = ft::launch_fetch(pool_base, expert_stride, record_bytes, n_experts, n_slots, layer_src, miss_list,
+                                  n_miss, max_miss, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ft_expert_fetch launch");
+  return FT_OK;
+}
+
 size_t ft_moe_workspace_bytes(const ft_moe_desc* desc, int32_t n_tokens) {
   if (check_desc(desc) || n_tokens < 0) return 0;
   return ft::plan_forward(*desc, n_tokens).bytes;

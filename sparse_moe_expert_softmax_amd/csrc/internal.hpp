@@ -26,6 +26,8 @@ hipError_t launch_slot_table_init(void* table, int L, int E, int S, hipStream_t 
 hipError_t launch_slot_lookup(void* table, int layer, const int32_t* ids, int n_pairs, int32_t* slot_ids,
                               uint8_t* miss_flags, int32_t* miss_list, int32_t* n_miss, hipStream_t st);
 int slot_max_slots();
+hipError_t launch_fetch(void* pool, int64_t stride, int64_t rec_bytes, int E, int S, const uint64_t* layer_src,
+                        const int32_t* miss_list, const int32_t* n_miss, int max_miss, hipStream_t st);
 int slot_max_experts();
 
 // forward paths

@@ -235,6 +235,55 @@ __global__ void __launch_bounds__(SLOT_THREADS) slot_lookup_kernel(
   }
 }
 
+// ------------------------------------------------------ device-side fetch --
+// The copy that follows a lookup, driven by the miss list the lookup wrote,
+// so no host round trip sits between the lookup and the forward.  Records
+// are read straight from pinned host memory (the GPU addresses it directly)
+// with 16-byte loads.  Workgroup b copies 64 KB chunk b % cpr of miss
+// b / cpr; workgroups past the reported count (or a negative count, from an
+// exhausted pool) copy nothing, and entries with an expert or slot out of
+// range are skipped.
+constexpr int FETCH_THREADS = 256;
+constexpr int64_t FETCH_CHUNK = 64 * 1024;
+
+__global__ void __launch_bounds__(FETCH_THREADS) fetch_kernel(uint8_t* __restrict__ pool, int64_t stride,
+                                                             int64_t rec_bytes, int E, int S,
+                                                             const uint64_t* __restrict__ layer_src,
+                                                             const int32_t* __restrict__ miss_list,
+                                                             const int32_t* __restrict__ n_miss, int cpr) {
+  const int m = blockIdx.x / cpr, c = blockIdx.x % cpr;
+  if (m >= *n_miss) return;  // also every workgroup when the count is negative
+  const int e = miss_list[2 * m], s = miss_list[2 * m + 1];
+  if (e < 0 || e >= E || s < 0 || s >= S) return;
+  const uint4* src = reinterpret_cast<const uint4*>(layer_src[e] + c * FETCH_CHUNK);
+  uint4* dst = reinterpret_cast<uint4*>(pool + (int64_t)s * stride + c * FETCH_CHUNK);
+  const int64_t rem = rec_bytes - c * FETCH_CHUNK;
+  const int n16 = (int)((rem < FETCH_CHUNK ? rem : FETCH_CHUNK) / 16);
+  // four 16-byte pieces per thread in flight, then their stores
+  for (int i0 = threadIdx.x; i0 < n16; i0 += 4 * FETCH_THREADS) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * FETCH_THREADS;
+      v[u] = src[i < n16 ? i : n16 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * FETCH_THREADS;
+      if (i < n16) dst[i] = v[u];
+    }
+  }
+}
+
+hipError_t launch_fetch(void* pool, int64_t stride, int64_t rec_bytes, int E, int S, const uint64_t* layer_src,
+                        const int32_t* miss_list, const int32_t* n_miss, int max_miss, hipStream_t st) {
+  const int cpr = (int)((rec_bytes + FETCH_CHUNK - 1) / FETCH_CHUNK);
+  fetch_kernel<<<(unsigned)(max_miss * cpr), FETCH_THREADS, 0, st>>>(reinterpret_cast<uint8_t*>(pool), stride,
+                                                                      rec_bytes, E, S, layer_src, miss_list, n_miss,
+                                                                      cpr);
+  return hipGetLastError();
+}
+
 hipError_t launch_slot_lookup(void* table, int layer, const int32_t* ids, int n_pairs, int32_t* slot_ids,
                               uint8_t* miss_flags, int32_t* miss_list, int32_t* n_miss, hipStream_t st) {
   slot_lookup_kernel<<<1, SLOT_THREADS, 0, st>>>(table, layer, ids, n_pairs, slot_ids, miss_flags, miss_list,

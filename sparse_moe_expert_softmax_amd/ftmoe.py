@@ -43,6 +43,7 @@ _SIGS = {
     "ft_slot_table_init": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp]),
     "ft_slot_lookup": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "ft_expert_upload": (ctypes.c_int, [_vp, _i64, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_vp), _i32, _vp, _vp]),
+    "ft_expert_fetch": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
     "ft_moe_workspace_bytes": (_sz, [ctypes.POINTER(Desc), _i32]),
     "ft_moe_forward": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ft_moe_route_forward_workspace_bytes": (_sz, [ctypes.POINTER(Desc), _i32]),
@@ -132,6 +133,14 @@ def ft_expert_upload(pool, expert_stride: int, record_bytes: int, slots, host_pt
             done_event.record(torch.cuda.current_stream() if stream is None else stream)
         ev = ctypes.c_void_p(done_event.cuda_event)
     _check(lib().ft_expert_upload(_ptr(pool), expert_stride, record_bytes, arr_s, arr_p, n, _stream(stream), ev))
+
+
+def ft_expert_fetch(pool, expert_stride: int, record_bytes: int, n_experts: int, n_slots: int, layer_src, miss_list,
+                    n_miss, max_miss: int, stream=None):
+    """layer_src: device int64 tensor [n_experts] of pinned host record addresses;
+    miss_list / n_miss: the device tensors ft_slot_lookup wrote."""
+    _check(lib().ft_expert_fetch(_ptr(pool), expert_stride, record_bytes, n_experts, n_slots, _ptr(layer_src),
+                                 _ptr(miss_list), _ptr(n_miss), max_miss, _stream(stream)))
 
 
 def ft_moe_workspace_bytes(desc: Desc, n_tokens: int) -> int:

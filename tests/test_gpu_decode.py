@@ -281,6 +281,55 @@ def test_upload_copies_records_and_rejects_pageable():
     assert ei.value.status == ftmoe.FT_EINVAL
 
 
+def test_fetch_copies_the_lookups_misses_on_the_device():
+    """ft_expert_fetch after ft_slot_lookup: the missed records land in their
+    slots byte for byte (records of 130,560 bytes: a full and a partial 64 KB
+    chunk), nothing else changes; an all-hit call and an exhausted pool
+    (count -1) copy nothing."""
+    from sparse_moe_expert_softmax_amd.configs import MXFP4
+    cfg = MoEConfig("fetch_mxfp4_h256_i320", 97, hidden=256, inter=320, n_experts=16, top_k=2, act_dtype=BF16,
+                    router_dtype=BF16, w_dtype=MXFP4, n_layers=1)
+    E, S = cfg.n_experts, 4
+    stride = synth.record_stride(cfg.hidden, cfg.inter, cfg.w_dtype)
+    rb = synth.record_bytes(cfg.hidden, cfg.inter, cfg.w_dtype)
+    recs = [synth.expert_record(cfg, 0, e) for e in range(E)]
+    host = [torch.from_numpy(r).pin_memory() for r in recs]
+    layer_src = torch.tensor([h.data_ptr() for h in host], dtype=torch.int64, device="cuda")
+    table = torch.zeros(ftmoe.ft_slot_table_bytes(1, E, S), dtype=torch.uint8, device="cuda")
+    ftmoe.ft_slot_table_init(table, 1, E, S)
+    pool = torch.full((S, stride), 0xA5, dtype=torch.uint8, device="cuda")
+    slots = torch.empty(8, dtype=torch.int32, device="cuda")
+    flags = torch.empty(8, dtype=torch.uint8, device="cuda")
+    mlist = torch.empty(17, dtype=torch.int32, device="cuda")  # [n_miss, (e, slot) ...]
+
+    def call(ids):
+        i = torch.tensor(ids, dtype=torch.int32, device="cuda")
+        ftmoe.ft_slot_lookup(table, 0, i, slots[:len(ids)], flags[:len(ids)], mlist[1:], mlist[:1])
+        ftmoe.ft_expert_fetch(pool, stride, rb, E, S, layer_src, mlist[1:], mlist[:1], max_miss=len(ids))
+        torch.cuda.synchronize()
+        return mlist.cpu().numpy()
+
+    m = call([3, 9, 3, 12])
+    assert m[0] == 3
+    got = pool.cpu().numpy()
+    filled = set()
+    for q in range(m[0]):
+        e, sl = int(m[1 + 2 * q]), int(m[2 + 2 * q])
+        assert np.array_equal(got[sl, :rb], recs[e][:rb]), (e, sl)
+        assert (got[sl, rb:] == 0xA5).all()  # the stride padding is not written
+        filled.add(sl)
+    for sl in set(range(S)) - filled:
+        assert (got[sl] == 0xA5).all()
+    before = pool.clone()
+    m = call([9, 12, 3, 3])  # all hits
+    assert m[0] == 0 and torch.equal(pool, before)
+    m = call([0, 1, 2, 4, 5])  # five misses, four slots: exhausted
+    assert m[0] == -1 and torch.equal(pool, before)
+    with pytest.raises(ftmoe.FtError) as ei:
+        ftmoe.ft_expert_fetch(pool, stride, rb + 8, E, S, layer_src, mlist[1:], mlist[:1], max_miss=4)
+    assert ei.value.status == ftmoe.FT_EINVAL
+
+
 @pytest.mark.parametrize("cfg,T", [(C2, 9), (C3, 11)])
 def test_forward_general_path_above_decode_pairs(cfg, T):
     """More than 64 (token, rank) pairs: the permute + grouped GEMV path."""

@@ -76,7 +76,9 @@ def test_fused_full_softmax_gates_and_oracle():
     assert max_rel_err(f_out.cpu().numpy(), ref) <= 1e-3
 
 
-@pytest.mark.parametrize("cfg,T", [(C1, 16), (SMALL, 300), (C2, 17)])
+@pytest.mark.parametrize("cfg,T", [(C1, 16), (SMALL, 300), (C2, 17), (C2, 12), (C5, 9)])
 def test_unfused_sizes_run_the_two_calls(cfg, T):
+    """fp32, many tokens, and decode-sized token counts whose T * k exceeds
+    the 64 pairs the fused kernels group (12 x top-8, 9 x top-8 NVFP4)."""
     print(f"route+forward {cfg.name} T={T}", flush=True)
     fused_vs_separate(cfg, T, 140 + T)

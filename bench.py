@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=8192, help="prefill: prompt tokens (multiples of 8192 run as chunks)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--host-layers", type=int, default=2, help="distinct pinned host layer images (aliased)")
+    ap.add_argument("--policy-study", action="store_true",
+                    help="LRU workload: miss rates of expert placement policies at equal capacity (slot table only)")
     ap.add_argument("--device-fetch", action="store_true",
                     help="LRU decode: missed experts copied by ft_expert_fetch on the device (no host round trip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -145,6 +147,8 @@ def main():
     torch.cuda.set_device(0)
     if cfg.name == "prefill_mxfp4_h4096_e256":
         return run_prefill(args, cfg, torch)
+    if args.policy_study:
+        return run_policy_study(args, cfg, torch)
     if cfg.name == "decode_mxfp4_h4096_e256_lru":
         return run_decode_lru(args, cfg, torch)
     if cfg.name == "decode_nvfp4_h6144_e256":
@@ -301,6 +305,96 @@ def _base_result(args, metric_value, unit, ms_per_step, config, dtype):
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
             "data": "synthetic", "config": config}
+
+
+def run_policy_study(args, cfg, torch):
+    """Expert placement at equal capacity (S slots for L layers x E experts),
+    on the Zipf trace and on a trace with temporal locality (each expert of a
+    token kept from one step to the next with probability 0.8):
+      - global LRU: one slot table for all layers (the library's);
+      - per-layer split: S / L slots per layer, LRU within each (the same
+        lookup kernel on one table per layer);
+      - profiled static set: the S most used (layer, expert) keys over the
+        first tenth of the steps stay resident, every other key is uploaded
+        each time it is selected.
+    Miss rates are counted over the steps after that first tenth, for every
+    policy; upload bytes and host-link time follow from the record size and
+    the link rate the LRU workload measures."""
+    from sparse_moe_expert_softmax_amd import ftmoe, synth
+    L, E, k = cfg.n_layers, cfg.n_experts, cfg.top_k
+    S = cfg.n_slots
+    n_steps = cfg.trace_steps
+    prof = n_steps // 10
+    rec = synth.record_bytes(cfg.hidden, cfg.inter, cfg.w_dtype)
+    link_gbs = 54.6  # measured: ft_expert_fetch from pinned host memory
+    t0 = time.perf_counter()
+    traces = {"zipf": synth.zipf_trace(cfg, n_steps=n_steps, n_tokens=4),
+              "sticky_p0.8": synth.sticky_trace(cfg, n_steps, 4, 0.8)}
+    study = {}
+    for tname, tr in traces.items():
+        for B in (1, 4):
+            ids_all = torch.from_numpy(tr[:, :, :B, :].reshape(n_steps, L, B * k).astype(np.int32)).cuda()
+            slots = torch.empty(B * k, dtype=torch.int32, device="cuda")
+            flags = torch.empty(B * k, dtype=torch.uint8, device="cuda")
+            mlist = torch.empty(2 * B * k + 1, dtype=torch.int32, device="cuda")
+            res = {}
+            for pol in ("global_lru", "per_layer_lru"):
+                if pol == "global_lru":
+                    tabs = [torch.zeros(ftmoe.ft_slot_table_bytes(L, E, S), dtype=torch.uint8, device="cuda")]
+                    ftmoe.ft_slot_table_init(tabs[0], L, E, S)
+                else:
+                    tabs = [torch.zeros(ftmoe.ft_slot_table_bytes(1, E, S // L), dtype=torch.uint8, device="cuda")
+                            for _ in range(L)]
+                    for t_ in tabs:
+                        ftmoe.ft_slot_table_init(t_, 1, E, S // L)
+                nm = torch.zeros((n_steps, L), dtype=torch.int32, device="cuda")
+                for s_ in range(n_steps):
+                    for l in range(L):
+                        if pol == "global_lru":
+                            ftmoe.ft_slot_lookup(tabs[0], l, ids_all[s_, l], slots, flags, mlist[1:], mlist[:1])
+                        else:
+                            ftmoe.ft_slot_lookup(tabs[l], 0, ids_all[s_, l], slots, flags, mlist[1:], mlist[:1])
+                        nm[s_, l].copy_(mlist[0])
+                res[pol] = nm.cpu().numpy()
+            # profiled static set: the S most frequent keys of the first tenth
+            ids_np = tr[:, :, :B, :].reshape(n_steps, L, B * k)
+            cnt = np.zeros((L, E), dtype=np.int64)
+            for s_ in range(prof):
+                for l in range(L):
+                    for e in np.unique(ids_np[s_, l]):
+                        cnt[l, e] += 1
+            order = np.argsort(-cnt.ravel(), kind="stable")[:S]
+            resident = np.zeros(L * E, dtype=bool)
+            resident[order] = True
+            st = np.zeros((n_steps, L), dtype=np.int64)
+            for s_ in range(n_steps):
+                for l in range(L):
+                    u = np.unique(ids_np[s_, l])
+                    st[s_, l] = int((~resident[l * E + u]).sum())
+            res["profiled_static"] = st
+            distinct = np.array([[len(np.unique(ids_np[s_, l])) for l in range(L)] for s_ in range(prof, n_steps)])
+            entry = {}
+            for pol, m in res.items():
+                if (m < 0).any():
+                    raise RuntimeError(f"{pol}: slot pool exhausted")
+                mm = m[prof:]
+                gb = float(mm.sum(axis=1).mean() * rec / 1e9)
+                entry[pol] = {"miss_rate": round(float(mm.sum() / distinct.sum()), 4),
+                              "misses_per_layer_call": round(float(mm.mean()), 3),
+                              "upload_gb_per_step": round(gb, 3),
+                              "host_link_ms_per_step": round(gb / link_gbs * 1e3, 2)}
+            study[f"{tname}_b{B}"] = entry
+            print(f"[bench] policy study {tname} b={B}: " +
+                  ", ".join(f"{p_} {v['miss_rate']}" for p_, v in entry.items()), file=sys.stderr, flush=True)
+    wall = (time.perf_counter() - t0) * 1e3
+    res = {"metric": "lru_miss_rate", "value": study["zipf_b1"]["global_lru"]["miss_rate"],
+           "unit": "misses per selected expert (global LRU, Zipf trace, batch 1)", "n_gpus": 1, "steps": n_steps,
+           "warmup": prof, "ms_per_step": round(wall / n_steps, 5), "higher_is_better": False, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+           "config": {"workload": "lru_policy_study", "layers": L, "experts": E, "top_k": k, "slots": S,
+                      "record_bytes": rec, "profile_steps": prof, "link_gbs_assumed": link_gbs},
+           "policies": study}
+    print(json.dumps(res), flush=True)
 
 
 def _fp4_layer_pool(cfg, layer, torch, stride):

@@ -235,6 +235,37 @@ def zipf_trace(cfg: MoEConfig, n_steps: int = None, n_tokens: int = 4) -> np.nda
     return out
 
 
+def sticky_trace(cfg: MoEConfig, n_steps: int, n_tokens: int, p_keep: float) -> np.ndarray:
+    """[steps, layers, n_tokens, k] like zipf_trace, but with temporal
+    locality: from one step to the next each of a token's k experts stays
+    with probability p_keep, and the others are redrawn from the same
+    popularity law (distinct from the kept ones)."""
+    E, k, L = cfg.n_experts, cfg.top_k, cfg.n_layers
+    ranks = np.arange(1, E + 1, dtype=np.float64)
+    logp = -cfg.zipf_s * np.log(ranks)
+    out = np.empty((n_steps, L, n_tokens, k), dtype=np.int32)
+    for layer in range(L):
+        perm = rng(cfg.cid, KIND_PERM, layer).permutation(E)
+        g = rng(cfg.cid, KIND_TRACE, layer, 1)
+        cur = None
+        for st in range(n_steps):
+            gum = logp[None, :] + g.gumbel(size=(n_tokens, E))
+            if cur is None:
+                cur = np.argsort(-gum, axis=-1, kind="stable")[:, :k]
+            else:
+                keep = g.random((n_tokens, k)) < p_keep
+                nxt = np.empty_like(cur)
+                for t in range(n_tokens):
+                    kept = [r for r, kp in zip(cur[t], keep[t]) if kp]
+                    sc = gum[t].copy()
+                    sc[kept] = -np.inf
+                    fresh = np.argsort(-sc, kind="stable")[:k - len(kept)]
+                    nxt[t] = np.concatenate([np.array(kept, dtype=np.int64), fresh])
+                cur = nxt
+            out[st, layer] = perm[cur]
+    return out
+
+
 def trace_bias(ids_tk: np.ndarray, n_experts: int, value: float = 30.0) -> np.ndarray:
     """Selection-only bias [T, E] fp32 that puts the trace's experts on top."""
     T = ids_tk.shape[0]

@@ -66,7 +66,8 @@ def parse():
     ap.add_argument("--policy-study", action="store_true",
                     help="LRU workload: miss rates of expert placement policies at equal capacity (slot table only)")
     ap.add_argument("--device-fetch", action="store_true",
-                    help="LRU decode: missed experts copied by ft_expert_fetch on the device (no host round trip)")
+                    help="LRU decode: missed experts copied by ft_expert_fetch on the device (no host round trip); "
+                         "the step is one captured HIP graph unless --eager")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -665,7 +666,28 @@ def run_decode_lru(args, cfg, torch):
         src_dev = [torch.tensor(host_ptr[h], dtype=torch.int64, device="cuda") for h in range(NH)]
         nm_dev = torch.zeros(n_steps * L, dtype=torch.int32, device="cuda")
         fetch_ev = []
+    fstep = None
+    if args.device_fetch and not args.eager:
+        # the whole step (route, lookup, fetch, forward per layer) as one HIP
+        # graph; each step's activations and trace bias are staged into its
+        # fixed input buffers first
+        from sparse_moe_expert_softmax_amd.decode_step import DeviceFetchStep
+        fstep = DeviceFetchStep(desc, L, B, table, pool, rec, routers, [src_dev[l % NH] for l in range(L)])
+        fstep.capture()
+        torch.cuda.synchronize()
+        x_idx = [torch.tensor([(s_ * L + l) % 64 for l in range(L)], device="cuda") for s_ in range(n_steps)]
     for s_ in range(n_steps):
+        if fstep is not None:
+            t_s = _t.perf_counter()
+            torch.index_select(xs, 0, x_idx[s_], out=fstep.x)
+            fstep.bias.zero_()
+            fstep.bias.scatter_(2, trace_dev[s_], 30.0)
+            fstep.run()
+            nm_dev[s_ * L:(s_ + 1) * L].copy_(fstep.mlist[:, 0])
+            comp.synchronize()
+            if s_ >= args.warmup:
+                step_ms.append((_t.perf_counter() - t_s) * 1e3)
+            continue
         t_s = _t.perf_counter()
         for l in range(L):
             x = xs[(s_ * L + l) % 64]
@@ -721,6 +743,8 @@ def run_decode_lru(args, cfg, torch):
         if min(misses) < 0:
             raise RuntimeError("slot pool exhausted")
         up_ev = [(a, b, misses[i]) for a, b, i in fetch_ev]
+    # records copied in the timed steps (fetch durations only exist when launched eagerly)
+    n_up = (sum(misses[args.warmup * L:]) if fstep is not None else sum(n for _, _, n in up_ev))
     # kernel-level forward time without host gaps: replay recorded calls with the queue filled ahead
     rec_calls = []
     for s_ in range(max(args.warmup, n_steps - 4), n_steps):
@@ -744,9 +768,8 @@ def run_decode_lru(args, cfg, torch):
     torch.cuda.synchronize()
     f_res_ms = np.array([a.elapsed_time(b) for a, b in f_res])
     d_res = np.array([len(np.unique(i_.cpu().numpy())) for _, i_, _, _ in rec_calls])
-    n_up = sum(n for _, _, n in up_ev)
     up_ms = sum(a.elapsed_time(b) for a, b, _ in up_ev)
-    f_ms = np.array([a.elapsed_time(b) for a, b in fwd_ms])
+    f_ms = np.array([a.elapsed_time(b) for a, b in fwd_ms]) if fwd_ms else None
     miss_arr = np.array(misses).reshape(n_steps, L)
     # distinct experts per call = the trace's distinct ids (routing follows the trace)
     distinct = np.array([[len(np.unique(trace[s_, l, :B])) for l in range(L)] for s_ in range(args.warmup, n_steps)])
@@ -757,7 +780,9 @@ def run_decode_lru(args, cfg, torch):
                        {"workload": cfg.name, "batch": B, "layers": L, "hidden": H, "experts": E, "top_k": k,
                         "inter": I, "weights": "mxfp4", "pool_slots": S, "pool_gb": round(S * stride / 1e9, 1),
                         "trace": f"zipf s={cfg.zipf_s}, {n_steps} steps, cold start", "host_layer_images": NH,
-                        "launch": ("eager, misses fetched on the device (ft_expert_fetch, no host round trip)"
+                        "launch": ("one HIP graph per step: route, lookup, on-device fetch, forward per layer"
+                                   if fstep is not None else
+                                   "eager, misses fetched on the device (ft_expert_fetch, no host round trip)"
                                    if args.device_fetch else
                                    "eager, host-synchronous per layer (miss list read back before uploads)")},
                        "bf16")
@@ -772,9 +797,9 @@ def run_decode_lru(args, cfg, torch):
                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                        "bytes_per_launch": round(float(np.mean(fwd_bytes))),
                        "avg_launch_us": round(float(np.mean(f_res_ms)) * 1e3, 2),
-                       "note": "forward calls of the last trace steps replayed with the queue filled ahead; "
-                               "in the host-synchronous loop the forward averaged "
-                               f"{float(np.mean(f_ms)) * 1e3:.1f} us"}
+                       "note": "forward calls of the last trace steps replayed with the queue filled ahead"
+                               + ("" if f_ms is None else "; in the timed loop the forward averaged "
+                                  f"{float(np.mean(f_ms)) * 1e3:.1f} us")}
     print(json.dumps(res), flush=True)
 
 

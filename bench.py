@@ -36,6 +36,12 @@ HBM_PEAK_GBS = 8000.0
 DECODE_TRAFFIC = {"321d938c5698ebb9": 75860516}
 DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_expert_softmax_amd", "csrc",
                           "decode_mfma.hip")
+# The same for the prefill workload (MXFP4, H4096, E256, top-6, 8,192 tokens):
+# every kernel of one ft_moe_forward call, keyed by the prefixes of the three
+# sources those kernels come from.
+PREFILL_TRAFFIC = {("06057512ed137d49", "8564bd36b3d79a3c", "eaa066699a61b5fb"): 4987291342}
+PREFILL_SRCS = [os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "csrc", f)
+                for f in ("mfma.hip", "permute.hip", "gemv.hip")]
 
 
 def measured_decode_traffic(cfg_name, batch):
@@ -45,6 +51,17 @@ def measured_decode_traffic(cfg_name, batch):
     with open(DECODE_SRC, "rb") as f:
         h = hashlib.sha256(f.read()).hexdigest()[:16]
     return DECODE_TRAFFIC.get(h)
+
+
+def measured_prefill_traffic(cfg_name, chunk_tokens):
+    import hashlib
+    if cfg_name != "prefill_mxfp4_h4096_e256" or chunk_tokens != 8192:
+        return None
+    key = []
+    for p in PREFILL_SRCS:
+        with open(p, "rb") as f:
+            key.append(hashlib.sha256(f.read()).hexdigest()[:16])
+    return PREFILL_TRAFFIC.get(tuple(key))
 
 
 def parse():
@@ -201,12 +218,8 @@ def main():
             ftmoe.ft_moe_forward(desc, xs[s, l], ids_all[s, l], gates_all[s, l], pools[l], out, ws, stream=stream)
             ev[l][1].record(stream)
 
-    if args.calibrate_copy:  # a plain copy kernel of known size, for hardware-counter calibration
-        src_c = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
-        dst_c = torch.empty_like(src_c)
-        dst_c.copy_(src_c)
-        torch.cuda.synchronize()
-        del src_c, dst_c
+    if args.calibrate_copy:
+        _calibration_copy(torch)
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -408,6 +421,16 @@ def _fp4_layer_pool(cfg, layer, torch, stride):
     return pool
 
 
+def _calibration_copy(torch):
+    """One plain 256 MiB device-to-device copy: a kernel of known traffic whose
+    hardware-counter readings scale the other kernels' readings."""
+    src_c = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+    dst_c = torch.empty_like(src_c)
+    dst_c.copy_(src_c)
+    torch.cuda.synchronize()
+    del src_c, dst_c
+
+
 def run_prefill(args, cfg, torch):
     """8,192-token chunks through the MXFP4 layers: compute with weights
     resident, then the full pipeline where the next layer's whole expert set
@@ -447,6 +470,8 @@ def run_prefill(args, cfg, torch):
     comp = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     EV = lambda: torch.cuda.Event(enable_timing=True)
+    if args.calibrate_copy:
+        _calibration_copy(torch)
 
     # ---- compute only, weights resident (alternating the two layer buffers)
     route_ms, fwd_ms = [], []
@@ -524,7 +549,8 @@ def run_prefill(args, cfg, torch):
                        "host_layer_images": NH}
     res["roofline"] = {"bound": "mfma", "kernel": "ft_moe_forward (grouped scaled-MFMA expert GEMM)",
                        "achieved": round(tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                       "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                       "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                       "traffic": measured_prefill_traffic(cfg.name, CH),
                        "flops_per_launch": useful, "avg_launch_us": round(float(np.mean(fwd_ms)) * 1e3, 1)}
     print(json.dumps(res), flush=True)
 

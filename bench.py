@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # plain 256 MiB device copy (FETCH_SIZE x 1.9997, WRITE_SIZE x 1.0).  Keyed by the
 # SHA-256 prefix of the kernel source the counters were taken on: any change to
 # that source reports null until the counters are taken again.
-DECODE_TRAFFIC = {"321d938c5698ebb9": 75860516}
+DECODE_TRAFFIC = {"f556c2820f43b052": 75864238}
 DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_expert_softmax_amd", "csrc",
                           "decode_mfma.hip")
 # The same for the prefill workload (MXFP4, H4096, E256, top-6, 8,192 tokens):

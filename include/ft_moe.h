@@ -180,10 +180,12 @@ int ft_moe_forward(const ft_moe_desc* desc, const void* x, int32_t n_tokens,
  * resident at its own slot (slot = expert id), for callers whose pool holds
  * all experts: the results (topk_ids, topk_gates, out) are bitwise those of
  * the two calls.  For decode-sized calls (at most 16 tokens on the grouped
- * GEMV path, at most 256 experts) the selection runs inside the gate/up
- * kernel instead of as a launch of its own (the routing rule itself is
- * unchanged: pages, explainer "how" and "who" sections); other sizes run
- * the two calls in sequence.
+ * GEMV path, at most 256 experts, a gate/up grid of at most 1,024
+ * workgroups: min(T k, E) experts x I/8 row tiles, halved where two tiles
+ * share a workgroup) the selection runs inside the gate/up kernel instead of
+ * as a launch of its own (the routing rule itself is unchanged: pages,
+ * explainer "how" and "who" sections); other sizes run the two calls in
+ * sequence.
  * workspace: ft_moe_route_forward_workspace_bytes(desc, T) bytes, 256-byte
  * aligned; calls sharing it must not overlap.  out must not overlap any
  * input.  Errors: those of ft_moe_route and ft_moe_forward. */

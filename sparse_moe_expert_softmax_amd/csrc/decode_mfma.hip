@@ -573,24 +573,38 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
   }
 }
 
+static size_t dec_xl_bytes(int T, int H) {
+  const int tmax = T < 16 ? T : 16;
+  return (size_t)tmax * (H + 8) * 2;
+}
+
+DecGateupShape dec_gateup_shape(const ft_moe_desc& d, int T) {
+  const int H = d.hidden, I = d.inter, E = d.n_experts, P = T * d.top_k;
+  const int nd_max = P < E ? P : E;
+  const int nchunk = H / ((d.w_dtype == FT_BF16) ? 64 : 128);
+  // two 8-row tiles per workgroup when at least DM_MERGE_MIN workgroups
+  // remain (each workgroup groups the pairs, and stages activations, once
+  // for both).  Measured: 10-15% faster on MXFP4 and NVFP4 layers with 1536
+  // and more tiles; on a bf16 layer with 768 tiles the halved grid keeps too
+  // few loads in flight (12% slower), so that one keeps a tile each.
+  DecGateupShape sh;
+  sh.xl = d.w_dtype != FT_BF16 && dec_xl_bytes(T, H) <= 56 * 1024 && nchunk % 16 == 0;  // staged activations
+  sh.ntw = (sh.xl && (I / 8) % 2 == 0 && (int64_t)nd_max * (I / 8) >= 2 * DM_MERGE_MIN) ? 2 : 1;
+  sh.grid = (unsigned)(nd_max * (I / 8 / sh.ntw));
+  return sh;
+}
+
 template <int WD>
 static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const void* x, const int32_t* ids,
                                 const uint32_t* mask, const int32_t* slot_ids, const void* pool, const float* gates,
                                 float* out, char* ws, const DecRoute& route, hipStream_t st) {
   const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k;
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + pl.off_h);
-  const int nd_max = pl.P < E ? pl.P : E;
-  const int nchunk = H / ((WD == FT_BF16) ? 64 : 128);
-  const int tmax = pl.T < 16 ? pl.T : 16;
-  const size_t xl_bytes = (size_t)tmax * (H + 8) * 2;
-  // two 8-row tiles per workgroup when at least DM_MERGE_MIN workgroups
-  // remain (each workgroup groups the pairs, and stages activations, once
-  // for both).  Measured: 10-15% faster on MXFP4 and NVFP4 layers with 1536
-  // and more tiles; on a bf16 layer with 768 tiles the halved grid keeps too
-  // few loads in flight (12% slower), so that one keeps a tile each.
-  const bool xl = WD != FT_BF16 && xl_bytes <= 56 * 1024 && nchunk % 16 == 0;  // staged-activation loop
-  const int ntw = (xl && (I / 8) % 2 == 0 && (int64_t)nd_max * (I / 8) >= 2 * DM_MERGE_MIN) ? 2 : 1;
-  const unsigned grid = nd_max * (I / 8 / ntw);
+  const size_t xl_bytes = dec_xl_bytes(pl.T, H);
+  const DecGateupShape shp = dec_gateup_shape(d, pl.T);
+  const bool xl = shp.xl;
+  const int ntw = shp.ntw;
+  const unsigned grid = shp.grid;
   const int rper = !route.logits ? 0 : (E <= 64 ? 1 : (E <= 128 ? 2 : 4));
   const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
 #define DM_GATEUP(UN, XL_, GRP_, SH)                                                                   \

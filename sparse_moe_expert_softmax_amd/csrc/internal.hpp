@@ -49,6 +49,13 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T);
 
 // decode path (matrix-core GEMV, in-kernel grouping, fused combine)
 bool dec_supported(const ft_moe_desc& d, int T);
+// launch shape of the decode gate/up kernel: staged-activation loop, 8-row
+// tiles per workgroup, workgroups (sized for min(P, E) distinct experts)
+struct DecGateupShape { bool xl; int ntw; unsigned grid; };
+DecGateupShape dec_gateup_shape(const ft_moe_desc& d, int T);
+// the fused route + forward selects inside the gate/up kernel, once per
+// workgroup: worth it only while the grid runs in about one round
+constexpr unsigned DEC_FUSE_MAX_GRID = 1024;
 // route_logits != nullptr: the gate/up kernel selects the top-k from these
 // fp64 logits itself (ids and gates are then ignored) and stores the
 // selection in ids_out / gates_out.

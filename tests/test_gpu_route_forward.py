@@ -2,22 +2,32 @@
 replaces (ft_moe_route, then ft_moe_forward with every expert at its own
 slot) on the same inputs, bit for bit, and against the oracle.
 
-At decode sizes the selection runs inside the gate/up kernel; at other sizes
-the entry point runs the two calls in sequence.  Both branches are covered."""
+At decode sizes whose gate/up grid (min(T k, E) experts x I/8 row tiles,
+halved when two tiles share a workgroup) stays within 1,024 workgroups, the
+selection runs inside the gate/up kernel; otherwise the entry point runs the
+two calls in sequence.  Both branches are covered: the *_SM shapes below keep
+several tokens, a selection bias, a partition mask and full-softmax gates on
+the in-kernel branch."""
 import numpy as np
 import pytest
 import torch
 
 from gpu_util import LayerData, dev, max_rel_err
 from sparse_moe_expert_softmax_amd import ftmoe
-from sparse_moe_expert_softmax_amd.configs import BF16, C1, C2, C3, C5, MXFP4, MoEConfig
+from sparse_moe_expert_softmax_amd.configs import BF16, C1, C2, C3, C5, MXFP4, NVFP4, MoEConfig
 
 pytestmark = pytest.mark.gpu
 
 SMALL = MoEConfig("prefill_small_mxfp4", 90, hidden=256, inter=256, n_experts=8, top_k=2, act_dtype=BF16,
                   router_dtype=BF16, w_dtype=MXFP4, n_layers=1)
-NORENORM = MoEConfig("decode_bf16_full_softmax", 94, hidden=512, inter=256, n_experts=40, top_k=3,
+NORENORM = MoEConfig("decode_bf16_full_softmax", 94, hidden=512, inter=128, n_experts=40, top_k=3,
                      act_dtype=BF16, router_dtype=BF16, w_dtype=BF16, n_layers=1, renormalize=False)
+# in-kernel selection at several tokens: 384 workgroups at T=3 (staged-activation loop)
+MX_SM = MoEConfig("decode_mxfp4_h2048_e64", 86, hidden=2048, inter=256, n_experts=64, top_k=4, act_dtype=BF16,
+                  router_dtype=BF16, w_dtype=MXFP4, n_layers=1)
+# 1,024 workgroups at T=4, the largest grid that still selects in-kernel
+NV_SM = MoEConfig("decode_nvfp4_h2048_e64", 87, hidden=2048, inter=256, n_experts=64, top_k=8, act_dtype=BF16,
+                  router_dtype=BF16, w_dtype=NVFP4, n_layers=1)
 
 
 def fused_vs_separate(cfg, T, step, bias=None, mask=None):
@@ -50,18 +60,22 @@ def test_fused_bf16_decode_matches_separate_calls(T):
     fused_vs_separate(C2, T, 100 + T)
 
 
-@pytest.mark.parametrize("T", [1, 3])
-def test_fused_mxfp4_decode_with_selection_bias(T):
-    print(f"fused C3 T={T} with selection bias", flush=True)
-    bias = np.random.default_rng(3 + T).normal(0.0, 0.5, (T, C3.n_experts))
-    fused_vs_separate(C3, T, 110 + T, bias=bias)
+@pytest.mark.parametrize("cfg,T", [(C3, 1), (C3, 3), (MX_SM, 3)])
+def test_fused_mxfp4_decode_with_selection_bias(cfg, T):
+    print(f"fused {cfg.name} T={T} with selection bias", flush=True)
+    bias = np.random.default_rng(3 + T).normal(0.0, 0.5, (T, cfg.n_experts))
+    fused_vs_separate(cfg, T, 110 + T, bias=bias)
 
 
-def test_fused_nvfp4_decode_with_partition_mask():
-    print("fused C5 T=4 with mask", flush=True)
+@pytest.mark.parametrize("cfg", [C5, NV_SM])
+def test_fused_nvfp4_decode_with_partition_mask(cfg):
+    print(f"fused {cfg.name} T=4 with mask", flush=True)
     m = np.array([0xA5A5A5A5, 0x0F0F0F0F, 0xFFFF0000, 0x12345678, 0x0, 0xFFFFFFFF, 0x3C3C3C3C, 0x55555555],
-                 dtype=np.uint32)
-    fused_vs_separate(C5, 4, 120, mask=m)
+                 dtype=np.uint32)[:(cfg.n_experts + 31) // 32]
+    ld, _, _, f_out = fused_vs_separate(cfg, 4, 120, mask=m)
+    if cfg is NV_SM:  # the oracle layer at C5's size would decode 32 experts of 6144 x 2048 in fp64
+        ref, _, _ = ld.oracle_layer(mask=m)
+        assert max_rel_err(f_out.cpu().numpy(), ref) <= 1e-2
 
 
 def test_fused_full_softmax_gates_and_oracle():

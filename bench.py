@@ -698,7 +698,7 @@ def run_decode_lru(args, cfg, torch):
         # graph; each step's activations and trace bias are staged into its
         # fixed input buffers first
         from sparse_moe_expert_softmax_amd.decode_step import DeviceFetchStep
-        fstep = DeviceFetchStep(desc, L, B, table, pool, rec, routers, [src_dev[l % NH] for l in range(L)])
+        fstep = DeviceFetchStep(desc, L, B, table, S, pool, rec, routers, [src_dev[l % NH] for l in range(L)])
         fstep.capture()
         torch.cuda.synchronize()
         x_idx = [torch.tensor([(s_ * L + l) % 64 for l in range(L)], device="cuda") for s_ in range(n_steps)]

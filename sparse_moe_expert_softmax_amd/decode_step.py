@@ -27,17 +27,24 @@ class DeviceFetchStep:
     [T, E], selection only).  Outputs after each run: `ids`, `gates`,
     `slots`, `flags`, `mlist[l]` = [n_miss, (expert, slot) ...] and `out[l]`.
     `layer_src[l]` is a device int64 tensor of layer l's pinned host record
-    addresses.  The slot table and pool belong to this object's stream while
-    a step runs."""
+    addresses.  `table` was set up by ft_slot_table_init for `n_layers`
+    layers and `n_slots` slots; `pool` is [>= n_slots, expert_stride] bytes.
+    The slot table and pool belong to this object's stream while a step
+    runs."""
 
-    def __init__(self, desc, n_layers, n_tokens, table, pool, record_bytes, routers, layer_src, with_bias=True):
+    def __init__(self, desc, n_layers, n_tokens, table, n_slots, pool, record_bytes, routers, layer_src,
+                 with_bias=True):
         H, E, k = desc.hidden, desc.n_experts, desc.top_k
         L, T = n_layers, n_tokens
         if len(routers) != L or len(layer_src) != L:
             raise ValueError("one router and one host address table per layer")
+        if pool.dim() != 2 or pool.shape[0] < n_slots or pool.shape[1] * pool.element_size() < desc.expert_stride:
+            raise ValueError(f"pool must hold {n_slots} records of {desc.expert_stride} bytes")
+        if table.numel() * table.element_size() < ftmoe.ft_slot_table_bytes(L, E, n_slots):
+            raise ValueError("slot table smaller than ft_slot_table_bytes(n_layers, n_experts, n_slots)")
         self.desc, self.L, self.T = desc, L, T
         self.table, self.pool, self.rec = table, pool, record_bytes
-        self.n_slots = pool.shape[0]
+        self.n_slots = n_slots
         self.routers, self.layer_src = routers, layer_src
         act = {F32: torch.float32, BF16: torch.bfloat16}[desc.act_dtype]
         dev = pool.device

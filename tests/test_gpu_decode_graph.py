@@ -33,7 +33,7 @@ def _make(cfg, S, T, host, routers):
     ftmoe.ft_slot_table_init(table, L, E, S)
     pool = torch.full((S, stride), 0xFF, dtype=torch.uint8, device="cuda")
     src = [torch.tensor([h.data_ptr() for h in host[l]], dtype=torch.int64, device="cuda") for l in range(L)]
-    return DeviceFetchStep(ftmoe.make_desc(cfg, stride), L, T, table, pool, rb, routers, src)
+    return DeviceFetchStep(ftmoe.make_desc(cfg, stride), L, T, table, S, pool, rb, routers, src)
 
 
 def _stage(st, xs, biases):

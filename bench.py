@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--single-batch", action="store_true",
+                    help="bf16 decode at batch 1: skip the batch-2 and batch-4 figures the line also reports")
     ap.add_argument("--workload", default="decode_bf16_h2048_e128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -150,38 +152,13 @@ def cpu_baseline(cfg, batch, seconds):
                       f"excluded), {t_total:.1f} s on 1 thread"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-    import torch
-
+def _measure_decode_bf16(args, cfg, torch, B, pools, routers, desc, calibrate):
+    """One batch size of the resident bf16 decode workload: warm-up, HIP-graph
+    (or eager) timing of whole 40-layer steps, then per-call forward durations
+    with the queue filled ahead; returns the figures the result line reports."""
     from sparse_moe_expert_softmax_amd import ftmoe, synth
-    from sparse_moe_expert_softmax_amd.configs import CONFIGS
-
-    cfg = CONFIGS[args.workload]
-    torch.cuda.set_device(0)
-    if cfg.name == "prefill_mxfp4_h4096_e256":
-        return run_prefill(args, cfg, torch)
-    if args.policy_study:
-        return run_policy_study(args, cfg, torch)
-    if cfg.name == "decode_mxfp4_h4096_e256_lru":
-        return run_decode_lru(args, cfg, torch)
-    if cfg.name == "decode_nvfp4_h6144_e256":
-        return run_decode_resident_fp4(args, cfg, torch)
-    if cfg.name != "decode_bf16_h2048_e128":
-        print(json.dumps({"error": f"no benchmark for workload {cfg.name}"}))
-        sys.exit(2)
-    B, L, E, H, I, k = args.batch, cfg.n_layers, cfg.n_experts, cfg.hidden, cfg.inter, cfg.top_k
-    stride = synth.record_stride(H, I, cfg.w_dtype)
+    L, E, H, I, k = cfg.n_layers, cfg.n_experts, cfg.hidden, cfg.inter, cfg.top_k
     rec_bytes = synth.record_bytes(H, I, cfg.w_dtype)
-    desc = ftmoe.make_desc(cfg, stride)
-    print(f"[bench] generating {L} layers x {E} experts ({L * E * stride / 1e9:.1f} GB) on the device",
-          file=sys.stderr, flush=True)
-    pools = [device_pool_bf16(cfg, l, torch) for l in range(L)]
-    routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(L)]
     n_steps = args.warmup + args.steps
     xs = torch.empty((n_steps, L, B, H), dtype=torch.int16, device="cuda")
     for s in range(n_steps):
@@ -218,7 +195,7 @@ def main():
             ftmoe.ft_moe_forward(desc, xs[s, l], ids_all[s, l], gates_all[s, l], pools[l], out, ws, stream=stream)
             ev[l][1].record(stream)
 
-    if args.calibrate_copy:
+    if calibrate:
         _calibration_copy(torch)
     for s in range(args.warmup):
         step(s)
@@ -252,7 +229,7 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
-    print(f"[bench] timed {args.steps} steps ({'graph' if graphs else 'eager'}): {ms_per_step:.4f} ms/step",
+    print(f"[bench] batch {B}: timed {args.steps} steps ({'graph' if graphs else 'eager'}): {ms_per_step:.4f} ms/step",
           file=sys.stderr, flush=True)
 
     # per-call forward durations: HIP events on the launch stream around every
@@ -279,6 +256,49 @@ def main():
     step_bytes = float(np.mean(d_timed)) * rec_bytes + L * (route_bytes + B * H * 4)
     layer_tok_s = B * L / (ms_per_step * 1e-3)
 
+    return {"ms_per_step": ms_per_step, "layer_tok_s": layer_tok_s, "graphs": len(graphs), "step_bytes": step_bytes,
+            "achieved_gbs": achieved_gbs, "fwd_bytes": float(np.mean(fwd_bytes)), "fwd_us": float(np.mean(fwd_ms)) * 1e3,
+            "distinct": float(np.mean(d_meas))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    from sparse_moe_expert_softmax_amd import ftmoe, synth
+    from sparse_moe_expert_softmax_amd.configs import CONFIGS
+
+    cfg = CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    if cfg.name == "prefill_mxfp4_h4096_e256":
+        return run_prefill(args, cfg, torch)
+    if args.policy_study:
+        return run_policy_study(args, cfg, torch)
+    if cfg.name == "decode_mxfp4_h4096_e256_lru":
+        return run_decode_lru(args, cfg, torch)
+    if cfg.name == "decode_nvfp4_h6144_e256":
+        return run_decode_resident_fp4(args, cfg, torch)
+    if cfg.name != "decode_bf16_h2048_e128":
+        print(json.dumps({"error": f"no benchmark for workload {cfg.name}"}))
+        sys.exit(2)
+    B, L, E, H, I, k = args.batch, cfg.n_layers, cfg.n_experts, cfg.hidden, cfg.inter, cfg.top_k
+    stride = synth.record_stride(H, I, cfg.w_dtype)
+    rec_bytes = synth.record_bytes(H, I, cfg.w_dtype)
+    desc = ftmoe.make_desc(cfg, stride)
+    print(f"[bench] generating {L} layers x {E} experts ({L * E * stride / 1e9:.1f} GB) on the device",
+          file=sys.stderr, flush=True)
+    pools = [device_pool_bf16(cfg, l, torch) for l in range(L)]
+    routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(L)]
+    batches = [B] + ([2, 4] if B == 1 and not args.single_batch else [])
+    meas = {}
+    for bq in batches:
+        meas[bq] = _measure_decode_bf16(args, cfg, torch, bq, pools, routers, desc, args.calibrate_copy and bq == B)
+    m = meas[B]
+    ms_per_step, layer_tok_s = m["ms_per_step"], m["layer_tok_s"]
     res = {
         "metric": "moe_layer_tokens_per_s",
         "value": round(layer_tok_s, 1),
@@ -294,17 +314,23 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": B, "layers": L, "hidden": H, "experts": E, "top_k": k,
                    "inter": I, "weights": "bf16", "resident_gb": round(L * E * stride / 1e9, 1),
-                   "launch": "eager" if not graphs else f"hip graphs ({len(graphs)} captured steps)",
+                   "launch": "eager" if not m["graphs"] else f"hip graphs ({m['graphs']} captured steps)",
                    "calls": "ft_moe_route + ft_moe_forward" if args.separate else "ft_moe_route_forward"},
         "stack_tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
-        "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_hbm_gbs": round(m["step_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "ft_moe_forward (expert GEMV)",
-                     "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "achieved": round(m["achieved_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(m["achieved_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": measured_decode_traffic(cfg.name, B),
-                     "bytes_per_launch": round(float(np.mean(fwd_bytes))), "avg_launch_us": round(float(np.mean(fwd_ms)) * 1e3, 2),
-                     "distinct_experts_per_call": round(float(np.mean(d_meas)), 2)},
+                     "bytes_per_launch": round(m["fwd_bytes"]), "avg_launch_us": round(m["fwd_us"], 2),
+                     "distinct_experts_per_call": round(m["distinct"], 2)},
     }
+    if len(batches) > 1:  # the metric's other decode batch sizes, same layers, same process
+        res["other_batches"] = {
+            str(bq): {"tokens_per_s": round(meas[bq]["layer_tok_s"], 1), "ms_per_step": round(meas[bq]["ms_per_step"], 5),
+                      "forward_us": round(meas[bq]["fwd_us"], 2), "forward_bytes": round(meas[bq]["fwd_bytes"]),
+                      "forward_hbm_frac": round(meas[bq]["achieved_gbs"] / HBM_PEAK_GBS, 4),
+                      "distinct_experts_per_call": round(meas[bq]["distinct"], 2)} for bq in batches[1:]}
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, B, args.cpu_seconds)

@@ -147,7 +147,10 @@ int ft_expert_upload(void* pool_base, int64_t expert_stride, int64_t record_byte
  *    guarantees that every address is pinned host memory (pageable memory
  *    cannot be read by the GPU).
  *  miss_list, n_miss: device, as ft_slot_lookup wrote them.
- *  max_miss: upper bound on *n_miss (the lookup's n_pairs); sizes the grid.
+ *  max_miss: upper bound on *n_miss; sizes the grid.  Pass the lookup's
+ *    n_pairs (a lookup never reports more misses than ids): misses past
+ *    max_miss would not be copied, and the call cannot see *n_miss on the
+ *    host to report it.
  *  Entries with e outside [0, n_experts) or a slot outside [0, n_slots) are
  *  skipped.  Asynchronous on `stream`, after the lookup on the same stream.
  * Errors: FT_EINVAL on nulls, non-positive sizes, record_bytes or stride not

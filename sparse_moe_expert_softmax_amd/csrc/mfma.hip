@@ -285,13 +285,21 @@ __global__ void __launch_bounds__(512, 1) mx_gemm256_kernel(GemmArgs ga) {
   // the scalar offset).  A: instruction t of this wave fills tile rows
   // 8j .. 8j+7, j = wv + 8t, lane -> row 8j + lane/8, physical chunk lane%8.
   // Rows past the tile's valid rows read row 0's line (results discarded).
+  // the rows' sources first, from clamped indices (a guarded load per row
+  // would be a load and a full wait each), then the offsets
+  int srcA[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = 8 * (wv + 8 * t) + (lane >> 3);
+    srcA[t] = arow(r < nv ? r : 0);
+  }
   int voA[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int j = wv + 8 * t;
     const int r = 8 * j + (lane >> 3);
     const int c = (lane & 7) ^ (((lane >> 4) + 4 * (j & 1)) & 7);
-    voA[t] = (r < nv ? arow(r) * K : 0) + 16 * c;
+    voA[t] = (r < nv ? srcA[t] * K : 0) + 16 * c;
   }
   // B: instruction t fills tile weight rows 16j .. 16j+15, j = wv + 8t,
   // lane -> row 16j + lane/4, physical chunk lane%4.
@@ -309,7 +317,7 @@ __global__ void __launch_bounds__(512, 1) mx_gemm256_kernel(GemmArgs ga) {
   int voS;
   {
     const int r = 64 * (wv & 3) + lane;
-    if (wv < 4) voS = (r < nv ? arow(r) : arow(0)) * (K / 32);
+    if (wv < 4) voS = arow(r < nv ? r : 0) * (K / 32);
     else voS = (int)(L.scale_off[wmat(r)] + (int64_t)wrow(r) * (K / 32));
   }
   const int ngroups = (nks + 2) / 3;

@@ -91,6 +91,9 @@ size_t ft_record_bytes(int32_t hidden, int32_t inter, int32_t w_dtype);
  * above (the excluded experts provably score below the k-th).
  * workspace: ft_route_workspace_bytes(desc, T) bytes, 256-byte aligned
  * (holds the logits when `logits` is NULL; calls sharing it must not overlap).
+ * Its contents need not be initialised; every workspace in this header is
+ * fully written before it is read, so one buffer can serve call after call,
+ * also from a replayed graph.
  * Errors: FT_EINVAL on null x/w_router/outputs, n_tokens < 0, k > E,
  * E > 1024, k > 32; FT_EUNSUPPORTED on other dtypes.  n_tokens = 0 is a no-op. */
 size_t ft_route_workspace_bytes(const ft_moe_desc* desc, int32_t n_tokens);

@@ -5,10 +5,15 @@ Test infrastructure only.  The definition followed, step by step:
 1. Router logits l[t,e] = sum_h x[t,h] * W_r[e,h] (no bias term).  Inputs are
    fp32 or bf16, so every product is exact in fp64; l is the correctly
    rounded exact sum (math.fsum).  For large inputs a BLAS fp64 product is
-   used first and its decisions are certified against the classical
-   summation error bound gamma_n * sum|x*w|; any token whose ordering the
-   bound cannot certify is recomputed with fsum, so the selection equals the
-   fsum selection exactly.
+   used first, only to decide the selection: each approximate score is
+   given an interval from the classical summation error bound
+   gamma_n * sum|x*w|, and a token is certified only when its k selected
+   intervals are strictly ordered and the k-th lies strictly above the
+   interval of every unselected expert.  Certified tokens then take the
+   selected experts' logits from fsum; every other token is recomputed with
+   fsum in full.  So ids and gates always equal the all-fsum ones exactly.
+   (The returned logits of unselected experts of certified tokens are the
+   BLAS values, within the bound.)
 2. Selection score s = l + b (b: optional selection-only bias, default 0).
    The k experts with the largest s are kept, ordered by (s descending,
    expert id ascending): equal scores go to the lower id.
@@ -68,6 +73,33 @@ def _gamma(n: int) -> float:
     return n * _U / (1.0 - n * _U)
 
 
+def approx_logits(x: np.ndarray, wr: np.ndarray):
+    """BLAS fp64 logits and, per entry, a bound on their distance from the
+    correctly rounded exact dot products: twice the classical bound
+    gamma_H * sum_h |x w| on any order of floating-point summation."""
+    H = x.shape[1]
+    return x @ wr.T, 2.0 * _gamma(H) * (np.abs(x) @ np.abs(wr).T)
+
+
+def certified_order(s: np.ndarray, slack: np.ndarray, k: int):
+    """Given approximate scores s and radii slack (each exact score lies in
+    [s - slack, s + slack]), return the top-k (score desc, id asc) of the
+    exact scores if the intervals decide it, else None.
+
+    Decided means: consecutive selected experts are strictly separated
+    (lower end of the higher one above the upper end of the next), and the
+    lower end of the k-th is above the upper end of EVERY unselected expert.
+    Then the exact scores are strictly ordered the same way, with no ties."""
+    order = np.argsort(-s, kind="stable")
+    sel, rest = order[:k], order[k:]
+    lo, hi = s - slack, s + slack
+    if np.any(lo[sel[:-1]] <= hi[sel[1:]]):
+        return None
+    if rest.size and lo[sel[-1]] <= hi[rest].max():
+        return None
+    return sel
+
+
 def route(x: np.ndarray, wr: np.ndarray, k: int, bias: np.ndarray = None,
           renormalize: bool = True, exact_all: bool = None):
     """x [T,H] f64, wr [E,H] f64, bias [T,E] or None.
@@ -80,8 +112,7 @@ def route(x: np.ndarray, wr: np.ndarray, k: int, bias: np.ndarray = None,
         logits = np.stack([exact_logits_row(x[t], wr) for t in range(T)]) if T else np.zeros((0, E))
         certified = np.ones(T, dtype=bool)
     else:
-        logits = x @ wr.T
-        bound = 2.0 * _gamma(H) * (np.abs(x) @ np.abs(wr).T)
+        logits, bound = approx_logits(x, wr)
         certified = np.zeros(T, dtype=bool)
     b = np.zeros((T, E)) if bias is None else np.asarray(bias, dtype=np.float64)
     ids = np.zeros((T, k), dtype=np.int32)
@@ -90,14 +121,15 @@ def route(x: np.ndarray, wr: np.ndarray, k: int, bias: np.ndarray = None,
         s = logits[t] + b[t]
         sel = select_topk(s, k)
         if not certified[t]:
-            # the k+1 best positions must be separated by more than the bounds
-            order = np.argsort(-s, kind="stable")[: k + 1]
-            slack = bound[t, order] + 2.0 * _U * np.abs(s[order])
-            gaps = s[order[:-1]] - s[order[1:]]
-            if np.any(gaps <= slack[:-1] + slack[1:]):
+            got = certified_order(s, bound[t] + 2.0 * _U * np.abs(s), k)
+            if got is None or not renormalize:
+                # undecided, or full-softmax gates that need every logit
                 logits[t] = exact_logits_row(x[t], wr)
                 s = logits[t] + b[t]
                 sel = select_topk(s, k)
+            else:
+                # decided: the gates use the exact logits of the selection
+                logits[t, sel] = exact_logits_row(x[t], wr[sel])
         ids[t] = sel
         ls = logits[t, sel]
         if renormalize:

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from oracle import formats, mx
+from oracle import moe as moe_mod
 from oracle.lru import LruSim
 from oracle.moe import exact_logits_row, mask_has, moe_layer, route, select_topk, silu, swiglu_expert
 from oracle.record import decode_record
@@ -280,6 +281,97 @@ def test_certified_blas_routing_equals_fsum_routing():
     ids_b, g_b, _ = route(x, w, 6, exact_all=False)
     np.testing.assert_array_equal(ids_a, ids_b)
     np.testing.assert_allclose(g_a, g_b, rtol=0, atol=1e-12)
+
+
+def _adversarial_layer():
+    """k=2 over 8 experts, x = ones.  Expert 7's router row cancels to an
+    exact logit of 2.25, true rank 2 (ahead of expert 1's 2.0), but its terms
+    are +-2^42, so the classical bound on a floating-point sum of that row is
+    large (about 4): an approximate product may legitimately report it far
+    lower.  Every value is an fp32 number and every product is exact."""
+    H = 64
+    x = np.ones((1, H))
+    w = np.zeros((8, H))
+    w[0, 0], w[1, 0], w[2, 0], w[3, 0] = 3.0, 2.0, 1.0, float(np.float32(0.9))
+    w[4, 0], w[5, 0], w[6, 0] = 0.5, 0.4, 0.3
+    w[7, :62] = np.where(np.arange(62) % 2 == 0, 2.0 ** 42, -(2.0 ** 42))
+    w[7, 62] = 2.25
+    return x, w
+
+
+def _perturbed_approx(delta):
+    """An approximate product that errs by `delta` [E] on every token, each
+    entry inside the error bound it reports."""
+    original = moe_mod.approx_logits
+
+    def approx(x, wr):
+        logits, bound = original(x, wr)
+        assert np.all(np.abs(delta) <= bound)
+        return logits + delta, bound
+    return approx
+
+
+def test_certification_checks_every_unselected_expert(monkeypatch):
+    """An unselected expert whose error interval reaches above the k-th
+    selected one blocks certification, however far down the approximate
+    ranking puts it.  Comparing only neighbours in the approximate top k+1
+    would certify {0, 1} here, while the exact top-2 is {0, 7}."""
+    x, w = _adversarial_layer()
+    ids_x, g_x, l_x = route(x, w, 2, exact_all=True)
+    assert list(ids_x[0]) == [0, 7] and l_x[0, 7] == 2.25
+    delta = np.zeros(8)
+    delta[7] = -1.6                     # approximate logit 0.65: rank 5
+    _, bound = moe_mod.approx_logits(x, w)
+    assert bound[0, 7] > 1.6 > 100 * bound[0, :7].max()
+    monkeypatch.setattr(moe_mod, "approx_logits", _perturbed_approx(delta))
+    ids, gates, _ = route(x, w, 2, exact_all=False)
+    np.testing.assert_array_equal(ids, ids_x)
+    np.testing.assert_array_equal(gates, g_x)
+
+
+def test_certified_tokens_take_gates_from_exact_logits(monkeypatch):
+    """When the approximate order is certified, the gates still come from the
+    correctly rounded logits of the selected experts, not the approximate
+    ones: the gates equal the exact path's bit for bit."""
+    T, E, H = 16, 32, 256
+    x = _bf16_vals((T, H), 1.0, 21)
+    w = _bf16_vals((E, H), 0.02, 22)
+    ids_x, g_x, l_x = route(x, w, 6, exact_all=True)
+    _, bound = moe_mod.approx_logits(x, w)
+    g = np.random.default_rng(23)
+    delta = (g.uniform(-1, 1, size=(T, E)) * bound * 0.5)
+    def approx(xx, wr):
+        logits, bnd = x @ w.T, bound
+        return logits + delta, bnd
+    monkeypatch.setattr(moe_mod, "approx_logits", approx)
+    ids, gates, logits = route(x, w, 6, exact_all=False)
+    np.testing.assert_array_equal(ids, ids_x)
+    np.testing.assert_array_equal(gates, g_x)
+    sel = np.take_along_axis(logits, ids, 1)
+    np.testing.assert_array_equal(sel, np.take_along_axis(l_x, ids_x, 1))
+
+
+def test_certification_rule_is_sound_on_random_intervals():
+    """Brute force over random score intervals: whenever the rule certifies,
+    every choice of exact scores inside the intervals (the end points
+    included) gives the certified selection, in the certified order."""
+    g = np.random.default_rng(24)
+    accepted = 0
+    for trial in range(3000):
+        E, k = 6, int(g.integers(1, 4))
+        s = np.round(g.standard_normal(E), 1)
+        slack = g.uniform(0, 0.3, size=E) * (g.random(E) < 0.7)
+        order = moe_mod.certified_order(s, slack, k)
+        if order is None:
+            continue
+        accepted += 1
+        for _ in range(20):
+            true = s + slack * g.choice([-1.0, 1.0, 0.0], size=E) * g.random(E)
+            np.testing.assert_array_equal(select_topk(true, k), order)
+        for corner in itertools.product([-1.0, 1.0], repeat=E):
+            true = s + slack * np.array(corner)
+            np.testing.assert_array_equal(select_topk(true, k), order)
+    assert accepted > 300
 
 
 # ------------------------------------------------------------- expert FFN --

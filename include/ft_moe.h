@@ -25,8 +25,18 @@
  *    a negative ft_status and launches nothing.  A failed HIP launch returns
  *    FT_EHIP.  ft_last_error() gives a thread-local message for the last
  *    non-OK status.  No C++ exception crosses this boundary.
- *  - Results are deterministic: no floating-point atomics, fixed reduction
- *    orders, so two identical calls give bitwise identical outputs.
+ *  - Results are deterministic: every reduction runs in a fixed order.
+ *    The one floating-point atomic is in the decode-sized forward's down
+ *    projection: each output element receives exactly two fp32 atomic
+ *    additions onto a zero that the same call wrote first, and
+ *    (0 + a) + b == (0 + b) + a in IEEE arithmetic, so two identical calls
+ *    give bitwise identical outputs whichever addition lands first.
+ *
+ * Page names used below: "explainer" = the blog.frelia.link FreeToken
+ * explainer, whose sections are named here "what happened", "why now",
+ * "how" (its section on what changes: co-execution and state reuse),
+ * "who", "caveats" and "glossary"; "architecture guide" = the freetoken.wiki
+ * architecture page.
  */
 #ifndef FT_MOE_H
 #define FT_MOE_H
@@ -79,6 +89,11 @@ typedef struct {
 size_t ft_record_bytes(int32_t hidden, int32_t inter, int32_t w_dtype);
 
 /* ---------------------------------------------------------------- route --
+ * Which experts each token uses: a token activates only a few of a layer's
+ * experts (explainer, "why now": 6 of 256 per layer), and the router's
+ * choice is never altered by where experts are computed (explainer, "what
+ * changes", closing dialogue).  The score function, top-k and renormalised
+ * gates are the textbook MoE router; the pages give no formula.
  * l[t,e] = sum_h x[t,h] W_r[e,h], accumulated from exact products in fp64;
  * score s = l + sel_bias[t,e] (fp64; sel_bias nullable = 0, selection only);
  * topk_ids[t,:] = the k experts with largest s in order (s desc, id asc);
@@ -103,6 +118,11 @@ int ft_moe_route(const ft_moe_desc* desc, const void* x, int32_t n_tokens,
                  void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------ global slot table --
+ * Free device memory is one expert cache shared by every MoE layer, managed
+ * least-recently-used (explainer, "how"; LRU as the glossary
+ * defines it: at capacity, drop what has gone unreferenced longest); the
+ * architecture guide compares this LRU with static and prefill-profiled
+ * placement.
  * One LRU table of n_slots expert slots shared by n_layers layers of
  * n_experts experts each; key = (layer, expert).  Device-resident layout:
  * header {tick u32, status i32, L, E, S} then key_slot i32 [L*E] (-1 absent),
@@ -121,12 +141,21 @@ int ft_slot_table_init(void* table, int32_t n_layers, int32_t n_experts, int32_t
  * Outputs (device): slot_ids i32 [n_pairs], miss_flags u8 [n_pairs] (1 on
  * every occurrence of a missed id), miss_list i32 [2*n_pairs] as (expert,
  * slot) pairs in ascending expert order, n_miss i32 [1].
- * Errors: FT_EINVAL on nulls, layer out of range, n_pairs < 1 or > 1024. */
+ * ids outside [0, n_experts) are not looked up: slot -1, flag 0.
+ * Errors (returned): FT_EINVAL on nulls, layer < 0, n_pairs < 1 or > 1024.
+ * The table's layer count lives on the device, so a layer >= n_layers is
+ * reported there: the call returns FT_OK, the kernel changes no state, sets
+ * the header status to FT_EINVAL, *n_miss = -1, every slot_ids entry -1
+ * and every miss flag 0. */
 int ft_slot_lookup(void* table, int32_t layer, const int32_t* topk_ids, int32_t n_pairs,
                    int32_t* slot_ids, uint8_t* miss_flags, int32_t* miss_list,
                    int32_t* n_miss, void* stream);
 
 /* --------------------------------------------------------------- upload --
+ * The full expert pool lives in host memory; experts missing from the cache
+ * cross the host link into it (explainer, "how"), and at prefill
+ * the next layer's whole expert set is copied while the current layer
+ * computes (same section; architecture guide, prefill passage).
  * Copy n packed expert records from pinned host memory into pool slots:
  * host_src[i] (host array of host pointers, each pinned) -> pool_base +
  * slots[i] * expert_stride, record_bytes bytes each, as hipMemcpyAsync on
@@ -139,9 +168,11 @@ int ft_expert_upload(void* pool_base, int64_t expert_stride, int64_t record_byte
 
 /* ---------------------------------------------------- device-side fetch --
  * The copy step after ft_slot_lookup without a host round trip: the pages
- * keep the per-layer control inside one captured graph (FreeToken blog
- * page, architecture section); here the miss list and its count never leave
- * the device.  Copies, for i < *n_miss, the record of expert miss_list[2i]
+ * keep the dynamic scheduling control inside a GPU-side graph of launches
+ * to cut per-token host overhead (explainer, "how"; the graph
+ * feature as the glossary describes it); here the miss list and its count
+ * never leave the device, so lookup, copy and forward can be captured and
+ * replayed as one graph.  Copies, for i < *n_miss, the record of expert miss_list[2i]
  * from host memory layer_src[e] to pool_base + miss_list[2i+1] *
  * expert_stride.  A negative *n_miss (exhausted pool) copies nothing.
  *  layer_src: device array [n_experts] of addresses of this layer's records
@@ -163,11 +194,16 @@ int ft_expert_fetch(void* pool_base, int64_t expert_stride, int64_t record_bytes
                     const int32_t* n_miss, int32_t max_miss, void* stream);
 
 /* -------------------------------------------------------------- forward --
+ * The experts of one token may be computed in different places and the
+ * partial outputs added, which leaves the MoE output exact (explainer,
+ * "how", decode co-execution passage and closing dialogue): the
+ * expert mask selects one such part.
  * out[t,:] = sum_j [expert_mask has e_tj] * topk_gates[t,j] * y_tj with
  * y_tj = D (silu(G x_t) * (U x_t)) of expert e_tj, summed over j in order.
  * The record of expert e is at pool_base + slot * expert_stride where slot =
  * slot_ids[t*k+j] (slot_ids nullable -> slot = e).  Masked-out experts are
  * never read.  expert_mask: bitset u32 [ceil(E/32)], nullable = all.
+ * A token may list an expert more than once; each listing adds its own term.
  * out: fp32 [T, H], fully overwritten; it must not overlap any input.
  * Decode-sized calls (few pairs per expert) run as bandwidth-bound grouped
  * GEMV; large MXFP4 calls run on gfx950 scaled MFMA with activations
@@ -182,6 +218,7 @@ int ft_moe_forward(const ft_moe_desc* desc, const void* x, int32_t n_tokens,
                    void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------ route + forward --
+ * The route and forward above (same passages) as one call.
  * One call doing ft_moe_route followed by ft_moe_forward with every expert
  * resident at its own slot (slot = expert id), for callers whose pool holds
  * all experts: the results (topk_ids, topk_gates, out) are bitwise those of

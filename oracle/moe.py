@@ -160,6 +160,29 @@ def swiglu_expert(x_t: np.ndarray, G: np.ndarray, U: np.ndarray, D: np.ndarray,
     return D @ h
 
 
+def experts_forward(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, expert, mask=None,
+                    x_quant=None, h_quant=None, y_quant=None, tokens=None) -> np.ndarray:
+    """Steps 4-5 for given ids [T,k] and gates [T,k]: out[t] = sum over j in
+    rank order of [e_tj in mask] g_tj y_tj.  A token may list an expert more
+    than once; each listing adds its own term.  -> out [T,H] (rows outside
+    `tokens` are NaN)."""
+    T, H = x.shape
+    out = np.full((T, H), np.nan)
+    rows = range(T) if tokens is None else tokens
+    for t in rows:
+        acc = np.zeros(H)
+        xt = x[t] if x_quant is None else x_quant(x[t])
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            if not mask_has(mask, e):
+                continue
+            G, U, D = expert(e)
+            y = swiglu_expert(xt, G, U, D, quant=h_quant)
+            acc = acc + gates[t, j] * (y if y_quant is None else y_quant(y))
+        out[t] = acc
+    return out
+
+
 def moe_layer(x: np.ndarray, wr: np.ndarray, expert, k: int, bias=None, mask=None,
               renormalize: bool = True, x_quant=None, h_quant=None, tokens=None, y_quant=None):
     """Full layer.  `expert(e)` returns (G, U, D) in fp64.  `tokens` limits the
@@ -168,19 +191,7 @@ def moe_layer(x: np.ndarray, wr: np.ndarray, expert, k: int, bias=None, mask=Non
     of h before the down projection, and of each expert output before the
     combine (identity when None).
     -> out [T,H] (rows outside `tokens` are NaN), ids, gates."""
-    T, H = x.shape
     ids, gates, _ = route(x, wr, k, bias=bias, renormalize=renormalize)
-    out = np.full((T, H), np.nan)
-    rows = range(T) if tokens is None else tokens
-    for t in rows:
-        acc = np.zeros(H)
-        xt = x[t] if x_quant is None else x_quant(x[t])
-        for j in range(k):
-            e = int(ids[t, j])
-            if not mask_has(mask, e):
-                continue
-            G, U, D = expert(e)
-            y = swiglu_expert(xt, G, U, D, quant=h_quant)
-            acc = acc + gates[t, j] * (y if y_quant is None else y_quant(y))
-        out[t] = acc
+    out = experts_forward(x, ids, gates, expert, mask=mask, x_quant=x_quant, h_quant=h_quant,
+                          y_quant=y_quant, tokens=tokens)
     return out, ids, gates

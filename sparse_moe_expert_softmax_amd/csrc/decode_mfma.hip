@@ -51,7 +51,10 @@ struct PairInfo {
   int n_distinct;   // distinct (kept) experts among the pairs
   int expert;       // expert handled by this workgroup (valid if d < n_distinct)
   int npairs;       // pairs routed to it
+  int ntok;         // distinct tokens among them (<= T)
   int pair[DEC_MAX_PAIRS];  // their pair indices t*k + j, ascending
+  int rank[DEC_MAX_PAIRS];  // rank of each pair's token among the distinct tokens
+  int tok[DEC_MAX_PAIRS];   // token of each rank
 };
 
 __device__ __forceinline__ bool dm_in_mask(const uint32_t* mask, int e) {
@@ -62,7 +65,7 @@ __device__ __forceinline__ bool dm_in_mask(const uint32_t* mask, int e) {
 // appearance goes to this workgroup.  Any fixed order works: d only chooses
 // which workgroup computes which expert.
 __device__ __forceinline__ void dm_group_pairs(const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask,
-                                               int P, int E, int d, PairInfo* pi) {
+                                               int P, int k, int E, int d, PairInfo* pi) {
   const int lane = threadIdx.x & 63;
   int e = -1;
   bool valid = false;
@@ -82,14 +85,25 @@ __device__ __forceinline__ void dm_group_pairs(const int32_t* __restrict__ ids, 
     todo &= ~m;
     ++n;
   }
-  if ((mine >> lane) & 1ull) {
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    pi->pair[__popcll(mine & below)] = lane;
+  // pairs ascend, so their tokens do not decrease; a pair is its token's
+  // first when no pair of the same token sits below it (a token lists an
+  // expert more than once only if the caller's ids repeat it)
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int t0 = (lane / k) * k;  // first pair of this lane's token
+  const uint64_t same_below = below & ~((t0 == 0) ? 0ull : (~0ull >> (64 - t0)));
+  const bool in = (mine >> lane) & 1ull;
+  const uint64_t first = __ballot(in && (mine & same_below) == 0ull);
+  if (in) {
+    const int q = __popcll(mine & below), r = __popcll(first & below);
+    pi->pair[q] = lane;
+    pi->rank[q] = r - (((first >> lane) & 1ull) ? 0 : 1);
+    if ((first >> lane) & 1ull) pi->tok[r] = lane / k;
   }
   if (lane == 0) {
     pi->n_distinct = n;
     pi->expert = my_e;
     pi->npairs = __popcll(mine);
+    pi->ntok = __popcll(first);
   }
 }
 
@@ -266,7 +280,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     ids = s_ids;
     gates = s_gates;
   }
-  if (wv == 0) dm_group_pairs(ids, mask, P, E, d, &pi);
+  if (wv == 0) dm_group_pairs(ids, mask, P, k, E, d, &pi);
   __syncthreads();
   if (d >= pi.n_distinct) return;
   const int e = pi.expert, np = pi.npairs;
@@ -296,19 +310,19 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
   const int cpw = nchunk / DM_WAVES;
   const int cbeg = GRP ? wv * cpw : wv, cend = GRP ? cbeg + cpw : nchunk;
   const int cstep = GRP ? UNROLL : DM_WAVES * UNROLL, ustep = GRP ? 1 : DM_WAVES;
+  if constexpr (XL) {  // stage the activation rows of the expert's distinct tokens (at most T <= 16), once
+    for (int q = tid; q < pi.ntok * (H / 8); q += DM_THREADS) {
+      const int r = q / (H / 8), c8 = q % (H / 8);
+      const int tr = pi.tok[r];
+      *reinterpret_cast<uint4*>(xs + r * XS + 8 * c8) = *reinterpret_cast<const uint4*>(x + (int64_t)tr * H + 8 * c8);
+    }
+  }
   for (int tg = 0; tg < np; tg += 16) {
     const bool tok_ok = tg + col < np;
     const int t = tok_ok ? pi.pair[tg + col] / k : 0;
+    const int xrow = tok_ok ? pi.rank[tg + col] : 0;  // LDS row of this column's token
     const float gate = (tok_ok && wv == 0) ? gates[pi.pair[tg + col]] : 0.f;  // issued before the stream
     const uint16_t* xr = x + (int64_t)t * H;
-    if constexpr (XL) {  // stage the group's activation rows (at most 16)
-      const int nt = (np - tg) < 16 ? (np - tg) : 16;
-      for (int q = tid; q < nt * (H / 8); q += DM_THREADS) {
-        const int r = q / (H / 8), c8 = q % (H / 8);
-        const int tr = pi.pair[tg + r] / k;
-        *reinterpret_cast<uint4*>(xs + r * XS + 8 * c8) = *reinterpret_cast<const uint4*>(x + (int64_t)tr * H + 8 * c8);
-      }
-    }
     for (int rt = rt0; rt < rt0 + ntw; ++rt) {  // this workgroup's tiles, activations staged once
       const int row = row0 + 8 * (rt - rt0);
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -393,7 +407,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     #pragma unroll
               for (int j = 0; j < NM; ++j) {
                 uint4 xv;
-                if constexpr (XL) xv = tok_ok ? *reinterpret_cast<const uint4*>(xs + col * XS + kofs<WD>(c, j, g)) : make_uint4(0, 0, 0, 0);
+                if constexpr (XL) xv = tok_ok ? *reinterpret_cast<const uint4*>(xs + xrow * XS + kofs<WD>(c, j, g)) : make_uint4(0, 0, 0, 0);
                 else xv = xb[u][j];
                 acc = mfma(decode_a<WD>(rw[u], j), as_bf16x8(xv), acc);
               }
@@ -445,7 +459,10 @@ struct DownInfo {
   int pair[DEC_MAX_PAIRS][DD_MAXT];        // pair index of (expert d, token t), -1 if t not routed to d
 };
 
-// Wave 0: every kept (expert, token) pair, grouped by expert in order of first appearance.
+// Wave 0: every kept (expert, token) pair, grouped by (expert, occurrence)
+// in order of first appearance.  A group holds at most one pair per token:
+// a token that lists an expert twice puts its second pair in a group of its
+// own (same expert and slot), so every pair's term reaches the output.
 __device__ __forceinline__ void dd_group_all(const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask,
                                              const int32_t* __restrict__ slot_ids, int P, int k, int E,
                                              DownInfo* di) {
@@ -456,6 +473,14 @@ __device__ __forceinline__ void dd_group_all(const int32_t* __restrict__ ids, co
     e = ids[lane];
     valid = e >= 0 && e < E && dm_in_mask(mask, e);
   }
+  // occurrence of e among this token's earlier ranks
+  const int j = lane % k;
+  int occ = 0;
+  for (int jj = 1; jj < k; ++jj) {
+    const int prev = __shfl(e, lane - jj, 64);
+    occ += (jj <= j && prev == e) ? 1 : 0;
+  }
+  const int key = valid ? (e | (occ << 16)) : -1;
   for (int q = lane; q < DEC_MAX_PAIRS * DD_MAXT; q += 64) (&di->pair[0][0])[q] = -1;
   uint64_t todo = __ballot(valid);
   int n = 0;
@@ -463,7 +488,8 @@ __device__ __forceinline__ void dd_group_all(const int32_t* __restrict__ ids, co
   while (todo) {
     const int leader = __ffsll((unsigned long long)todo) - 1;
     const int el = __builtin_amdgcn_readlane(e, leader);
-    const uint64_t m = __ballot(valid && e == el);
+    const int kl = __builtin_amdgcn_readlane(key, leader);
+    const uint64_t m = __ballot(valid && key == kl);
     if ((m >> lane) & 1ull) my_d = n;
     if (lane == leader) di->slot[n] = slot_ids ? slot_ids[leader] : el;
     todo &= ~m;

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 from gpu_util import LayerData, dev, max_rel_err
+from oracle.moe import experts_forward, to_f64
 from oracle.lru import LruSim
 from sparse_moe_expert_softmax_amd import ftmoe, synth
 from sparse_moe_expert_softmax_amd.configs import C1, C2, C3, C5, MoEConfig, F32, BF16
@@ -171,6 +172,34 @@ def test_forward_rejects_bad_arguments():
     with pytest.raises(ftmoe.FtError) as ei:
         ftmoe.ft_moe_forward(bad, x, ids, gates, ld.pool, out, small)
     assert ei.value.status == ftmoe.FT_EINVAL
+
+
+@pytest.mark.parametrize("cfg,T", [(C2, 2), (C3, 4), (C5, 3), (C2, 9), (C1, 5)])
+def test_forward_repeated_expert_in_a_token(cfg, T):
+    """ids given by the caller may list an expert twice for one token; each
+    listing adds its own gated term, on the decode path (C2 T=2, C3 T=4, C5
+    T=3), the general path (C2 T=9: 72 pairs) and the fp32 path alike."""
+    print(f"repeated ids {cfg.name} T={T}", flush=True)
+    ld = LayerData(cfg, 1, 3, T)
+    g = np.random.default_rng(77 + T)
+    k = cfg.top_k
+    ids_np = np.stack([g.choice(cfg.n_experts, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids_np[0, k - 1] = ids_np[0, 0]                  # token 0: first expert again at the last rank
+    if T > 1:
+        ids_np[1, 1:] = ids_np[1, 0]                 # token 1: one expert at every rank
+    gates_np = g.uniform(0.05, 1.0, size=(T, k)).astype(np.float32)
+    ld.build_pool(ids_np.ravel())
+    out = ld.gpu_forward(dev(ids_np), dev(gates_np)).cpu().numpy()
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = ld.experts_f64(e)
+        return cache[e]
+
+    ref = experts_forward(to_f64(ld.x, cfg.act_dtype), ids_np, gates_np.astype(np.float64), expert)
+    err = max_rel_err(out, ref)
+    assert err <= tol(cfg), f"max rel err {err:.3g}"
 
 
 # ------------------------------------------------------------ slot table --

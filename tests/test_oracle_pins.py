@@ -462,6 +462,20 @@ def test_masked_layer_equals_dense_bruteforce_and_partitions_sum():
     assert np.all(none == 0)
 
 
+def test_repeated_expert_in_a_token_adds_each_term():
+    """A token listing expert e twice with gates a and b gets (a + b) y_e."""
+    g = np.random.default_rng(31)
+    H, I = 16, 24
+    mats = {e: (g.standard_normal((I, H)), g.standard_normal((I, H)), g.standard_normal((H, I))) for e in range(4)}
+    x = g.standard_normal((2, H))
+    ids = np.array([[3, 1, 3], [2, 2, 2]])
+    gates = np.array([[0.5, 0.3, 0.2], [0.1, 0.6, 0.3]])
+    out = moe_mod.experts_forward(x, ids, gates, mats.__getitem__)
+    y = {e: swiglu_expert(x[t], *mats[e]) for t, e in ((0, 3), (0, 1))}
+    np.testing.assert_allclose(out[0], 0.7 * y[3] + 0.3 * y[1], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(out[1], 1.0 * swiglu_expert(x[1], *mats[2]), rtol=1e-13, atol=1e-13)
+
+
 def test_identical_experts_give_plain_ffn():
     x, wr, _ = _tiny_layer(40)
     g = np.random.default_rng(41)

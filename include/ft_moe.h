@@ -239,6 +239,31 @@ int ft_moe_route_forward(const ft_moe_desc* desc, const void* x, int32_t n_token
                          const void* pool_base, const uint32_t* expert_mask, float* out,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/* ----------------------------------------- route + forward, no allocation --
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as ft_moe_route_forward
+ * without workspace / ws_bytes; the workspace is a fixed device array inside
+ * this library, FT_NOALLOC_SCRATCH_BYTES per GPU, held by each GPU the
+ * library runs on from module load until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * its device address is looked up once per device on that device's first
+ * call.
+ *  - Calls whose ft_moe_route_forward_workspace_bytes exceeds
+ *    FT_NOALLOC_SCRATCH_BYTES fail with FT_EWORKSPACE before any launch
+ *    (decode batches fit; an 8,192-token prefill chunk does not).
+ *  - Every call on one GPU shares that GPU's array: calls that overlap in
+ *    time on one GPU (other streams, other host threads) race on it and must
+ *    be serialised by the caller.  Consecutive calls on one stream are fine:
+ *    the array needs no initialisation (every byte is written before it is
+ *    read), so the previous call's contents do not matter. */
+#define FT_NOALLOC_SCRATCH_BYTES (32u << 20)
+int ft_moe_route_forward_noalloc(const ft_moe_desc* desc, const void* x, int32_t n_tokens,
+                                 const void* w_router, const float* sel_bias,
+                                 int32_t* topk_ids, float* topk_gates,
+                                 const void* pool_base, const uint32_t* expert_mask, float* out,
+                                 void* stream);
+
 /* Thread-local message for the last non-OK status of this thread. */
 const char* ft_last_error(void);
 

@@ -49,6 +49,14 @@ int check_desc(const ft_moe_desc* d) {
 
 namespace ft {
 
+int report(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
 FwdPlan plan_forward(const ft_moe_desc& d, int T) {
   FwdPlan p{};
   p.T = T;

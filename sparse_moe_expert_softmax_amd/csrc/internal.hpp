@@ -8,6 +8,9 @@
 
 namespace ft {
 
+// record a non-OK status and its message for ft_last_error(); returns code
+int report(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 // router
 // logits: [T, E] fp64 (the caller's when want_logits, else workspace, which
 // the bounded prefill path also uses for its own arrays)

@@ -49,6 +49,8 @@ _SIGS = {
     "ft_moe_route_forward_workspace_bytes": (_sz, [ctypes.POINTER(Desc), _i32]),
     "ft_moe_route_forward": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                             _sz, _vp]),
+    "ft_moe_route_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                    _vp, _vp]),
     "ft_last_error": (ctypes.c_char_p, []),
 }
 EXPORTED = tuple(_SIGS)
@@ -165,6 +167,16 @@ def ft_moe_route_forward(desc: Desc, x, w_router, topk_ids, topk_gates, pool, ou
     _check(lib().ft_moe_route_forward(ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(w_router), _ptr(sel_bias),
                                       _ptr(topk_ids), _ptr(topk_gates), _ptr(pool), _ptr(expert_mask), _ptr(out),
                                       _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def ft_moe_route_forward_noalloc(desc: Desc, x, w_router, topk_ids, topk_gates, pool, out, sel_bias=None,
+                                 expert_mask=None, stream=None):
+    _check(lib().ft_moe_route_forward_noalloc(ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(w_router),
+                                              _ptr(sel_bias), _ptr(topk_ids), _ptr(topk_gates), _ptr(pool),
+                                              _ptr(expert_mask), _ptr(out), _stream(stream)))
+
+
+FT_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def ft_last_error() -> str:

@@ -439,12 +439,7 @@ def run_policy_study(args, cfg, torch):
 
 def _fp4_layer_pool(cfg, layer, torch, stride):
     from sparse_moe_expert_softmax_amd import synth
-    g = torch.Generator(device="cuda")
-    g.manual_seed(synth.ENTROPY * 1000 + cfg.cid * 100 + layer)
-    pool = torch.empty((cfg.n_experts, stride), dtype=torch.uint8, device="cuda")
-    for e in range(cfg.n_experts):
-        pool[e].copy_(synth.device_record_fp4(torch, g, cfg.hidden, cfg.inter, cfg.weight_std, cfg.w_dtype, stride))
-    return pool
+    return synth.device_layer_pool(torch, cfg, layer, stride)
 
 
 def _calibration_copy(torch):

@@ -183,6 +183,36 @@ def experts_forward(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, expert, m
     return out
 
 
+def experts_forward_by_expert(x: np.ndarray, ids: np.ndarray, gates: np.ndarray, expert, tokens, mask=None,
+                              x_quant=None, h_quant=None, y_quant=None) -> np.ndarray:
+    """experts_forward for the rows `tokens`, visiting each expert once, for
+    experts too large to keep decoded together: every y_tj is computed as
+    there and the terms are added in the same rank order, so the result is
+    the same bit for bit.  -> out [T,H] (rows outside `tokens` are NaN)."""
+    T, H = x.shape
+    want = {}
+    for t in tokens:
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            if mask_has(mask, e):
+                want.setdefault(e, []).append((t, j))
+    ys = {}
+    for e in sorted(want):
+        G, U, D = expert(e)
+        for t, j in want[e]:
+            xt = x[t] if x_quant is None else x_quant(x[t])
+            y = swiglu_expert(xt, G, U, D, quant=h_quant)
+            ys[(t, j)] = y if y_quant is None else y_quant(y)
+    out = np.full((T, H), np.nan)
+    for t in tokens:
+        acc = np.zeros(H)
+        for j in range(ids.shape[1]):
+            if (t, j) in ys:
+                acc = acc + gates[t, j] * ys[(t, j)]
+        out[t] = acc
+    return out
+
+
 def moe_layer(x: np.ndarray, wr: np.ndarray, expert, k: int, bias=None, mask=None,
               renormalize: bool = True, x_quant=None, h_quant=None, tokens=None, y_quant=None):
     """Full layer.  `expert(e)` returns (G, U, D) in fp64.  `tokens` limits the

@@ -346,3 +346,14 @@ def device_record_fp4(torch, gen, H: int, I: int, std: float, w_dtype: int, stri
     flat = torch.cat(parts)
     rec[: flat.numel()] = flat
     return rec
+
+
+def device_layer_pool(torch, cfg: MoEConfig, layer: int, stride: int):
+    """[E, stride] u8 device pool holding every expert record of one fp4 layer,
+    generated on the device from a generator seeded by (workload, layer)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(ENTROPY * 1000 + cfg.cid * 100 + layer)
+    pool = torch.empty((cfg.n_experts, stride), dtype=torch.uint8, device="cuda")
+    for e in range(cfg.n_experts):
+        pool[e].copy_(device_record_fp4(torch, g, cfg.hidden, cfg.inter, cfg.weight_std, cfg.w_dtype, stride))
+    return pool

@@ -9,8 +9,11 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import LayerData, max_rel_err
+from gpu_util import LayerData, dev, max_rel_err
+from oracle.moe import experts_forward_by_expert, to_f64
 from oracle.mx import bf16_round_f32, mxfp8_quantize, mxfp8_quantize_f32
+from oracle.record import decode_record
+from sparse_moe_expert_softmax_amd import ftmoe, synth
 from sparse_moe_expert_softmax_amd.configs import BF16, C4, MXFP4, MoEConfig
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
@@ -152,3 +155,86 @@ def test_prefill_experts_spanning_several_row_chunks():
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=2)
     assert counts.min() > 512, counts
     print(f"  rows per expert {counts.tolist()}, max rel err {err:.3g}")
+
+
+# ------------------------------------------------- full 8,192-token chunks --
+def _route_bounded(ld, x):
+    """The many-token router as the forward's callers use it (no logits
+    output: bf16 matrix-core scores with a rounding bound, fp64 refinement)."""
+    cfg, T = ld.cfg, x.shape[0]
+    ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, cfg.top_k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ftmoe.ft_route_workspace_bytes(ld.desc, T), dtype=torch.uint8, device="cuda")
+    ftmoe.ft_moe_route(ld.desc, dev(x), dev(ld.wr), ids, gates, workspace=ws)
+    return ids, gates
+
+
+def _cover_all_experts(o_ids, E, seed):
+    """Tokens, in a seeded random order, each kept if it routes to an expert no
+    earlier kept token does, until every expert is covered."""
+    order = np.random.default_rng(seed).permutation(o_ids.shape[0])
+    seen, rows = set(), []
+    for t in order:
+        new = set(int(e) for e in o_ids[t]) - seen
+        if new:
+            rows.append(int(t))
+            seen |= new
+        if len(seen) == E:
+            break
+    assert len(seen) == E
+    return sorted(rows)
+
+
+def test_prefill_full_chunks_outputs_cover_every_expert():
+    """The 284B-like MXFP4 layer (4,096 / 2,048 / 256 experts / top-6) with
+    every expert resident, as one 8,192-token chunk and as the 16,384-token
+    prompt in two such chunks.  Routing (the bounded router) bit-exact on
+    every token of both chunks; outputs against the oracle (same storage
+    precisions mirrored) on tokens chosen so that together they use all 256
+    experts (chunk 1), and on 8 tokens of chunk 2, run on the same pool and
+    workspace.  Also reported: the error of 12 of chunk 1's sampled outputs
+    against the oracle without the MXFP8 activation quantisation (bf16 x,
+    fp64 h), bounded at 0.1: the matrix cores take x and h as E4M3 with 3
+    mantissa bits, which costs about 5-6% of the output range."""
+    cfg, T, layer = C4, 8192, 2
+    ld = LayerData(cfg, layer, 0, T)
+    print("prefill full chunks: generating 256 expert records on the device", flush=True)
+    pool = synth.device_layer_pool(torch, cfg, layer, ld.stride)
+    fws = torch.empty(ftmoe.ft_moe_workspace_bytes(ld.desc, T), dtype=torch.uint8, device="cuda")
+    chunks = [ld.x, synth.activations(cfg, 1, layer, T)]
+    w64 = to_f64(ld.wr, cfg.router_dtype)
+    results = []
+    for c, x in enumerate(chunks):
+        ids, gates = _route_bounded(ld, x)
+        out = torch.empty((T, cfg.hidden), dtype=torch.float32, device="cuda")
+        ftmoe.ft_moe_forward(ld.desc, dev(x), ids, gates, pool, out, fws)
+        torch.cuda.synchronize()
+        x64 = to_f64(x, cfg.act_dtype)
+        from oracle.moe import route
+        o_ids, o_gates, _ = route(x64, w64, cfg.top_k)
+        np.testing.assert_array_equal(ids.cpu().numpy(), o_ids)
+        np.testing.assert_allclose(gates.cpu().numpy(), o_gates, rtol=0, atol=1e-6)
+        print(f"  chunk {c + 1}: routing bit-exact on all {T} tokens", flush=True)
+        results.append((x64, o_ids, o_gates, out.cpu().numpy()))
+    rows1 = _cover_all_experts(results[0][1], cfg.n_experts, 41)
+    rows2 = sorted(np.random.default_rng(42).choice(T, 8, replace=False).tolist())
+    print(f"  chunk 1: {len(rows1)} tokens cover all {cfg.n_experts} experts", flush=True)
+
+    def expert(e):
+        return decode_record(pool[e].cpu().numpy(), cfg.hidden, cfg.inter, cfg.w_dtype)
+
+    for c, rows in ((0, rows1), (1, rows2)):
+        x64, o_ids, o_gates, out = results[c]
+        ref = experts_forward_by_expert(x64, o_ids, o_gates, expert, rows, x_quant=mxfp8_quantize,
+                                        h_quant=mxfp8_quantize_f32, y_quant=bf16_round_f32)
+        assert not np.isnan(out[rows]).any()
+        err = max_rel_err(out[rows], ref[rows])
+        print(f"  chunk {c + 1}: max rel err {err:.3g} on {len(rows)} tokens (mirrored precisions)", flush=True)
+        assert err <= 1e-2, f"chunk {c + 1}: max rel err {err:.3g}"
+        if c == 0:
+            few = rows[:12]
+            exact = experts_forward_by_expert(x64, o_ids, o_gates, expert, few)
+            dev_err = max_rel_err(out[few], exact[few])
+            print(f"  chunk 1: max rel err {dev_err:.3g} on {len(few)} tokens against bf16 x and fp64 h "
+                  "(no MXFP8 mirroring)", flush=True)
+            assert dev_err <= 0.1

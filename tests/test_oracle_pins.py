@@ -476,6 +476,24 @@ def test_repeated_expert_in_a_token_adds_each_term():
     np.testing.assert_allclose(out[1], 1.0 * swiglu_expert(x[1], *mats[2]), rtol=1e-13, atol=1e-13)
 
 
+def test_expert_major_order_gives_the_same_bits():
+    """experts_forward_by_expert (each expert visited once) equals
+    experts_forward bit for bit, with repeated ids, a mask, quantisation
+    hooks and a subset of rows."""
+    g = np.random.default_rng(32)
+    T, H, I, E, k = 9, 32, 40, 6, 3
+    mats = {e: (g.standard_normal((I, H)), g.standard_normal((I, H)), g.standard_normal((H, I))) for e in range(E)}
+    x = g.standard_normal((T, H))
+    ids = g.integers(0, E, size=(T, k))
+    gates = g.random((T, k))
+    mask = np.array([0b101101], dtype=np.uint32)
+    q = lambda v: np.round(v * 8) / 8
+    rows = [0, 2, 3, 7]
+    a = moe_mod.experts_forward(x, ids, gates, mats.__getitem__, mask=mask, x_quant=q, h_quant=q, tokens=rows)
+    b = moe_mod.experts_forward_by_expert(x, ids, gates, mats.__getitem__, rows, mask=mask, x_quant=q, h_quant=q)
+    np.testing.assert_array_equal(a, b)
+
+
 def test_identical_experts_give_plain_ffn():
     x, wr, _ = _tiny_layer(40)
     g = np.random.default_rng(41)

@@ -193,6 +193,47 @@ int ft_expert_fetch(void* pool_base, int64_t expert_stride, int64_t record_bytes
                     int32_t n_slots, const uint64_t* layer_src, const int32_t* miss_list,
                     const int32_t* n_miss, int32_t max_miss, void* stream);
 
+/* ------------------------------------------------------ prefill pipeline --
+ * Full-layer double buffering at prefill: while layer n computes from one
+ * device layer buffer, the next layer's whole expert set is copied from
+ * pinned host memory into the other on a second stream, so the copy hides
+ * behind the compute (explainer, "how": prefill passage; architecture
+ * guide, prefill passage).  The state below is caller-owned; the library
+ * keeps none.  Buffer b holds expert e of its layer at e * expert_stride
+ * (identity slots), so each layer runs as ft_moe_route_forward on it. */
+typedef struct {
+  void* layer_buf[2];      /* device, each >= n_experts * expert_stride bytes, 256-byte aligned */
+  int64_t expert_stride;   /* bytes between records in a buffer (= desc->expert_stride) */
+  int64_t record_bytes;    /* bytes copied per record (ft_record_bytes) */
+  int32_t n_experts;
+  int32_t n_done;          /* layers enqueued so far (written by the calls) */
+  int32_t n_uploaded;      /* layers whose copy has been enqueued (written by the calls) */
+  int32_t reserved;
+  void* compute_stream;    /* hipStream_t of the route + forward launches */
+  void* copy_stream;       /* hipStream_t of the copies; must differ from compute_stream */
+  void* ready[2];          /* hipEvent_t: buffer b holds its layer (recorded on copy_stream) */
+  void* freed[2];          /* hipEvent_t: the last compute reading buffer b is done (on compute_stream) */
+} ft_prefill_pipeline;
+
+/* Reset the counters and enqueue layer 0's copy into layer_buf[0].
+ * first_layer: (host) array of n_experts pointers to pinned host records.
+ * Errors: FT_EINVAL on a missing buffer, event or record, equal streams,
+ * pageable records (see ft_expert_upload); FT_EHIP on a failed copy. */
+int ft_prefill_pipeline_start(ft_prefill_pipeline* p, const void* const* first_layer);
+
+/* Layer n = p->n_done: (1) if next_layer is not NULL, copy_stream waits
+ * until layer n-1's compute has left buffer (n+1)%2, then that buffer
+ * receives next_layer's records; (2) compute_stream waits for buffer n%2's
+ * copy, then runs ft_moe_route_forward on it (same arguments and results as
+ * that call, pool_base = layer_buf[n%2], no bias, no mask).  Pass next_layer
+ * for every layer but the last: a layer whose copy was never enqueued is
+ * refused with FT_EINVAL (nothing launched).  desc must match the pipeline's
+ * n_experts and expert_stride.  The workspace is the route + forward one;
+ * calls sharing it must be on compute_stream. */
+int ft_prefill_pipeline_layer(ft_prefill_pipeline* p, const void* const* next_layer, const ft_moe_desc* desc,
+                              const void* x, int32_t n_tokens, const void* w_router, int32_t* topk_ids,
+                              float* topk_gates, float* out, void* workspace, size_t ws_bytes);
+
 /* -------------------------------------------------------------- forward --
  * The experts of one token may be computed in different places and the
  * partial outputs added, which leaves the MoE output exact (explainer,

@@ -33,6 +33,14 @@ class Desc(ctypes.Structure):
                 ("expert_stride", ctypes.c_int64)]
 
 
+class PrefillPipelineState(ctypes.Structure):
+    """ft_prefill_pipeline (caller-owned state of the double-buffered prefill)."""
+    _fields_ = [("layer_buf", ctypes.c_void_p * 2), ("expert_stride", ctypes.c_int64),
+                ("record_bytes", ctypes.c_int64), ("n_experts", ctypes.c_int32), ("n_done", ctypes.c_int32),
+                ("n_uploaded", ctypes.c_int32), ("reserved", ctypes.c_int32), ("compute_stream", ctypes.c_void_p),
+                ("copy_stream", ctypes.c_void_p), ("ready", ctypes.c_void_p * 2), ("freed", ctypes.c_void_p * 2)]
+
+
 _lib = None
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _SIGS = {
@@ -51,6 +59,9 @@ _SIGS = {
                                             _sz, _vp]),
     "ft_moe_route_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                                     _vp, _vp]),
+    "ft_prefill_pipeline_start": (ctypes.c_int, [ctypes.POINTER(PrefillPipelineState), ctypes.POINTER(_vp)]),
+    "ft_prefill_pipeline_layer": (ctypes.c_int, [ctypes.POINTER(PrefillPipelineState), ctypes.POINTER(_vp),
+                                                 ctypes.POINTER(Desc), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz]),
     "ft_last_error": (ctypes.c_char_p, []),
 }
 EXPORTED = tuple(_SIGS)
@@ -177,6 +188,22 @@ def ft_moe_route_forward_noalloc(desc: Desc, x, w_router, topk_ids, topk_gates, 
 
 
 FT_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def ft_prefill_pipeline_start(state: PrefillPipelineState, first_layer_ptrs):
+    """first_layer_ptrs: list of n_experts integer addresses of pinned host records."""
+    arr = (_vp * len(first_layer_ptrs))(*first_layer_ptrs)
+    _check(lib().ft_prefill_pipeline_start(ctypes.byref(state), arr))
+
+
+def ft_prefill_pipeline_layer(state: PrefillPipelineState, next_layer_ptrs, desc: Desc, x, w_router, topk_ids,
+                              topk_gates, out, workspace):
+    """next_layer_ptrs: list of pinned host record addresses, or None at the last layer."""
+    arr = None if next_layer_ptrs is None else (_vp * len(next_layer_ptrs))(*next_layer_ptrs)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().ft_prefill_pipeline_layer(ctypes.byref(state), arr, ctypes.byref(desc), _ptr(x), x.shape[0],
+                                           _ptr(w_router), _ptr(topk_ids), _ptr(topk_gates), _ptr(out),
+                                           _ptr(workspace), ws_bytes))
 
 
 def ft_last_error() -> str:

@@ -50,3 +50,30 @@ def test_size_queries_and_validation_without_gpu():
     assert rc == ftmoe.FT_EINVAL and "top_k" in ftmoe.ft_last_error()
     rc = ftmoe.lib().ft_slot_lookup(None, 0, None, 4, None, None, None, None, None)
     assert rc == ftmoe.FT_EINVAL
+
+
+def test_prefill_pipeline_refuses_bad_state_without_gpu():
+    """Checks that run before any HIP call: missing buffers, equal streams,
+    a layer whose copy was never enqueued."""
+    if not os.path.exists(ftmoe.LIB_PATH):
+        pytest.skip("library not built")
+    assert ctypes.sizeof(ftmoe.PrefillPipelineState) == 96
+    s = ftmoe.PrefillPipelineState()
+    rc = ftmoe.lib().ft_prefill_pipeline_start(ctypes.byref(s), None)
+    assert rc == ftmoe.FT_EINVAL and "layer buffers" in ftmoe.ft_last_error()
+    s.layer_buf[0], s.layer_buf[1] = 4096, 8192
+    s.ready[0] = s.ready[1] = s.freed[0] = s.freed[1] = 1
+    s.expert_stride, s.record_bytes, s.n_experts = 4096, 4096, 2
+    s.compute_stream = s.copy_stream = 7
+    rc = ftmoe.lib().ft_prefill_pipeline_start(ctypes.byref(s), None)
+    assert rc == ftmoe.FT_EINVAL and "copy_stream" in ftmoe.ft_last_error()
+    s.copy_stream = 9
+    from sparse_moe_expert_softmax_amd.configs import MXFP4, MoEConfig, BF16
+    cfg = MoEConfig("abi_pipe", 99, hidden=256, inter=256, n_experts=2, top_k=1, act_dtype=BF16,
+                    router_dtype=BF16, w_dtype=MXFP4, n_layers=1)
+    d = ftmoe.make_desc(cfg, 4096)
+    s.n_done, s.n_uploaded = 1, 1      # layer 1 was never uploaded
+    buf = ctypes.create_string_buffer(64)
+    rc = ftmoe.lib().ft_prefill_pipeline_layer(ctypes.byref(s), None, ctypes.byref(d), buf, 4, buf, buf, buf, buf,
+                                               buf, 1 << 30)
+    assert rc == ftmoe.FT_EINVAL and "not uploaded" in ftmoe.ft_last_error()

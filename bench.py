@@ -11,8 +11,12 @@ gate/up + SwiGLU GEMV, down GEMV, combine), with fresh activations for every
 Printed: one JSON line with the metric, a roofline object for the expert
 forward (algorithmic bytes = the distinct experts each call actually routed
 to, times their record bytes, plus activations in and fp32 outputs out, over
-the forward's measured duration, against the 8 TB/s HBM peak), and the fp64
-oracle timed on this host's cores on a bounded sample of the same workload.
+the forward's measured duration, against the 8 TB/s HBM peak), the same
+figures at batches 2 and 4 (other_batches), the metric's prefill half (one
+8,192-token chunk through the MXFP4 layer with its experts resident: route
+and forward durations, tokens/s, matrix-core TFLOP/s against the issued fp8
+rate and the MXFP4 peak, measured HBM traffic), and the fp64 oracle timed on
+this host's cores on a bounded sample of the same decode workload.
 """
 import argparse
 import json
@@ -71,7 +75,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--single-batch", action="store_true",
-                    help="bf16 decode at batch 1: skip the batch-2 and batch-4 figures the line also reports")
+                    help="bf16 decode at batch 1 only: skip the batch-2 and batch-4 figures and the 8,192-token "
+                         "prefill figures the default line also reports")
     ap.add_argument("--workload", default="decode_bf16_h2048_e128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -107,12 +112,21 @@ def device_pool_bf16(cfg, layer, torch):
     return w.view(torch.uint8).view(cfg.n_experts, stride)
 
 
-def cpu_baseline(cfg, batch, seconds):
-    """fp64 oracle on a bounded sample of the same workload: fresh activations
-    per call through one layer whose expert records (host generator) are made
-    once and cached; generation is outside the timed region, the oracle's own
-    record decoding is inside it."""
-    from threadpoolctl import threadpool_limits
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(cfg, batch, seconds, threads):
+    """Oracle calls on fresh activations through one layer, `threads` BLAS
+    threads (None = the library default), until `seconds` of timed work."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle.moe import moe_layer, route, to_f64
     from oracle.record import decode_record
@@ -124,7 +138,8 @@ def cpu_baseline(cfg, batch, seconds):
     calls, tokens, t_total = 0, 0, 0.0
     wall0 = time.perf_counter()
     last = wall0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
+        used = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
         while t_total < seconds and calls < 2000 and time.perf_counter() - wall0 < 4 * seconds + 60:
             x = synth.activations(cfg, 10_000 + calls, layer, batch)
             x64 = to_f64(x, cfg.act_dtype)
@@ -145,11 +160,25 @@ def cpu_baseline(cfg, batch, seconds):
             tokens += batch
             if time.perf_counter() - last > 5:
                 last = time.perf_counter()
-                print(f"[bench] oracle: {calls} calls, {t_total:.1f} s timed", file=sys.stderr, flush=True)
-    return {"value": tokens / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{calls} calls of one decode layer at batch {batch} (route with exact fsum logits + "
+                print(f"[bench] oracle ({used} threads): {calls} calls, {t_total:.1f} s timed", file=sys.stderr,
+                      flush=True)
+    return tokens / t_total, calls, t_total, used
+
+
+def cpu_baseline(cfg, batch, seconds):
+    """fp64 oracle on a bounded sample of the same workload: fresh activations
+    per call through one layer whose expert records (host generator) are made
+    once and cached; generation is outside the timed region, the oracle's own
+    record decoding is inside it.  Timed with the BLAS library's default
+    thread count (all the cores it is allowed) and with one thread."""
+    v_all, c_all, t_all, used = _oracle_rate(cfg, batch, seconds / 2, None)
+    v_one, c_one, t_one, _ = _oracle_rate(cfg, batch, seconds / 2, 1)
+    return {"value": v_all, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{c_all} calls of one decode layer at batch {batch} (route with exact fsum logits + "
                       f"{cfg.top_k} fp64 SwiGLU experts per token, record decoding included, generation "
-                      f"excluded), {t_total:.1f} s on 1 thread"}
+                      f"excluded), {t_all:.1f} s with {used} BLAS threads (the exact router sums run on one)",
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
+            "one_thread": {"value": v_one, "unit": "tokens/s", "calls": c_one, "seconds": round(t_one, 1)}}
 
 
 def _measure_decode_bf16(args, cfg, torch, B, pools, routers, desc, calibrate):
@@ -331,6 +360,10 @@ def main():
                       "forward_us": round(meas[bq]["fwd_us"], 2), "forward_bytes": round(meas[bq]["fwd_bytes"]),
                       "forward_hbm_frac": round(meas[bq]["achieved_gbs"] / HBM_PEAK_GBS, 4),
                       "distinct_experts_per_call": round(meas[bq]["distinct"], 2)} for bq in batches[1:]}
+    if not args.single_batch:  # the metric's prefill half: one 8,192-token chunk, experts resident
+        del pools
+        torch.cuda.empty_cache()
+        res["prefill"] = prefill_figures(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, B, args.cpu_seconds)
@@ -452,6 +485,71 @@ def _calibration_copy(torch):
     del src_c, dst_c
 
 
+def _prefill_resident_times(torch, desc, x, routers, bufs, ids, gates, out, ws, rws, comp, n_warm, n_meas):
+    """Route and forward durations (ms) of 8,192-token calls with the experts
+    resident, alternating between the layer buffers and the routers; HIP
+    events on the launch stream."""
+    from sparse_moe_expert_softmax_amd import ftmoe
+    EV = lambda: torch.cuda.Event(enable_timing=True)
+    route_ms, fwd_ms = [], []
+    for it in range(n_warm + n_meas):
+        l = it % len(routers)
+        e0, e1, e2 = EV(), EV(), EV()
+        e0.record(comp)
+        ftmoe.ft_moe_route(desc, x, routers[l], ids, gates, workspace=rws, stream=comp)
+        e1.record(comp)
+        ftmoe.ft_moe_forward(desc, x, ids, gates, bufs[it % len(bufs)], out, ws, stream=comp)
+        e2.record(comp)
+        if it >= n_warm:
+            torch.cuda.synchronize()
+            route_ms.append(e0.elapsed_time(e1))
+            fwd_ms.append(e1.elapsed_time(e2))
+    return np.array(route_ms), np.array(fwd_ms)
+
+
+MXFP4_PEAK_TFLOPS = 10100.0  # dense MXFP4 x MXFP4 matrix rate
+
+
+def prefill_figures(torch, n_meas=8):
+    """The prefill half of the metric for the default line: one 8,192-token
+    chunk through the 284B-like MXFP4 layer (4,096 / 2,048 / 256 experts /
+    top-6) with its experts resident; two layers generated on the device,
+    alternated."""
+    from sparse_moe_expert_softmax_amd import ftmoe, synth
+    from sparse_moe_expert_softmax_amd.configs import C4
+    cfg, T = C4, 8192
+    H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
+    stride = synth.record_stride(H, I, cfg.w_dtype)
+    desc = ftmoe.make_desc(cfg, stride)
+    print("[bench] prefill figures: generating 2 MXFP4 layers on the device", file=sys.stderr, flush=True)
+    bufs = [synth.device_layer_pool(torch, cfg, l, stride) for l in range(2)]
+    routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(2)]
+    x = torch.from_numpy(synth.activations(cfg, 0, 0, T).view(np.int16)).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ftmoe.ft_moe_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+    rws = torch.empty(ftmoe.ft_route_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+    comp = torch.cuda.current_stream()
+    route_ms, fwd_ms = _prefill_resident_times(torch, desc, x, routers, bufs, ids, gates, out, ws, rws, comp, 2,
+                                               n_meas)
+    del bufs, ws
+    torch.cuda.empty_cache()
+    useful = 6.0 * T * k * H * I
+    tflops = useful / (float(np.mean(fwd_ms)) * 1e-3) / 1e12
+    t_layer = float(np.mean(route_ms + fwd_ms))
+    print(f"[bench] prefill: route {route_ms.mean():.3f} ms, forward {fwd_ms.mean():.3f} ms per layer",
+          file=sys.stderr, flush=True)
+    return {"workload": cfg.name, "tokens": T, "weights": "mxfp4 resident",
+            "tokens_per_s": round(T / (t_layer * 1e-3), 1),
+            "route_us": round(float(route_ms.mean()) * 1e3, 1), "forward_us": round(float(fwd_ms.mean()) * 1e3, 1),
+            "mfma": {"useful_flops_per_forward": useful, "achieved_tflops": round(tflops, 1),
+                     "frac_of_issued_fp8_peak": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                     "frac_of_mxfp4_peak": round(tflops / MXFP4_PEAK_TFLOPS, 4),
+                     "issued": "v_mfma_scale_f32_16x16x128_f8f6f4, MXFP8 activations x MXFP4 weights"},
+            "traffic": measured_prefill_traffic(cfg.name, T)}
+
+
 def run_prefill(args, cfg, torch):
     """8,192-token chunks through the MXFP4 layers: compute with weights
     resident, then the full pipeline where the next layer's whole expert set
@@ -489,70 +587,56 @@ def run_prefill(args, cfg, torch):
     ws = torch.empty(ftmoe.ft_moe_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
     rws = torch.zeros(ftmoe.ft_route_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
     comp = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
     EV = lambda: torch.cuda.Event(enable_timing=True)
     if args.calibrate_copy:
         _calibration_copy(torch)
 
     # ---- compute only, weights resident (alternating the two layer buffers)
-    route_ms, fwd_ms = [], []
     n_warm, n_meas = max(2, args.warmup // 10), max(4, min(args.steps, L))
-    for it in range(n_warm + n_meas):
-        l = it % L
-        e0, e1, e2 = EV(), EV(), EV()
-        e0.record(comp)
-        ftmoe.ft_moe_route(desc, xs[0], routers[l], ids, gates, workspace=rws, stream=comp)
-        e1.record(comp)
-        ftmoe.ft_moe_forward(desc, xs[0], ids, gates, bufs[it % 2], out, ws, stream=comp)
-        e2.record(comp)
-        if it >= n_warm:
-            torch.cuda.synchronize()
-            route_ms.append(e0.elapsed_time(e1))
-            fwd_ms.append(e1.elapsed_time(e2))
-    route_ms, fwd_ms = np.array(route_ms), np.array(fwd_ms)
+    route_ms, fwd_ms = _prefill_resident_times(torch, desc, xs[0], routers, bufs, ids, gates, out, ws, rws, comp,
+                                               n_warm, n_meas)
     t_layer = float(np.mean(route_ms + fwd_ms))
     print(f"[bench] resident: route {route_ms.mean():.3f} ms, forward {fwd_ms.mean():.3f} ms per layer",
           file=sys.stderr, flush=True)
 
-    # ---- full pipeline: next layer's experts uploaded while this layer computes
+    # ---- one layer's upload alone: the host-link rate
+    from sparse_moe_expert_softmax_amd.prefill_pipeline import PrefillPipeline
     recs_ptr = [[host[h][e].data_ptr() for e in range(E)] for h in range(NH)]
-    ready = [EV() for _ in range(L * chunks + 1)]
-    free = [EV() for _ in range(2)]
-    copy_ev = []
+    side = torch.cuda.Stream()
+    copy_ms = []
+    for it in range(3):
+        a, b = EV(), EV()
+        a.record(side)
+        ftmoe.ft_expert_upload(bufs[it % 2], stride, rec, list(range(E)), recs_ptr[it % NH], stream=side)
+        b.record(side)
+        torch.cuda.synchronize()
+        copy_ms.append(a.elapsed_time(b))
+    t_copy = float(np.median(copy_ms))
+    del bufs
+    torch.cuda.empty_cache()
+
+    # ---- full pipeline (the library's double-buffered prefill): the next
+    # layer's experts are copied while this layer computes
+    pp = PrefillPipeline(desc, rec, compute_stream=comp)
+    fws = torch.empty(ftmoe.ft_moe_route_forward_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+    del ws
+    n_total = L * chunks
     torch.cuda.synchronize()
     w0, w1 = EV(), EV()
     w0.record(comp)
-    # layer 0 of chunk 0 is uploaded before the clock as part of the pipeline fill
-    side.wait_stream(comp)
-    c0 = EV(); c0.record(side)
-    ftmoe.ft_expert_upload(bufs[0], stride, rec, list(range(E)), recs_ptr[0], stream=side, done_event=ready[0])
-    c1 = EV(); c1.record(side)
-    copy_ev.append((c0, c1))
+    pp.start(recs_ptr[0])  # layer 0 of chunk 0: part of the pipeline fill, inside the clock
     n = 0
     for c in range(chunks):
         for l in range(L):
-            cur = n % 2
-            if n + 1 < L * chunks:  # start the next layer's upload into the other buffer
-                nl = (n + 1) % L
-                if n >= 1:
-                    side.wait_event(free[(n + 1) % 2])
-                a, b = EV(), EV()
-                a.record(side)
-                ftmoe.ft_expert_upload(bufs[(n + 1) % 2], stride, rec, list(range(E)), recs_ptr[nl % NH],
-                                       stream=side, done_event=ready[n + 1])
-                b.record(side)
-                copy_ev.append((a, b))
-            comp.wait_event(ready[n])
-            ftmoe.ft_moe_route(desc, xs[c], routers[l], ids, gates, workspace=rws, stream=comp)
-            ftmoe.ft_moe_forward(desc, xs[c], ids, gates, bufs[cur], out, ws, stream=comp)
-            free[cur].record(comp)
+            nxt = recs_ptr[((n + 1) % L) % NH] if n + 1 < n_total else None
+            pp.layer(nxt, xs[c], routers[l], ids, gates, out, fws)
             n += 1
     w1.record(comp)
     torch.cuda.synchronize()
     wall_ms = w0.elapsed_time(w1)
-    copy_ms = float(sum(a.elapsed_time(b) for a, b in copy_ev))
-    comp_ms = t_layer * L * chunks
-    upload_gbs = len(copy_ev) * E * rec / (copy_ms * 1e-3) / 1e9
+    copy_sum = t_copy * n_total
+    comp_ms = t_layer * n_total
+    upload_gbs = E * rec / (t_copy * 1e-3) / 1e9
 
     useful = 6.0 * T * k * H * I  # gate/up 4*P*H*I + down 2*P*H*I
     tflops = useful / (float(np.mean(fwd_ms)) * 1e-3) / 1e12
@@ -562,9 +646,10 @@ def run_prefill(args, cfg, torch):
                         "activations": "bf16, quantised to mxfp8 for the matrix cores"}, "f8xf4 (f32 accumulate)")
     res["note"] = "value = tokens/s through one MoE layer with its experts resident (route + forward)"
     res["per_layer_ms"] = {"route": round(float(route_ms.mean()), 4), "forward": round(float(fwd_ms.mean()), 4)}
-    res["pipeline"] = {"wall_ms": round(wall_ms, 2), "upload_ms_sum": round(copy_ms, 2),
+    res["pipeline"] = {"wall_ms": round(wall_ms, 2), "upload_ms_sum": round(copy_sum, 2),
                        "compute_ms_sum": round(comp_ms, 2),
-                       "overlap_efficiency": round(max(copy_ms, comp_ms) / wall_ms, 4),
+                       "overlap_efficiency": round(max(copy_sum, comp_ms) / wall_ms, 4),
+                       "calls": "ft_prefill_pipeline_start / ft_prefill_pipeline_layer",
                        "host_link_gbs": round(upload_gbs, 2),
                        "tokens_per_s_end_to_end": round(T * chunks / (wall_ms * 1e-3), 1),
                        "host_layer_images": NH}

@@ -92,6 +92,9 @@ def parse():
     ap.add_argument("--device-fetch", action="store_true",
                     help="LRU decode: missed experts copied by ft_expert_fetch on the device (no host round trip); "
                          "the step is one captured HIP graph unless --eager")
+    ap.add_argument("--coexec", action="store_true",
+                    help="LRU decode: co-execution (a measured share of each layer's misses computed on the host, "
+                         "the rest fetched on the device), against the graph-captured device-fetch step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -307,6 +310,8 @@ def main():
         return run_prefill(args, cfg, torch)
     if args.policy_study:
         return run_policy_study(args, cfg, torch)
+    if cfg.name == "decode_mxfp4_h4096_e256_lru" and args.coexec:
+        return run_decode_coexec(args, cfg, torch)
     if cfg.name == "decode_mxfp4_h4096_e256_lru":
         return run_decode_lru(args, cfg, torch)
     if cfg.name == "decode_nvfp4_h6144_e256":
@@ -403,49 +408,15 @@ def run_policy_study(args, cfg, torch):
     t0 = time.perf_counter()
     traces = {"zipf": synth.zipf_trace(cfg, n_steps=n_steps, n_tokens=4),
               "sticky_p0.8": synth.sticky_trace(cfg, n_steps, 4, 0.8)}
+    from sparse_moe_expert_softmax_amd import placement
     study = {}
     for tname, tr in traces.items():
         for B in (1, 4):
-            ids_all = torch.from_numpy(tr[:, :, :B, :].reshape(n_steps, L, B * k).astype(np.int32)).cuda()
-            slots = torch.empty(B * k, dtype=torch.int32, device="cuda")
-            flags = torch.empty(B * k, dtype=torch.uint8, device="cuda")
-            mlist = torch.empty(2 * B * k + 1, dtype=torch.int32, device="cuda")
-            res = {}
-            for pol in ("global_lru", "per_layer_lru"):
-                if pol == "global_lru":
-                    tabs = [torch.zeros(ftmoe.ft_slot_table_bytes(L, E, S), dtype=torch.uint8, device="cuda")]
-                    ftmoe.ft_slot_table_init(tabs[0], L, E, S)
-                else:
-                    tabs = [torch.zeros(ftmoe.ft_slot_table_bytes(1, E, S // L), dtype=torch.uint8, device="cuda")
-                            for _ in range(L)]
-                    for t_ in tabs:
-                        ftmoe.ft_slot_table_init(t_, 1, E, S // L)
-                nm = torch.zeros((n_steps, L), dtype=torch.int32, device="cuda")
-                for s_ in range(n_steps):
-                    for l in range(L):
-                        if pol == "global_lru":
-                            ftmoe.ft_slot_lookup(tabs[0], l, ids_all[s_, l], slots, flags, mlist[1:], mlist[:1])
-                        else:
-                            ftmoe.ft_slot_lookup(tabs[l], 0, ids_all[s_, l], slots, flags, mlist[1:], mlist[:1])
-                        nm[s_, l].copy_(mlist[0])
-                res[pol] = nm.cpu().numpy()
-            # profiled static set: the S most frequent keys of the first tenth
             ids_np = tr[:, :, :B, :].reshape(n_steps, L, B * k)
-            cnt = np.zeros((L, E), dtype=np.int64)
-            for s_ in range(prof):
-                for l in range(L):
-                    for e in np.unique(ids_np[s_, l]):
-                        cnt[l, e] += 1
-            order = np.argsort(-cnt.ravel(), kind="stable")[:S]
-            resident = np.zeros(L * E, dtype=bool)
-            resident[order] = True
-            st = np.zeros((n_steps, L), dtype=np.int64)
-            for s_ in range(n_steps):
-                for l in range(L):
-                    u = np.unique(ids_np[s_, l])
-                    st[s_, l] = int((~resident[l * E + u]).sum())
-            res["profiled_static"] = st
-            distinct = np.array([[len(np.unique(ids_np[s_, l])) for l in range(L)] for s_ in range(prof, n_steps)])
+            res = {"global_lru": placement.lru_misses(torch, ids_np, E, S, per_layer=False),
+                   "per_layer_lru": placement.lru_misses(torch, ids_np, E, S, per_layer=True),
+                   "profiled_static": placement.profiled_static_misses(ids_np, E, S, prof)}
+            distinct = placement.distinct_selected(ids_np[prof:])
             entry = {}
             for pol, m in res.items():
                 if (m < 0).any():
@@ -932,6 +903,104 @@ def run_decode_lru(args, cfg, torch):
                        "note": "forward calls of the last trace steps replayed with the queue filled ahead"
                                + ("" if f_ms is None else "; in the timed loop the forward averaged "
                                   f"{float(np.mean(f_ms)) * 1e3:.1f} us")}
+    print(json.dumps(res), flush=True)
+
+
+def run_decode_coexec(args, cfg, torch):
+    """MXFP4 decode through the global LRU pool on the Zipf trace, twice on
+    the same trace and inputs from a cold start: (1) co-execution (CoExecStep:
+    per layer, a measured share q of the misses computed on the host CPU, the
+    rest fetched on the device), (2) the graph-captured device-fetch step
+    (every miss fetched).  Step times, miss split and host-leg time."""
+    from sparse_moe_expert_softmax_amd import ftmoe, synth
+    from sparse_moe_expert_softmax_amd.coexec import CoExecStep
+    from sparse_moe_expert_softmax_amd.decode_step import DeviceFetchStep
+    L = args.layers or cfg.n_layers
+    B = args.batch
+    H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
+    S = int(cfg.pool_fraction * E * L)
+    stride = synth.record_stride(H, I, cfg.w_dtype)
+    rec = synth.record_bytes(H, I, cfg.w_dtype)
+    desc = ftmoe.make_desc(cfg, stride)
+    NH = max(1, min(args.host_layers, L))
+    n_steps = min(cfg.trace_steps, args.warmup + args.steps)
+    print(f"[bench] co-execution: {L} layers, pool {S} slots, {n_steps} trace steps at batch {B}", file=sys.stderr,
+          flush=True)
+    host = []
+    for h in range(NH):
+        d_ = _fp4_layer_pool(cfg, h, torch, stride)
+        hb = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
+        hb.copy_(d_)
+        host.append(hb)
+        del d_
+    host_ptr = [[host[h][e].data_ptr() for e in range(E)] for h in range(NH)]
+    src_dev = [torch.tensor(host_ptr[h], dtype=torch.int64, device="cuda") for h in range(NH)]
+    routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(L)]
+    trace = synth.zipf_trace(cfg, n_steps=n_steps)
+    trace_dev = torch.from_numpy(trace[:, :, :B, :].astype(np.int64)).cuda()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.ENTROPY + 3)
+    xs = torch.randn((64, B, H), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    x_idx = [torch.tensor([(s_ * L + l) % 64 for l in range(L)], device="cuda") for s_ in range(n_steps)]
+    results = {}
+    for mode in ("coexec", "device_fetch"):
+        pool = torch.empty((S, stride), dtype=torch.uint8, device="cuda")
+        table = torch.zeros(ftmoe.ft_slot_table_bytes(L, E, S), dtype=torch.uint8, device="cuda")
+        ftmoe.ft_slot_table_init(table, L, E, S)
+        x = torch.empty((L, B, H), dtype=torch.bfloat16, device="cuda")
+        bias = torch.zeros((L, B, E), dtype=torch.float32, device="cuda")
+        if mode == "coexec":
+            st = CoExecStep(desc, L, B, table, S, pool, rec, routers, [src_dev[l % NH] for l in range(L)],
+                            [host_ptr[l % NH] for l in range(L)])
+            cal = st.calibrate()
+            print(f"[bench] calibration: link {cal['link_gbs']:.1f} GB/s, host {cal['host_gbs']:.1f} GB/s, "
+                  f"q = {cal['q']:.3f}", file=sys.stderr, flush=True)
+        else:
+            st = DeviceFetchStep(desc, L, B, table, S, pool, rec, routers, [src_dev[l % NH] for l in range(L)])
+            st.capture()
+        torch.cuda.synchronize()
+        step_ms, host_ms, n_host, n_up = [], [], 0, 0
+        for s_ in range(n_steps):
+            t0 = time.perf_counter()
+            if mode == "coexec":
+                torch.index_select(xs, 0, x_idx[s_], out=x)
+                bias.zero_()
+                bias.scatter_(2, trace_dev[s_], 30.0)
+                st.step(x, bias)
+            else:
+                torch.index_select(xs, 0, x_idx[s_], out=st.x)
+                st.bias.zero_()
+                st.bias.scatter_(2, trace_dev[s_], 30.0)
+                st.run()
+            torch.cuda.current_stream().synchronize()
+            if s_ >= args.warmup:
+                step_ms.append((time.perf_counter() - t0) * 1e3)
+                if mode == "coexec":
+                    host_ms.append(st.host_ms)
+                    n_host += sum(len(c) for c in st.host_sets)
+                    n_up += sum(len(u) for u in st.uploaded)
+                else:
+                    n_up += int(st.mlist[:, 0].sum())
+        nt = len(step_ms)
+        r = {"ms_per_step": round(float(np.mean(step_ms)), 3), "tokens_per_s": round(B * L / (np.mean(step_ms) * 1e-3), 1),
+             "uploaded_per_step": round(n_up / nt, 2), "host_computed_per_step": round(n_host / nt, 2)}
+        if mode == "coexec":
+            r.update({"q": round(cal["q"], 4), "link_gbs": round(cal["link_gbs"], 1),
+                      "host_gbs": round(cal["host_gbs"], 1), "host_leg_ms_per_step": round(float(np.mean(host_ms)), 3)})
+        results[mode] = r
+        print(f"[bench] {mode}: {r}", file=sys.stderr, flush=True)
+        del st, pool, table
+        torch.cuda.empty_cache()
+    c, f = results["coexec"], results["device_fetch"]
+    res = _base_result(args, c["tokens_per_s"], "tokens/s", c["ms_per_step"],
+                       {"workload": cfg.name, "batch": B, "layers": L, "experts": E, "top_k": k, "slots": S,
+                        "trace": f"zipf s={cfg.zipf_s}, {n_steps} steps, cold start", "host_layer_images": NH,
+                        "calls": "route, ft_slot_probe, host split, ft_slot_lookup, ft_expert_fetch, ft_moe_forward "
+                                 "(mask), ft_moe_forward_host, ft_moe_add_partial per layer"}, "bf16")
+    res["steps"] = n_steps - args.warmup
+    res["coexec"] = c
+    res["device_fetch_graph"] = f
+    res["speedup_vs_device_fetch"] = round(f["ms_per_step"] / c["ms_per_step"], 4)
     print(json.dumps(res), flush=True)
 
 

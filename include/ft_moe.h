@@ -151,6 +151,15 @@ int ft_slot_lookup(void* table, int32_t layer, const int32_t* topk_ids, int32_t 
                    int32_t* slot_ids, uint8_t* miss_flags, int32_t* miss_list,
                    int32_t* n_miss, void* stream);
 
+/* Residency without a state change: resident[p] = 1 if ids[p] (an expert of
+ * `layer`) holds a slot now, else 0 (also for ids outside [0, n_experts) or
+ * a layer beyond the table's).  The decode co-execution step uses it to
+ * choose, before the lookup, which missed experts the host computes: the
+ * lookup is then given those ids as -1, so they take no slot.
+ * Errors: FT_EINVAL on nulls, n < 0, layer < 0.  n = 0 is a no-op. */
+int ft_slot_probe(const void* table, int32_t layer, const int32_t* ids, int32_t n, uint8_t* resident,
+                  void* stream);
+
 /* --------------------------------------------------------------- upload --
  * The full expert pool lives in host memory; experts missing from the cache
  * cross the host link into it (explainer, "how"), and at prefill
@@ -257,6 +266,35 @@ int ft_moe_forward(const ft_moe_desc* desc, const void* x, int32_t n_tokens,
                    const int32_t* slot_ids, const void* pool_base,
                    const uint32_t* expert_mask, float* out,
                    void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------- decode co-execution --
+ * The pages split a decode step's missed experts between a copy over the
+ * host link (computed on the device) and computation in place on the host
+ * CPU, run both at once, and add the partial outputs, which leaves the MoE
+ * output exact (explainer, "how", decode passage and closing dialogue;
+ * architecture guide, decode passage).  These two calls are the host leg
+ * and the sum; the device leg is ft_moe_forward with the complement mask.
+ *
+ * ft_moe_forward_host: out = the masked forward of ft_moe_forward, computed
+ * on the calling process's CPU threads in fp32 (weights decoded exactly,
+ * fp32 accumulation, combine in rank order).  All pointers are HOST
+ * pointers: x [T, H] (desc->act_dtype), topk_ids / topk_gates [T, k],
+ * records[e] = address of expert e's packed record in host memory (only
+ * the experts the mask keeps are read; other entries may be NULL),
+ * expert_mask bitset (nullable = all), out fp32 [T, H] overwritten.
+ * n_threads <= 0: the hardware thread count.  Synchronous.  It runs only
+ * when called: no device entry point falls back to it.
+ * Errors: FT_EINVAL on nulls, bad sizes, a NULL record that is needed;
+ * FT_EUNSUPPORTED on dtypes. */
+int ft_moe_forward_host(const ft_moe_desc* desc, const void* x, int32_t n_tokens,
+                        const int32_t* topk_ids, const float* topk_gates,
+                        const void* const* records, const uint32_t* expert_mask,
+                        float* out, int32_t n_threads);
+
+/* out[i] += part[i] for i < n (device pointers, on `stream`): the sum of two
+ * partial outputs over disjoint expert sets.  Errors: FT_EINVAL on nulls or
+ * n < 0. */
+int ft_moe_add_partial(float* out, const float* part, int64_t n, void* stream);
 
 /* ------------------------------------------------------ route + forward --
  * The route and forward above (same passages) as one call.

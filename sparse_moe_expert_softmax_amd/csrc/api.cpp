@@ -168,6 +168,25 @@ int ft_slot_lookup(void* table, int32_t layer, const int32_t* topk_ids, int32_t 
   return FT_OK;
 }
 
+int ft_slot_probe(const void* table, int32_t layer, const int32_t* ids, int32_t n, uint8_t* resident, void* stream) {
+  if (!table || !ids || !resident) return fail(FT_EINVAL, "NULL argument to ft_slot_probe");
+  if (n < 0) return fail(FT_EINVAL, "n < 0");
+  if (layer < 0) return fail(FT_EINVAL, "layer %d < 0", layer);
+  if (n == 0) return FT_OK;
+  hipError_t e = ft::launch_slot_probe(table, layer, ids, n, resident, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ft_slot_probe launch");
+  return FT_OK;
+}
+
+int ft_moe_add_partial(float* out, const float* part, int64_t n, void* stream) {
+  if (n < 0) return fail(FT_EINVAL, "n < 0");
+  if (n == 0) return FT_OK;
+  if (!out || !part) return fail(FT_EINVAL, "NULL argument to ft_moe_add_partial");
+  hipError_t e = ft::launch_add_partial(out, part, n, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ft_moe_add_partial launch");
+  return FT_OK;
+}
+
 int ft_expert_upload(void* pool_base, int64_t expert_stride, int64_t record_bytes, const int32_t* slots,
                      const void* const* host_src, int32_t n, void* stream, void* done_event) {
   if (n < 0) return fail(FT_EINVAL, "n < 0");

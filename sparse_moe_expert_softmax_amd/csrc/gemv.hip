@@ -287,6 +287,21 @@ __global__ void __launch_bounds__(256) combine_bf16_kernel(const uint16_t* __res
   o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
+// out += part, elementwise (the sum of two partial outputs over disjoint
+// expert sets)
+__global__ void __launch_bounds__(256) add_partial_kernel(float* __restrict__ out, const float* __restrict__ part,
+                                                          int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] += part[i];
+}
+
+hipError_t launch_add_partial(float* out, const float* part, int64_t n, hipStream_t st) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  add_partial_kernel<<<(unsigned)blocks, 256, 0, st>>>(out, part, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const FwdPlan& pl, const int32_t* pos, const float* gates, float* out, char* ws,
                           hipStream_t st) {
   const uint16_t* ybuf = reinterpret_cast<const uint16_t*>(ws + pl.off_y);

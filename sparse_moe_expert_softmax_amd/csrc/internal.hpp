@@ -29,6 +29,8 @@ hipError_t launch_slot_table_init(void* table, int L, int E, int S, hipStream_t 
 hipError_t launch_slot_lookup(void* table, int layer, const int32_t* ids, int n_pairs, int32_t* slot_ids,
                               uint8_t* miss_flags, int32_t* miss_list, int32_t* n_miss, hipStream_t st);
 int slot_max_slots();
+hipError_t launch_slot_probe(const void* table, int layer, const int32_t* ids, int n, uint8_t* resident,
+                             hipStream_t st);
 hipError_t launch_fetch(void* pool, int64_t stride, int64_t rec_bytes, int E, int S, const uint64_t* layer_src,
                         const int32_t* miss_list, const int32_t* n_miss, int max_miss, hipStream_t st);
 int slot_max_experts();
@@ -79,6 +81,8 @@ hipError_t launch_gemv_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
 // large-batch MXFP4 path on gfx950 scaled MFMA
 constexpr int MFMA_MIN_TOKENS = 256;
 bool mfma_supported(const ft_moe_desc& d, int T);
+// out += part over n floats
+hipError_t launch_add_partial(float* out, const float* part, int64_t n, hipStream_t st);
 // fixed-j-order fp32 combine over the bf16 expert outputs y [P, H] at off_y
 hipError_t launch_combine(const FwdPlan& pl, const int32_t* pos, const float* gates, float* out, char* ws,
                           hipStream_t st);

@@ -284,6 +284,25 @@ hipError_t launch_fetch(void* pool, int64_t stride, int64_t rec_bytes, int E, in
   return hipGetLastError();
 }
 
+// Residency of each id in one layer, without changing the table.
+__global__ void slot_probe_kernel(const int32_t* __restrict__ table, int layer, const int32_t* __restrict__ ids,
+                                  int n, uint8_t* __restrict__ resident) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= n) return;
+  const int L = table[2], E = table[3];
+  const int e = ids[p];
+  const bool ok = layer < L && e >= 0 && e < E;
+  const int32_t* key_slot = table + 16;
+  resident[p] = (ok && key_slot[(int64_t)layer * E + (ok ? e : 0)] >= 0) ? 1 : 0;
+}
+
+hipError_t launch_slot_probe(const void* table, int layer, const int32_t* ids, int n, uint8_t* resident,
+                             hipStream_t st) {
+  slot_probe_kernel<<<(n + 255) / 256, 256, 0, st>>>(reinterpret_cast<const int32_t*>(table), layer, ids, n,
+                                                    resident);
+  return hipGetLastError();
+}
+
 hipError_t launch_slot_lookup(void* table, int layer, const int32_t* ids, int n_pairs, int32_t* slot_ids,
                               uint8_t* miss_flags, int32_t* miss_list, int32_t* n_miss, hipStream_t st) {
   slot_lookup_kernel<<<1, SLOT_THREADS, 0, st>>>(table, layer, ids, n_pairs, slot_ids, miss_flags, miss_list,

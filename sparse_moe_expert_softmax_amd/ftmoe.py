@@ -62,6 +62,10 @@ _SIGS = {
     "ft_prefill_pipeline_start": (ctypes.c_int, [ctypes.POINTER(PrefillPipelineState), ctypes.POINTER(_vp)]),
     "ft_prefill_pipeline_layer": (ctypes.c_int, [ctypes.POINTER(PrefillPipelineState), ctypes.POINTER(_vp),
                                                  ctypes.POINTER(Desc), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz]),
+    "ft_slot_probe": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _vp]),
+    "ft_moe_forward_host": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _i32, _vp, _vp, ctypes.POINTER(_vp), _vp, _vp,
+                                           _i32]),
+    "ft_moe_add_partial": (ctypes.c_int, [_vp, _vp, _i64, _vp]),
     "ft_last_error": (ctypes.c_char_p, []),
 }
 EXPORTED = tuple(_SIGS)
@@ -204,6 +208,32 @@ def ft_prefill_pipeline_layer(state: PrefillPipelineState, next_layer_ptrs, desc
     _check(lib().ft_prefill_pipeline_layer(ctypes.byref(state), arr, ctypes.byref(desc), _ptr(x), x.shape[0],
                                            _ptr(w_router), _ptr(topk_ids), _ptr(topk_gates), _ptr(out),
                                            _ptr(workspace), ws_bytes))
+
+
+def ft_slot_probe(table, layer: int, ids, resident, stream=None):
+    _check(lib().ft_slot_probe(_ptr(table), layer, _ptr(ids), ids.numel(), _ptr(resident), _stream(stream)))
+
+
+def _host_ptr(a):
+    """Address of a host array: a CPU torch tensor or a numpy array."""
+    if a is None:
+        return None
+    if hasattr(a, "data_ptr"):
+        return ctypes.c_void_p(a.data_ptr())
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def ft_moe_forward_host(desc: Desc, x, topk_ids, topk_gates, record_ptrs, out, expert_mask=None, n_threads=0):
+    """Host pointers throughout: x, topk_ids, topk_gates, out and expert_mask are
+    CPU tensors or numpy arrays; record_ptrs is a list of n_experts integer
+    host addresses (0 / None for experts that are not read)."""
+    arr = (_vp * len(record_ptrs))(*[p or None for p in record_ptrs])
+    _check(lib().ft_moe_forward_host(ctypes.byref(desc), _host_ptr(x), x.shape[0], _host_ptr(topk_ids),
+                                     _host_ptr(topk_gates), arr, _host_ptr(expert_mask), _host_ptr(out), n_threads))
+
+
+def ft_moe_add_partial(out, part, stream=None):
+    _check(lib().ft_moe_add_partial(_ptr(out), _ptr(part), out.numel(), _stream(stream)))
 
 
 def ft_last_error() -> str:

@@ -43,7 +43,7 @@ DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_mo
 # The same for the prefill workload (MXFP4, H4096, E256, top-6, 8,192 tokens):
 # every kernel of one ft_moe_forward call, keyed by the prefixes of the three
 # sources those kernels come from.
-PREFILL_TRAFFIC = {("a00c7698a35b8841", "8564bd36b3d79a3c", "eaa066699a61b5fb"): 4986282040}
+PREFILL_TRAFFIC = {}
 PREFILL_SRCS = [os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "csrc", f)
                 for f in ("mfma.hip", "permute.hip", "gemv.hip")]
 
@@ -57,7 +57,7 @@ def measured_decode_traffic(cfg_name, batch):
     return DECODE_TRAFFIC.get(h)
 
 
-def measured_prefill_traffic(cfg_name, chunk_tokens):
+def measured_prefill_traffic(cfg_name, chunk_tokens, terms=2):
     import hashlib
     if cfg_name != "prefill_mxfp4_h4096_e256" or chunk_tokens != 8192:
         return None
@@ -65,7 +65,7 @@ def measured_prefill_traffic(cfg_name, chunk_tokens):
     for p in PREFILL_SRCS:
         with open(p, "rb") as f:
             key.append(hashlib.sha256(f.read()).hexdigest()[:16])
-    return PREFILL_TRAFFIC.get(tuple(key))
+    return PREFILL_TRAFFIC.get((terms,) + tuple(key))
 
 
 def parse():
@@ -85,6 +85,9 @@ def parse():
                     help="decode: ft_moe_route then ft_moe_forward instead of the fused ft_moe_route_forward")
     ap.add_argument("--graphs", type=int, default=16, help="distinct captured steps (distinct inputs) replayed in turn")
     ap.add_argument("--tokens", type=int, default=8192, help="prefill: prompt tokens (multiples of 8192 run as chunks)")
+    ap.add_argument("--act-terms", type=int, default=2, choices=(1, 2),
+                    help="prefill: MXFP8 terms per activation on the matrix cores (2: within 1e-2 of the bf16 "
+                         "layer; 1: half the matrix work)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--host-layers", type=int, default=2, help="distinct pinned host layer images (aliased)")
     ap.add_argument("--policy-study", action="store_true",
@@ -485,13 +488,14 @@ def prefill_figures(torch, n_meas=8):
     """The prefill half of the metric for the default line: one 8,192-token
     chunk through the 284B-like MXFP4 layer (4,096 / 2,048 / 256 experts /
     top-6) with its experts resident; two layers generated on the device,
-    alternated."""
+    alternated.  Both activation modes of the matrix-core path: two MXFP8
+    terms (the default, within 1e-2 of the bf16-activation layer) and one
+    (half the matrix work, about 5-6% off it)."""
     from sparse_moe_expert_softmax_amd import ftmoe, synth
     from sparse_moe_expert_softmax_amd.configs import C4
     cfg, T = C4, 8192
     H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
     stride = synth.record_stride(H, I, cfg.w_dtype)
-    desc = ftmoe.make_desc(cfg, stride)
     print("[bench] prefill figures: generating 2 MXFP4 layers on the device", file=sys.stderr, flush=True)
     bufs = [synth.device_layer_pool(torch, cfg, l, stride) for l in range(2)]
     routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(2)]
@@ -499,26 +503,33 @@ def prefill_figures(torch, n_meas=8):
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
     out = torch.empty((T, H), dtype=torch.float32, device="cuda")
-    ws = torch.empty(ftmoe.ft_moe_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
-    rws = torch.empty(ftmoe.ft_route_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
     comp = torch.cuda.current_stream()
-    route_ms, fwd_ms = _prefill_resident_times(torch, desc, x, routers, bufs, ids, gates, out, ws, rws, comp, 2,
-                                               n_meas)
-    del bufs, ws
-    torch.cuda.empty_cache()
     useful = 6.0 * T * k * H * I
-    tflops = useful / (float(np.mean(fwd_ms)) * 1e-3) / 1e12
-    t_layer = float(np.mean(route_ms + fwd_ms))
-    print(f"[bench] prefill: route {route_ms.mean():.3f} ms, forward {fwd_ms.mean():.3f} ms per layer",
-          file=sys.stderr, flush=True)
-    return {"workload": cfg.name, "tokens": T, "weights": "mxfp4 resident",
-            "tokens_per_s": round(T / (t_layer * 1e-3), 1),
+    res = {"workload": cfg.name, "tokens": T, "weights": "mxfp4 resident",
+           "useful_flops_per_forward": useful,
+           "issued": "v_mfma_scale_f32_16x16x128_f8f6f4, MXFP8 activations x MXFP4 weights (fp8 rate)"}
+    for terms in (2, 1):
+        desc = ftmoe.make_desc(cfg, stride, act_terms=terms)
+        ws = torch.empty(ftmoe.ft_moe_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+        rws = torch.empty(ftmoe.ft_route_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+        route_ms, fwd_ms = _prefill_resident_times(torch, desc, x, routers, bufs, ids, gates, out, ws, rws, comp, 2,
+                                                   n_meas)
+        del ws
+        tflops = useful / (float(np.mean(fwd_ms)) * 1e-3) / 1e12
+        t_layer = float(np.mean(route_ms + fwd_ms))
+        print(f"[bench] prefill ({terms} term(s)): route {route_ms.mean():.3f} ms, forward {fwd_ms.mean():.3f} ms "
+              "per layer", file=sys.stderr, flush=True)
+        res["two_terms" if terms == 2 else "one_term"] = {
+            "act_terms": terms, "tokens_per_s": round(T / (t_layer * 1e-3), 1),
             "route_us": round(float(route_ms.mean()) * 1e3, 1), "forward_us": round(float(fwd_ms.mean()) * 1e3, 1),
-            "mfma": {"useful_flops_per_forward": useful, "achieved_tflops": round(tflops, 1),
-                     "frac_of_issued_fp8_peak": round(tflops / MFMA_PEAK_TFLOPS, 4),
-                     "frac_of_mxfp4_peak": round(tflops / MXFP4_PEAK_TFLOPS, 4),
-                     "issued": "v_mfma_scale_f32_16x16x128_f8f6f4, MXFP8 activations x MXFP4 weights"},
-            "traffic": measured_prefill_traffic(cfg.name, T)}
+            "useful_tflops": round(tflops, 1), "issued_tflops": round(tflops * terms, 1),
+            "frac_useful_of_fp8_peak": round(tflops / MFMA_PEAK_TFLOPS, 4),
+            "frac_issued_of_fp8_peak": round(tflops * terms / MFMA_PEAK_TFLOPS, 4),
+            "frac_useful_of_mxfp4_peak": round(tflops / MXFP4_PEAK_TFLOPS, 4),
+            "traffic": measured_prefill_traffic(cfg.name, T, terms)}
+    del bufs
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_prefill(args, cfg, torch):
@@ -535,7 +546,7 @@ def run_prefill(args, cfg, torch):
     stride = synth.record_stride(H, I, cfg.w_dtype)
     rec = synth.record_bytes(H, I, cfg.w_dtype)
     layer_bytes = E * stride
-    desc = ftmoe.make_desc(cfg, stride)
+    desc = ftmoe.make_desc(cfg, stride, act_terms=args.act_terms)
     NH = max(1, min(args.host_layers, L))
     print(f"[bench] prefill: {L} layers, {chunks} chunk(s) of {CH}; {NH} pinned host layer images "
           f"of {layer_bytes / 1e9:.2f} GB", file=sys.stderr, flush=True)
@@ -614,7 +625,8 @@ def run_prefill(args, cfg, torch):
     res = _base_result(args, T / (t_layer * 1e-3), "tokens/s", t_layer * L,
                        {"workload": cfg.name, "tokens_per_chunk": CH, "chunks": chunks, "layers": L, "hidden": H,
                         "experts": E, "top_k": k, "inter": I, "weights": "mxfp4",
-                        "activations": "bf16, quantised to mxfp8 for the matrix cores"}, "f8xf4 (f32 accumulate)")
+                        "activations": f"bf16, as {args.act_terms} MXFP8 term(s) for the matrix cores",
+                        "act_terms": args.act_terms}, "f8xf4 (f32 accumulate)")
     res["note"] = "value = tokens/s through one MoE layer with its experts resident (route + forward)"
     res["per_layer_ms"] = {"route": round(float(route_ms.mean()), 4), "forward": round(float(fwd_ms.mean()), 4)}
     res["pipeline"] = {"wall_ms": round(wall_ms, 2), "upload_ms_sum": round(copy_sum, 2),
@@ -627,7 +639,8 @@ def run_prefill(args, cfg, torch):
     res["roofline"] = {"bound": "mfma", "kernel": "ft_moe_forward (grouped scaled-MFMA expert GEMM)",
                        "achieved": round(tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
-                       "traffic": measured_prefill_traffic(cfg.name, CH),
+                       "issued_frac": round(tflops * args.act_terms / MFMA_PEAK_TFLOPS, 4),
+                       "traffic": measured_prefill_traffic(cfg.name, CH, args.act_terms),
                        "flops_per_launch": useful, "avg_launch_us": round(float(np.mean(fwd_ms)) * 1e3, 1)}
     print(json.dumps(res), flush=True)
 

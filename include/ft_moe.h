@@ -67,11 +67,22 @@ typedef enum { FT_F32 = 0, FT_BF16 = 1, FT_MXFP4 = 2, FT_NVFP4 = 3 } ft_dtype;
  *  renormalize: 1 = gates are the softmax over the k selected logits (the
  *    full softmax renormalised over the selection); 0 = full-softmax probs.
  *  expert_stride: bytes between consecutive expert records in a pool
- *    (>= ft_record_bytes(), multiple of 256). */
+ *    (>= ft_record_bytes(), multiple of 256).
+ *  act_terms: how the large-batch MXFP4 path (matrix cores) carries the
+ *    activations x (before gate/up) and h (before down), which that
+ *    instruction takes only as 8-bit floats: 2 or 0 (the default) = two
+ *    MXFP8 terms, the value and its quantised residual (rms error about
+ *    6e-4 of the value; the outputs stay within 1e-2 of the bf16-activation
+ *    layer), at twice the matrix work; 1 = one MXFP8 term (about 3% rms per
+ *    element, about 5-6% of the output range on the 4096/2048 layer), at
+ *    half the work.  Other paths compute on the exact bf16 activations and
+ *    ignore it. */
 typedef struct {
   int32_t hidden, inter, n_experts, top_k;
   int32_t act_dtype, w_dtype, router_dtype, renormalize;
   int64_t expert_stride;
+  int32_t act_terms;
+  int32_t reserved;   /* 0 */
 } ft_moe_desc;
 
 /* Packed expert record (the offline pre-converted weight format the pages
@@ -282,7 +293,9 @@ int ft_moe_forward(const ft_moe_desc* desc, const void* x, int32_t n_tokens,
  * records[e] = address of expert e's packed record in host memory (only
  * the experts the mask keeps are read; other entries may be NULL),
  * expert_mask bitset (nullable = all), out fp32 [T, H] overwritten.
- * n_threads <= 0: the hardware thread count.  Synchronous.  It runs only
+ * n_threads = 0: the hardware thread count; n_threads < 0: -n_threads
+ * threads on the portable loops only (no AVX2 path for MXFP4 rows, which is
+ * otherwise taken when the CPU has AVX2 and FMA).  Synchronous.  It runs only
  * when called: no device entry point falls back to it.
  * Errors: FT_EINVAL on nulls, bad sizes, a NULL record that is needed;
  * FT_EUNSUPPORTED on dtypes. */

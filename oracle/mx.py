@@ -1,4 +1,5 @@
-"""MXFP8 (E4M3 elements, E8M0 scale per 32) quantisation, and the bf16
+"""MXFP8 (E4M3 elements, E8M0 scale per 32) quantisation, in one term or
+as two terms (the value and its residual, each quantised), and the bf16
 rounding of the expert outputs y, both mirrored for the prefill path (test
 infrastructure).
 
@@ -55,6 +56,23 @@ def mxfp8_quantize_f32(v: np.ndarray) -> np.ndarray:
     h in fp32 when they quantise it, so the oracle takes the same decision on
     the same precision."""
     return mxfp8_quantize(np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64))
+
+
+def mxfp8_two_term(v: np.ndarray) -> np.ndarray:
+    """Two MXFP8 terms: q1 = mxfp8_quantize(v), then the residual v - q1 (exact
+    in fp64, and exact in fp32 too for bf16 or fp32 inputs) quantised the
+    same way with its own block scales; returns q1 + q2.  This is the
+    matrix cores' operand when a bf16 activation is carried as two E4M3
+    terms instead of one."""
+    v = np.asarray(v, dtype=np.float64)
+    q1 = mxfp8_quantize(v)
+    return q1 + mxfp8_quantize(v - q1)
+
+
+def mxfp8_two_term_f32(v: np.ndarray) -> np.ndarray:
+    """mxfp8_two_term of the fp32-rounded values (h is held in fp32 when the
+    kernels quantise it)."""
+    return mxfp8_two_term(np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64))
 
 
 def bf16_round_f32(v: np.ndarray) -> np.ndarray:

@@ -42,6 +42,7 @@ int check_desc(const ft_moe_desc* d) {
     return fail(FT_EUNSUPPORTED, "router_dtype %d (need F32 or BF16)", d->router_dtype);
   if (d->w_dtype < FT_F32 || d->w_dtype > FT_NVFP4) return fail(FT_EUNSUPPORTED, "w_dtype %d", d->w_dtype);
   if (d->hidden % 32 || d->inter % 32) return fail(FT_EINVAL, "hidden and inter must be multiples of 32");
+  if (d->act_terms < 0 || d->act_terms > 2) return fail(FT_EINVAL, "act_terms %d (need 0, 1 or 2)", d->act_terms);
   return FT_OK;
 }
 
@@ -68,7 +69,8 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T) {
   if (p.nb < 1) p.nb = 1;
   p.mfma = mfma_supported(d, T);
   p.path = p.mfma ? PATH_MFMA : (dec_supported(d, T) ? PATH_DEC : PATH_GEMV);
-  p.max_tiles = p.P / 256 + p.E + 1;
+  p.terms = (d.act_terms == 1) ? 1 : 2;
+  p.max_tiles = p.P / (256 / p.terms) + p.E + 1;
   size_t o = 0;
   p.off_hist = o;    o = align256(o + sizeof(int32_t) * (size_t)p.nb * p.E);
   p.off_offsets = o; o = align256(o + sizeof(int32_t) * (size_t)(p.E + 2));
@@ -79,9 +81,9 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T) {
   p.off_h = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.I);   // fp32 h, bf16 hi/lo, or MXFP8 codes
   p.off_y = o;       o = align256(o + (p.mfma ? 2 : 4) * (size_t)p.P * p.H);  // bf16 y on the matrix-core path
   if (p.mfma) {
-    p.off_xq = o;    o = align256(o + (size_t)T * p.H);                     // MXFP8 x codes
-    p.off_xs = o;    o = align256(o + (size_t)T * p.H / 32);                // and scales
-    p.off_hs = o;    o = align256(o + (size_t)p.P * p.I / 32);              // h scales
+    p.off_xq = o;    o = align256(o + (size_t)p.terms * T * p.H);             // MXFP8 x codes (per term)
+    p.off_xs = o;    o = align256(o + (size_t)p.terms * T * p.H / 32);        // and scales
+    p.off_hs = o;    o = align256(o + (size_t)p.terms * p.P * p.I / 32);      // h scales (h codes: off_h)
     p.off_tiles = o; o = align256(o + sizeof(int32_t) * ((size_t)2 * p.max_tiles + 1 +
                                                           (size_t)p.max_tiles * (p.I / 128 + p.H / 256)));
   } else {

@@ -15,9 +15,12 @@
 // atomic counter; the combine is sequential.
 #include <hip/hip_runtime.h>
 
+#include <immintrin.h>
+
 #include <atomic>
 #include <exception>
 #include <cmath>
+#include <algorithm>
 #include <cstring>
 #include <thread>
 #include <vector>
@@ -101,13 +104,57 @@ float dot(const float* a, const float* b, int K) {
   return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
 }
 
+// AVX2 dot products of one MXFP4 row with n vectors: decode and multiply in
+// one pass, no decoded row stored.  2 * E2M1 is an integer in
+// {0, 1, 2, 3, 4, 6, 8, 12} (with sign), so each nibble maps to an int8 by a
+// byte shuffle, widened to int32 and converted to fp32 exactly; every block
+// sum is scaled by 2^(s - 127) / 2.  Sums per block run in a fixed order.
+__attribute__((target("avx2,fma"))) void dot_mxfp4_avx2(const uint8_t* codes, const uint8_t* scales, int K,
+                                                        const float* const* vec, int n, float* res) {
+  const __m128i lut = _mm_setr_epi8(0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12);
+  const __m128i lo4 = _mm_set1_epi8(0x0F);
+  __m256 acc[8];
+  for (int p = 0; p < n; ++p) acc[p] = _mm256_setzero_ps();
+  for (int b = 0; b < K / 32; ++b) {
+    const __m128i q = _mm_loadu_si128(reinterpret_cast<const __m128i*>(codes + 16 * b));
+    const __m128i lo = _mm_and_si128(q, lo4), hi = _mm_and_si128(_mm_srli_epi16(q, 4), lo4);
+    const __m128i v0 = _mm_shuffle_epi8(lut, _mm_unpacklo_epi8(lo, hi));  // elements 0..15
+    const __m128i v1 = _mm_shuffle_epi8(lut, _mm_unpackhi_epi8(lo, hi));  // elements 16..31
+    const __m256 w0 = _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(v0));
+    const __m256 w1 = _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(v0, 8)));
+    const __m256 w2 = _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(v1));
+    const __m256 w3 = _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(v1, 8)));
+    const uint8_t sv = scales[b];
+    const float s = (sv == 255) ? NAN : std::ldexp(0.5f, (int)sv - 127);
+    const __m256 vs = _mm256_set1_ps(s);
+    for (int p = 0; p < n; ++p) {
+      const float* x = vec[p] + 32 * b;
+      __m256 t = _mm256_mul_ps(w0, _mm256_loadu_ps(x));
+      t = _mm256_fmadd_ps(w1, _mm256_loadu_ps(x + 8), t);
+      t = _mm256_fmadd_ps(w2, _mm256_loadu_ps(x + 16), t);
+      t = _mm256_fmadd_ps(w3, _mm256_loadu_ps(x + 24), t);
+      acc[p] = _mm256_fmadd_ps(vs, t, acc[p]);
+    }
+  }
+  for (int p = 0; p < n; ++p) {
+    alignas(32) float f[8];
+    _mm256_store_ps(f, acc[p]);
+    res[p] = ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
+  }
+}
+
+bool have_avx2() {
+  static const bool ok = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma");
+  return ok;
+}
+
 }  // namespace
 
 extern "C" {
 
 static int forward_host(const ft_moe_desc* desc, const void* x, int32_t n_tokens, const int32_t* topk_ids,
                         const float* topk_gates, const void* const* records, const uint32_t* expert_mask,
-                        float* out, int32_t n_threads) {
+                        float* out, int32_t n_threads, bool no_simd) {
   if (!desc) return ft::report(FT_EINVAL, "desc is NULL");
   const int H = desc->hidden, I = desc->inter, E = desc->n_experts, k = desc->top_k, T = n_tokens;
   if (H <= 0 || I <= 0 || E <= 0 || k <= 0 || k > E || H % 32 || I % 32)
@@ -159,6 +206,7 @@ static int forward_host(const ft_moe_desc* desc, const void* x, int32_t n_tokens
   if (nt < 1) nt = 1;
   if (nt > 256) nt = 256;
 
+  const bool fast = wd == FT_MXFP4 && have_avx2() && !no_simd;
   auto worker = [&]() {
     std::vector<float> wg(H > I ? H : I), wu(H > I ? H : I);
     for (;;) {
@@ -167,6 +215,20 @@ static int forward_host(const ft_moe_desc* desc, const void* x, int32_t n_tokens
       Expert& X = ex[it / items_a_per];
       const int r0 = (it % items_a_per) * ROWS_PER_ITEM;
       for (int r = r0; r < r0 + ROWS_PER_ITEM && r < I; ++r) {
+        if (fast) {  // MXFP4 rows, pairs in groups of up to 8
+          for (size_t p0 = 0; p0 < X.pairs.size(); p0 += 8) {
+            const int n = (int)std::min<size_t>(8, X.pairs.size() - p0);
+            const float* v[8];
+            float a[8], b[8];
+            for (int i = 0; i < n; ++i) v[i] = xf.data() + (size_t)X.pairs[p0 + i].t * H;
+            dot_mxfp4_avx2(X.rec + L.code_off[0] + (int64_t)r * H / 2, X.rec + L.scale_off[0] + (int64_t)r * (H / 32),
+                           H, v, n, a);
+            dot_mxfp4_avx2(X.rec + L.code_off[1] + (int64_t)r * H / 2, X.rec + L.scale_off[1] + (int64_t)r * (H / 32),
+                           H, v, n, b);
+            for (int i = 0; i < n; ++i) X.h[(p0 + i) * I + r] = a[i] / (1.0f + std::exp(-a[i])) * b[i];
+          }
+          continue;
+        }
         decode_row(X.rec, L, wd, 0, r, H, wg.data());
         decode_row(X.rec, L, wd, 1, r, H, wu.data());
         for (size_t p = 0; p < X.pairs.size(); ++p) {
@@ -185,6 +247,18 @@ static int forward_host(const ft_moe_desc* desc, const void* x, int32_t n_tokens
       Expert& X = ex[it / items_b_per];
       const int r0 = (it % items_b_per) * ROWS_PER_ITEM;
       for (int r = r0; r < r0 + ROWS_PER_ITEM && r < H; ++r) {
+        if (fast) {
+          for (size_t p0 = 0; p0 < X.pairs.size(); p0 += 8) {
+            const int n = (int)std::min<size_t>(8, X.pairs.size() - p0);
+            const float* v[8];
+            float y[8];
+            for (int i = 0; i < n; ++i) v[i] = X.h.data() + (p0 + i) * I;
+            dot_mxfp4_avx2(X.rec + L.code_off[2] + (int64_t)r * I / 2, X.rec + L.scale_off[2] + (int64_t)r * (I / 32),
+                           I, v, n, y);
+            for (int i = 0; i < n; ++i) X.y[(p0 + i) * H + r] = y[i];
+          }
+          continue;
+        }
         decode_row(X.rec, L, wd, 2, r, I, wg.data());
         for (size_t p = 0; p < X.pairs.size(); ++p) X.y[p * H + r] = dot(wg.data(), X.h.data() + p * I, I);
       }
@@ -219,7 +293,9 @@ int ft_moe_forward_host(const ft_moe_desc* desc, const void* x, int32_t n_tokens
                         const float* topk_gates, const void* const* records, const uint32_t* expert_mask,
                         float* out, int32_t n_threads) {
   try {
-    return forward_host(desc, x, n_tokens, topk_ids, topk_gates, records, expert_mask, out, n_threads);
+    const bool no_simd = n_threads < 0;  // negative: the portable loops (tests compare the two)
+    return forward_host(desc, x, n_tokens, topk_ids, topk_gates, records, expert_mask, out,
+                        n_threads < 0 ? -n_threads : n_threads, no_simd);
   } catch (const std::exception& ex) {
     return ft::report(FT_EINVAL, "host forward: %s", ex.what());
   }

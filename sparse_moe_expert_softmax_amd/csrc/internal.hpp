@@ -44,9 +44,10 @@ struct FwdPlan {
   int T, P, E, H, I, nb;       // tokens, pairs, experts, hidden, inter, permute blocks
   int path;                    // FwdPath
   bool mfma;                   // large-batch MXFP4 path on scaled MFMA
+  int terms;                   // MXFP8 terms per activation on that path (1 or 2)
   size_t off_hist, off_offsets, off_active, off_perm, off_pos, off_h, off_y, off_xq, off_xs, off_hs, off_cnt;
   size_t off_tiles;            // MFMA path: tile list (2 ints per tile) + count
-  int max_tiles;               // upper bound of (expert, 256-row chunk) tiles: P/256 + E + 1
+  int max_tiles;               // upper bound of (expert, row chunk) tiles: P/(256/terms) + E + 1
   size_t bytes;
 };
 typedef FwdPlan DecPlan;

@@ -96,9 +96,36 @@ __device__ __forceinline__ uint32_t quant_block32(const float* v, uint8_t* dst) 
   return sb;
 }
 
-// x [T, H] bf16 -> xq [T, H] E4M3 + xs [T, H/32] E8M0; one thread per 32-block.
+// E4M3 code -> its value (finite codes)
+__device__ __forceinline__ float e4m3_val(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = (e == 0u) ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Two MXFP8 terms of 32 fp32 values: the first as quant_block32, the second
+// the same quantisation of the residual v - q1 (exact in fp32: q1 is within
+// a factor of two of v, or zero).  Codes to dst_hi / dst_lo, scale bytes
+// returned in *s_hi / *s_lo.
+__device__ __forceinline__ void quant_block32_2t(const float* v, uint8_t* dst_hi, uint8_t* dst_lo, uint32_t* s_hi,
+                                                 uint32_t* s_lo) {
+  *s_hi = quant_block32(v, dst_hi);
+  const float sc = e8m0_f32(*s_hi);
+  const uint4* c = reinterpret_cast<const uint4*>(dst_hi);
+  const uint4 c0 = c[0], c1 = c[1];
+  const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  float r[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) r[i] = v[i] - e4m3_val((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * sc;
+  *s_lo = quant_block32(r, dst_lo);
+}
+
+// x [T, H] bf16 -> xq [TERMS*T, H] E4M3 + xs [TERMS*T, H/32] E8M0 (two
+// terms: row 2t holds the first term of token t, row 2t+1 the second); one
+// thread per 32-block.
+template <int TERMS>
 __global__ void __launch_bounds__(256) quant_x_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ xq,
-                                                      uint8_t* __restrict__ xs, int64_t nblocks) {
+                                                      uint8_t* __restrict__ xs, int64_t nblocks, int bpr) {
   const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nblocks) return;
   const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
@@ -113,11 +140,20 @@ __global__ void __launch_bounds__(256) quant_x_kernel(const uint16_t* __restrict
       v[8 * q + 2 * j + 1] = bf16_hi(a[j]);
     }
   }
-  xs[b] = (uint8_t)quant_block32(v, xq + b * 32);
+  if constexpr (TERMS == 1) {
+    xs[b] = (uint8_t)quant_block32(v, xq + b * 32);
+  } else {
+    const int64_t t = b / bpr, c = b % bpr;   // token, block within the row
+    const int64_t b0 = (2 * t) * bpr + c, b1 = b0 + bpr;
+    uint32_t s0, s1;
+    quant_block32_2t(v, xq + b0 * 32, xq + b1 * 32, &s0, &s1);
+    xs[b0] = (uint8_t)s0;
+    xs[b1] = (uint8_t)s1;
+  }
 }
 
 // Tile geometry of the expert GEMM (below).
-constexpr int BG_BM = 256;                    // pair rows per tile
+constexpr int BG_BM = 256;                    // A rows per tile (pair rows x activation terms)
 constexpr int BG_BN = 256;                    // weight rows per tile
 constexpr int BG_ASZ = BG_BM * 128;           // A bytes per step
 constexpr int BG_STG = BG_ASZ + BG_BN * 64;   // A + B bytes per step
@@ -147,7 +183,7 @@ constexpr int BG_HSTR = 33;                   // row stride (floats) of the h st
 __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                            int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                                            int32_t* __restrict__ work_a, int n_nt_a,
-                                                           int32_t* __restrict__ work_b, int n_nt_b) {
+                                                           int32_t* __restrict__ work_b, int n_nt_b, int chunk) {
   // Workgroup b writes expert b's entries; every workgroup first forms the
   // exclusive prefix sum of the per-expert tile counts (E <= 1024): wave scans
   // of 64 lanes, then a scan of the wave totals.
@@ -155,7 +191,7 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
   __shared__ int32_t s_start, s_mt;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, eb = blockIdx.x;
   const int cnt = (t < E) ? offsets[t + 1] - offsets[t] : 0;
-  const int mt_own = (cnt + BG_BM - 1) / BG_BM;
+  const int mt_own = (cnt + chunk - 1) / chunk;
   int incl = mt_own;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -175,7 +211,7 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
   const int st = s_start, mt = s_mt, o0 = offsets[eb];
   for (int i = t; i < mt; i += blockDim.x) {
     tiles[2 * (st + i)] = eb;
-    tiles[2 * (st + i) + 1] = o0 + i * BG_BM;
+    tiles[2 * (st + i) + 1] = o0 + i * chunk;
   }
   for (int j = t; j < mt * n_nt_a; j += blockDim.x) work_a[st * n_nt_a + j] = (st + j % mt) | ((j / mt) << 20);
   for (int j = t; j < mt * n_nt_b; j += blockDim.x) work_b[st * n_nt_b + j] = (st + j % mt) | ((j / mt) << 20);
@@ -242,7 +278,7 @@ __device__ __forceinline__ uint32_t bg_lds_addr(const uint8_t* p) {
 //   B: weight row n (64 B) at n*64, chunk c at 16*(c ^ ((n >> 1) & 3))
 //   (both measured free of bank conflicts for the operand reads on gfx950)
 //   scales: row r of a group at r*16 (12 bytes used), byte 4*j + g for step j, block g.
-template <int MODE>
+template <int MODE, int TERMS>
 __global__ void __launch_bounds__(512, 1) mx_gemm256_kernel(GemmArgs ga) {
   // LDS: three operand stages, then two scale-group buffers (A rows, B rows each)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * BG_STG + 4 * BG_SCL];
@@ -258,7 +294,9 @@ __global__ void __launch_bounds__(512, 1) mx_gemm256_kernel(GemmArgs ga) {
   const int tile = item & 0xFFFFF, ntile = item >> 20;
   const int e = ga.tiles[2 * tile], m0 = ga.tiles[2 * tile + 1];
   const int m_lim = ga.offsets[e + 1];
-  const int nv = (m_lim - m0 < BG_BM) ? m_lim - m0 : BG_BM;  // valid rows of this tile
+  constexpr int BMP = BG_BM / TERMS;  // pair rows per tile
+  const int nvp = (m_lim - m0 < BMP) ? m_lim - m0 : BMP;  // valid pair rows of this tile
+  const int nv = nvp * TERMS;                              // valid A rows
   const int K = (MODE == GM_GATEUP) ? ga.H : ga.I;
   const int nks = K / GM_BK;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
@@ -272,10 +310,16 @@ __global__ void __launch_bounds__(512, 1) mx_gemm256_kernel(GemmArgs ga) {
   const bg_i32x4_t rAs = bg_rsrc(ga.as, ga.a_bytes / 32);
   const bg_i32x4_t rB = bg_rsrc(rec, L.bytes);
 
-  // activation row of tile row r (valid rows only)
+  // activation row of tile row r (valid rows only); with two terms, tile
+  // rows 2i and 2i+1 are the first and second term of pair row i
   auto arow = [&](int r) -> int {
-    const int m = m0 + r;
-    return (MODE == GM_GATEUP) ? ga.perm[m] / ga.k : m;
+    if constexpr (TERMS == 1) {
+      const int m = m0 + r;
+      return (MODE == GM_GATEUP) ? ga.perm[m] / ga.k : m;
+    } else {
+      const int m = m0 + (r >> 1);
+      return 2 * ((MODE == GM_GATEUP) ? ga.perm[m] / ga.k : m) + (r & 1);
+    }
   };
   // tile weight row n -> matrix, row within it
   auto wmat = [&](int n) { return (MODE == GM_GATEUP) ? (n < 128 ? 0 : 1) : 2; };
@@ -457,7 +501,10 @@ __global__ void __launch_bounds__(512, 1) mx_gemm256_kernel(GemmArgs ga) {
   if (MODE == GM_GATEUP) {
     // two MX blocks of h per row: h columns 64 wn + 32 hb .. + 31 of the
     // tile's 128 (gate sub-tiles 2hb, 2hb+1 with up sub-tiles 4+2hb, 5+2hb);
-    // staged per wave in LDS so that lane l quantises wave row l
+    // staged per wave in LDS so that lane l quantises wave row l (with two
+    // terms, the pair row's value is the sum of its two tile rows, and lanes
+    // 0-31 quantise the wave's 32 pair rows, into two term rows each)
+    constexpr int WR = 64 / TERMS;  // pair rows per wave
     float* sh = reinterpret_cast<float*>(smem) + wv * (BG_BM / 4) * BG_HSTR;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -466,20 +513,37 @@ __global__ void __launch_bounds__(512, 1) mx_gemm256_kernel(GemmArgs ga) {
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float gv = acc[i][2 * hb + ss][k], uv = acc[i][4 + 2 * hb + ss][k];
-            sh[(16 * i + 4 * g + k) * BG_HSTR + 16 * ss + c16] = gv / (1.0f + expf(-gv)) * uv;
+          for (int k = 0; k < 4 / TERMS; ++k) {
+            float gv, uv;
+            if constexpr (TERMS == 1) {
+              gv = acc[i][2 * hb + ss][k];
+              uv = acc[i][4 + 2 * hb + ss][k];
+            } else {
+              gv = acc[i][2 * hb + ss][2 * k] + acc[i][2 * hb + ss][2 * k + 1];
+              uv = acc[i][4 + 2 * hb + ss][2 * k] + acc[i][4 + 2 * hb + ss][2 * k + 1];
+            }
+            sh[(WR / 4 * i + 4 / TERMS * g + k) * BG_HSTR + 16 * ss + c16] = gv / (1.0f + expf(-gv)) * uv;
           }
       __syncthreads();
-      const int tr = 16 * (wm + 4 * (lane >> 4)) + (lane & 15);
-      if (tr < nv) {
+      // wave pair row l -> tile pair row (16 / TERMS) (wm + 4 (l / (16 / TERMS))) + l % (16 / TERMS)
+      constexpr int RB = 16 / TERMS;
+      const int tr = RB * (wm + 4 * (lane / RB)) + (lane % RB);
+      if (lane < WR && tr < nvp) {
         float v[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) v[i] = sh[lane * BG_HSTR + i];
         const int m = m0 + tr;
         const int i0 = ntile * 128 + 64 * wn + 32 * hb;
-        const uint32_t sb = quant_block32(v, ga.hq + (int64_t)m * ga.I + i0);
-        ga.hs[(int64_t)m * (ga.I / 32) + i0 / 32] = (uint8_t)sb;
+        if constexpr (TERMS == 1) {
+          const uint32_t sb = quant_block32(v, ga.hq + (int64_t)m * ga.I + i0);
+          ga.hs[(int64_t)m * (ga.I / 32) + i0 / 32] = (uint8_t)sb;
+        } else {
+          uint32_t s0, s1;
+          quant_block32_2t(v, ga.hq + (int64_t)(2 * m) * ga.I + i0, ga.hq + (int64_t)(2 * m + 1) * ga.I + i0, &s0,
+                           &s1);
+          ga.hs[(int64_t)(2 * m) * (ga.I / 32) + i0 / 32] = (uint8_t)s0;
+          ga.hs[(int64_t)(2 * m + 1) * (ga.I / 32) + i0 / 32] = (uint8_t)s1;
+        }
       }
       __syncthreads();
     }
@@ -488,12 +552,15 @@ __global__ void __launch_bounds__(512, 1) mx_gemm256_kernel(GemmArgs ga) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int tr = 16 * (wm + 4 * i) + 4 * g + k;
-        if (tr < nv) {
+      for (int k = 0; k < 4 / TERMS; ++k) {
+        const int tr = (16 / TERMS) * (wm + 4 * i) + (4 / TERMS) * g + k;  // tile pair row
+        if (tr < nvp) {
           __bf16* yr = yb + (int64_t)(m0 + tr) * ga.H;
 #pragma unroll
-          for (int s = 0; s < 8; ++s) yr[nB(s)] = (__bf16)acc[i][s][k];
+          for (int s = 0; s < 8; ++s) {
+            const float yv = (TERMS == 1) ? acc[i][s][k] : acc[i][s][2 * k] + acc[i][s][2 * k + 1];
+            yr[nB(s)] = (__bf16)yv;
+          }
         }
       }
   }
@@ -516,10 +583,17 @@ hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
   const int32_t* pos = reinterpret_cast<const int32_t*>(ws + pl.off_pos);
 
   const int64_t nblk = (int64_t)T * H / 32;
-  quant_x_kernel<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(reinterpret_cast<const uint16_t*>(x), xq, xs, nblk);
+  const bool two = pl.terms == 2;
+  if (two)
+    quant_x_kernel<2><<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(reinterpret_cast<const uint16_t*>(x), xq, xs,
+                                                                      nblk, H / 32);
+  else
+    quant_x_kernel<1><<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(reinterpret_cast<const uint16_t*>(x), xq, xs,
+                                                                      nblk, H / 32);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  build_tiles_kernel<<<E, 1024, 0, st>>>(offsets, E, tiles, n_tiles, work_a, I / 128, work_b, H / 256);
+  build_tiles_kernel<<<E, 1024, 0, st>>>(offsets, E, tiles, n_tiles, work_a, I / 128, work_b, H / 256,
+                                         BG_BM / pl.terms);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   GemmArgs ga{};
@@ -536,30 +610,34 @@ hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
   // gate/up: A = x_q gathered by token, N = I in 128-column tiles (gate + up rows)
   ga.aq = xq;
   ga.as = xs;
-  ga.a_bytes = (int64_t)T * H;
+  ga.a_bytes = (int64_t)pl.terms * T * H;
   ga.hq = hq;
   ga.hs = hs;
   ga.n_ntiles = I / 128;
   ga.work = work_a;
   // the grid covers the most items possible; surplus workgroups exit at once
-  mx_gemm256_kernel<GM_GATEUP><<<(unsigned)((pl.max_tiles * ga.n_ntiles + 7) / 8 * 8), 512, 0, st>>>(ga);
+  const unsigned grid_a = (unsigned)((pl.max_tiles * ga.n_ntiles + 7) / 8 * 8);
+  if (two) mx_gemm256_kernel<GM_GATEUP, 2><<<grid_a, 512, 0, st>>>(ga);
+  else mx_gemm256_kernel<GM_GATEUP, 1><<<grid_a, 512, 0, st>>>(ga);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // down: A = h_q by sorted position, N = H in 256-row tiles
   ga.aq = hq;
   ga.as = hs;
-  ga.a_bytes = (int64_t)pl.P * I;
+  ga.a_bytes = (int64_t)pl.terms * pl.P * I;
   ga.y = y;
   ga.n_ntiles = H / 256;
   ga.work = work_b;
-  mx_gemm256_kernel<GM_DOWN><<<(unsigned)((pl.max_tiles * ga.n_ntiles + 7) / 8 * 8), 512, 0, st>>>(ga);
+  const unsigned grid_b = (unsigned)((pl.max_tiles * ga.n_ntiles + 7) / 8 * 8);
+  if (two) mx_gemm256_kernel<GM_DOWN, 2><<<grid_b, 512, 0, st>>>(ga);
+  else mx_gemm256_kernel<GM_DOWN, 1><<<grid_b, 512, 0, st>>>(ga);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   return launch_combine(pl, pos, gates, out, ws, st);
 }
 
 bool mfma_supported(const ft_moe_desc& d, int T) {
   return d.w_dtype == FT_MXFP4 && d.act_dtype == FT_BF16 && T >= MFMA_MIN_TOKENS && d.hidden % 256 == 0 &&
-         d.inter % 128 == 0 && (int64_t)T * d.hidden < (1ll << 31) &&
-         (int64_t)T * d.top_k * d.inter < (1ll << 31) &&
+         d.inter % 128 == 0 && (int64_t)2 * T * d.hidden < (1ll << 31) &&
+         (int64_t)2 * T * d.top_k * d.inter < (1ll << 31) &&
          record_layout(d.hidden, d.inter, FT_MXFP4).bytes < (1ll << 31);
 }
 

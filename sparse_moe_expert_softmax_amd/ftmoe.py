@@ -30,7 +30,7 @@ class Desc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
                 ("router_dtype", ctypes.c_int32), ("renormalize", ctypes.c_int32),
-                ("expert_stride", ctypes.c_int64)]
+                ("expert_stride", ctypes.c_int64), ("act_terms", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class PrefillPipelineState(ctypes.Structure):
@@ -103,11 +103,11 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def make_desc(cfg: MoEConfig, expert_stride: int = None) -> Desc:
+def make_desc(cfg: MoEConfig, expert_stride: int = None, act_terms: int = 0) -> Desc:
     from .synth import record_stride
     stride = record_stride(cfg.hidden, cfg.inter, cfg.w_dtype) if expert_stride is None else expert_stride
     return Desc(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.act_dtype, cfg.w_dtype, cfg.router_dtype,
-                1 if cfg.renormalize else 0, stride)
+                1 if cfg.renormalize else 0, stride, act_terms, 0)
 
 
 def ft_record_bytes(hidden: int, inter: int, w_dtype: int) -> int:

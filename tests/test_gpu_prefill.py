@@ -1,17 +1,23 @@
 """GPU parity of the prefill path (MXFP4 weights on scaled MFMA, activations
-quantised to MXFP8) against the fp64 oracle with the same storage precisions
-mirrored (OCP MX rule for x before gate/up and for h before down; expert
-outputs y rounded to bf16 before the combine).
+carried as MXFP8) against the fp64 oracle, in both activation modes: two
+MXFP8 terms (the default) and one.
+
+Each output is compared with the oracle that mirrors the kernels' storage
+precisions (OCP MX rule, one or two terms, for x before gate/up and for h
+before down; expert outputs y rounded to bf16 before the combine) and, in
+the two-term mode, also with the oracle on the exact bf16 activations and
+fp64 h (no mirroring).
 
 Bars: routing ids bit-exact for every token; gates within 1e-6; outputs within
-max relative error 1e-2."""
+max relative error 1e-2 of the mirrored oracle, and in the two-term mode also
+of the unmirrored one."""
 import numpy as np
 import pytest
 import torch
 
 from gpu_util import LayerData, dev, max_rel_err
 from oracle.moe import experts_forward_by_expert, to_f64
-from oracle.mx import bf16_round_f32, mxfp8_quantize, mxfp8_quantize_f32
+from oracle.mx import bf16_round_f32, mxfp8_quantize, mxfp8_quantize_f32, mxfp8_two_term, mxfp8_two_term_f32
 from oracle.record import decode_record
 from sparse_moe_expert_softmax_amd import ftmoe, synth
 from sparse_moe_expert_softmax_amd.configs import BF16, C4, MXFP4, MoEConfig
@@ -22,8 +28,16 @@ SMALL = MoEConfig("prefill_small_mxfp4", 90, hidden=256, inter=256, n_experts=8,
                   router_dtype=BF16, w_dtype=MXFP4, n_layers=1)
 
 
-def run_prefill(cfg, T, layer, step, sample=None, mask=None):
+def mirror(terms):
+    """The oracle's quantisation hooks for the kernels' activation mode."""
+    if terms == 1:
+        return dict(x_quant=mxfp8_quantize, h_quant=mxfp8_quantize_f32, y_quant=bf16_round_f32)
+    return dict(x_quant=mxfp8_two_term, h_quant=mxfp8_two_term_f32, y_quant=bf16_round_f32)
+
+
+def run_prefill(cfg, T, layer, step, sample=None, mask=None, terms=2):
     ld = LayerData(cfg, layer, step, T)
+    ld.desc.act_terms = terms
     ids, gates, logits = ld.gpu_route()
     torch.cuda.synchronize()
     o_ids, o_gates, _ = ld.oracle_route()
@@ -33,19 +47,23 @@ def run_prefill(cfg, T, layer, step, sample=None, mask=None):
     need = sorted(set(int(e) for t in rows for e in o_ids[t]))
     ld.build_pool(need)
     out = ld.gpu_forward(ids, gates, mask=mask).cpu().numpy()
-    ref, _, _ = ld.oracle_layer(mask=mask, tokens=list(rows), x_quant=mxfp8_quantize, h_quant=mxfp8_quantize_f32,
-                                y_quant=bf16_round_f32)
+    ref, _, _ = ld.oracle_layer(mask=mask, tokens=list(rows), **mirror(terms))
     rows = list(rows)
     err = max_rel_err(out[rows], ref[rows])
     assert not np.isnan(out[rows]).any()
     assert err <= 1e-2, f"max rel err {err:.3g}"
+    if terms == 2:
+        exact, _, _ = ld.oracle_layer(mask=mask, tokens=rows)
+        e2 = max_rel_err(out[rows], exact[rows])
+        assert e2 <= 1e-2, f"max rel err {e2:.3g} against bf16 x and fp64 h"
     return ld, ids, gates, out, ref, err
 
 
+@pytest.mark.parametrize("terms", [2, 1])
 @pytest.mark.parametrize("T", [256, 300, 1031])
-def test_prefill_small_layer_all_outputs(T):
-    print(f"prefill small T={T}", flush=True)
-    _, _, _, _, _, err = run_prefill(SMALL, T, 0, T)
+def test_prefill_small_layer_all_outputs(T, terms):
+    print(f"prefill small T={T} terms={terms}", flush=True)
+    _, _, _, _, _, err = run_prefill(SMALL, T, 0, T, terms=terms)
     print(f"  max rel err {err:.3g}")
 
 
@@ -60,11 +78,12 @@ def test_prefill_small_layer_partition_masks():
     assert np.array_equal(again, out)  # deterministic
 
 
-def test_prefill_full_chunk_routing_and_sampled_outputs():
+@pytest.mark.parametrize("terms", [2, 1])
+def test_prefill_full_chunk_routing_and_sampled_outputs(terms):
     cfg, T = C4, 8192
-    print("prefill 8192 tokens, full layer shape", flush=True)
+    print(f"prefill 8192 tokens, full layer shape, terms={terms}", flush=True)
     sample = [0, 1234, 5000, 8191]
-    _, _, _, _, _, err = run_prefill(cfg, T, 2, 0, sample=sample)
+    _, _, _, _, _, err = run_prefill(cfg, T, 2, 0, sample=sample, terms=terms)
     print(f"  sampled max rel err {err:.3g}")
 
 
@@ -72,12 +91,13 @@ MID = MoEConfig("prefill_mid_mxfp4", 91, hidden=512, inter=384, n_experts=16, to
                 router_dtype=BF16, w_dtype=MXFP4, n_layers=1)
 
 
-def test_prefill_k_tails_and_several_weight_tiles():
+@pytest.mark.parametrize("terms", [2, 1])
+def test_prefill_k_tails_and_several_weight_tiles(terms):
     """H 512 (four 128-K steps: one full group of three plus a tail), I 384
     (three steps, no tail), two gate/up and two down weight tiles, ragged
     expert row counts over 777 tokens."""
-    print("prefill mid T=777", flush=True)
-    _, _, _, _, _, err = run_prefill(MID, 777, 0, 3)
+    print(f"prefill mid T=777 terms={terms}", flush=True)
+    _, _, _, _, _, err = run_prefill(MID, 777, 0, 3, terms=terms)
     print(f"  max rel err {err:.3g}")
 
 
@@ -137,6 +157,7 @@ def test_prefill_sparse_experts_and_k_tails():
     scale group and a tail of five), five gate/up and three down weight tiles."""
     print("prefill sparse T=300", flush=True)
     _, ids, _, _, _, err = run_prefill(SPARSE, 300, 0, 17)
+    run_prefill(SPARSE, 300, 0, 17, terms=1)
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=SPARSE.n_experts)
     assert counts.min() == 0 and counts.max() < 16, (counts.min(), counts.max())
     print(f"  max rel err {err:.3g}")
@@ -152,6 +173,7 @@ def test_prefill_experts_spanning_several_row_chunks():
     128-K step (I 128)."""
     print("prefill fat T=1100", flush=True)
     ld, ids, _, _, _, err = run_prefill(FAT, 1100, 0, 19)
+    run_prefill(FAT, 1100, 0, 19, terms=1)
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=2)
     assert counts.min() > 512, counts
     print(f"  rows per expert {counts.tolist()}, max rel err {err:.3g}")
@@ -188,14 +210,14 @@ def _cover_all_experts(o_ids, E, seed):
 def test_prefill_full_chunks_outputs_cover_every_expert():
     """The 284B-like MXFP4 layer (4,096 / 2,048 / 256 experts / top-6) with
     every expert resident, as one 8,192-token chunk and as the 16,384-token
-    prompt in two such chunks.  Routing (the bounded router) bit-exact on
-    every token of both chunks; outputs against the oracle (same storage
-    precisions mirrored) on tokens chosen so that together they use all 256
-    experts (chunk 1), and on 8 tokens of chunk 2, run on the same pool and
-    workspace.  Also reported: the error of 12 of chunk 1's sampled outputs
-    against the oracle without the MXFP8 activation quantisation (bf16 x,
-    fp64 h), bounded at 0.1: the matrix cores take x and h as E4M3 with 3
-    mantissa bits, which costs about 5-6% of the output range."""
+    prompt in two such chunks, activations as two MXFP8 terms.  Routing (the
+    bounded router) bit-exact on every token of both chunks; outputs on
+    tokens chosen so that together they use all 256 experts (chunk 1), and
+    on 8 tokens of chunk 2, run on the same pool and workspace, against the
+    oracle with the two-term storage mirrored and against the oracle on the
+    exact bf16 x and fp64 h.  Chunk 1 also runs with one MXFP8 term, against
+    its mirrored oracle; its error against the exact one is reported (one
+    term keeps 3 mantissa bits: about 5-6% of the output range)."""
     cfg, T, layer = C4, 8192, 2
     ld = LayerData(cfg, layer, 0, T)
     print("prefill full chunks: generating 256 expert records on the device", flush=True)
@@ -203,19 +225,24 @@ def test_prefill_full_chunks_outputs_cover_every_expert():
     fws = torch.empty(ftmoe.ft_moe_workspace_bytes(ld.desc, T), dtype=torch.uint8, device="cuda")
     chunks = [ld.x, synth.activations(cfg, 1, layer, T)]
     w64 = to_f64(ld.wr, cfg.router_dtype)
+    from oracle.moe import route
     results = []
     for c, x in enumerate(chunks):
         ids, gates = _route_bounded(ld, x)
         out = torch.empty((T, cfg.hidden), dtype=torch.float32, device="cuda")
         ftmoe.ft_moe_forward(ld.desc, dev(x), ids, gates, pool, out, fws)
+        out1 = None
+        if c == 0:  # one MXFP8 term
+            d1 = ftmoe.make_desc(cfg, ld.stride, act_terms=1)
+            out1 = torch.empty((T, cfg.hidden), dtype=torch.float32, device="cuda")
+            ftmoe.ft_moe_forward(d1, dev(x), ids, gates, pool, out1, fws)
         torch.cuda.synchronize()
         x64 = to_f64(x, cfg.act_dtype)
-        from oracle.moe import route
         o_ids, o_gates, _ = route(x64, w64, cfg.top_k)
         np.testing.assert_array_equal(ids.cpu().numpy(), o_ids)
         np.testing.assert_allclose(gates.cpu().numpy(), o_gates, rtol=0, atol=1e-6)
         print(f"  chunk {c + 1}: routing bit-exact on all {T} tokens", flush=True)
-        results.append((x64, o_ids, o_gates, out.cpu().numpy()))
+        results.append((x64, o_ids, o_gates, out.cpu().numpy(), None if out1 is None else out1.cpu().numpy()))
     rows1 = _cover_all_experts(results[0][1], cfg.n_experts, 41)
     rows2 = sorted(np.random.default_rng(42).choice(T, 8, replace=False).tolist())
     print(f"  chunk 1: {len(rows1)} tokens cover all {cfg.n_experts} experts", flush=True)
@@ -224,17 +251,22 @@ def test_prefill_full_chunks_outputs_cover_every_expert():
         return decode_record(pool[e].cpu().numpy(), cfg.hidden, cfg.inter, cfg.w_dtype)
 
     for c, rows in ((0, rows1), (1, rows2)):
-        x64, o_ids, o_gates, out = results[c]
-        ref = experts_forward_by_expert(x64, o_ids, o_gates, expert, rows, x_quant=mxfp8_quantize,
-                                        h_quant=mxfp8_quantize_f32, y_quant=bf16_round_f32)
+        x64, o_ids, o_gates, out, out1 = results[c]
         assert not np.isnan(out[rows]).any()
+        ref = experts_forward_by_expert(x64, o_ids, o_gates, expert, rows, **mirror(2))
         err = max_rel_err(out[rows], ref[rows])
-        print(f"  chunk {c + 1}: max rel err {err:.3g} on {len(rows)} tokens (mirrored precisions)", flush=True)
-        assert err <= 1e-2, f"chunk {c + 1}: max rel err {err:.3g}"
-        if c == 0:
-            few = rows[:12]
-            exact = experts_forward_by_expert(x64, o_ids, o_gates, expert, few)
-            dev_err = max_rel_err(out[few], exact[few])
-            print(f"  chunk 1: max rel err {dev_err:.3g} on {len(few)} tokens against bf16 x and fp64 h "
-                  "(no MXFP8 mirroring)", flush=True)
-            assert dev_err <= 0.1
+        print(f"  chunk {c + 1}: max rel err {err:.3g} on {len(rows)} tokens (two terms, mirrored)", flush=True)
+        assert err <= 1e-2
+        few = rows if c == 1 else rows[:24]
+        exact = experts_forward_by_expert(x64, o_ids, o_gates, expert, few)
+        e2 = max_rel_err(out[few], exact[few])
+        print(f"  chunk {c + 1}: max rel err {e2:.3g} on {len(few)} tokens against bf16 x and fp64 h", flush=True)
+        assert e2 <= 1e-2
+        if out1 is not None:
+            few1 = rows[:24]
+            r1 = experts_forward_by_expert(x64, o_ids, o_gates, expert, few1, **mirror(1))
+            e1 = max_rel_err(out1[few1], r1[few1])
+            d1 = max_rel_err(out1[few1], exact[few1])
+            print(f"  chunk 1, one term: max rel err {e1:.3g} mirrored, {d1:.3g} against bf16 x and fp64 h",
+                  flush=True)
+            assert e1 <= 1e-2 and d1 <= 0.1

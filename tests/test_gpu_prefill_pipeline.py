@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from gpu_util import LayerData, dev, max_rel_err
-from oracle.mx import bf16_round_f32, mxfp8_quantize, mxfp8_quantize_f32
+from oracle.mx import bf16_round_f32, mxfp8_two_term, mxfp8_two_term_f32
 from sparse_moe_expert_softmax_amd import ftmoe, synth
 from sparse_moe_expert_softmax_amd.configs import BF16, MXFP4, MoEConfig
 from sparse_moe_expert_softmax_amd.prefill_pipeline import PrefillPipeline
@@ -61,7 +61,7 @@ def test_pipeline_layers_match_oracle_and_a_corrupted_record_shows(cfg, T):
     mx = cfg.w_dtype == MXFP4
     for l, ld in enumerate(lds):
         ld._records = {e: host[l][e].numpy() for e in range(cfg.n_experts)}
-        q = dict(x_quant=mxfp8_quantize, h_quant=mxfp8_quantize_f32, y_quant=bf16_round_f32) if mx else {}
+        q = dict(x_quant=mxfp8_two_term, h_quant=mxfp8_two_term_f32, y_quant=bf16_round_f32) if mx else {}
         ref, o_ids, o_gates = ld.oracle_layer(**q)
         np.testing.assert_array_equal(ids[l], o_ids)
         np.testing.assert_allclose(gates[l], o_gates, rtol=0, atol=1e-6)

@@ -64,6 +64,8 @@ def test_host_forward_matches_oracle_with_masks(cfg, T):
     assert _max_rel(a + b, full) <= 1e-6
     # one thread gives the same bits: every sum runs in a fixed order
     assert np.array_equal(_host(cfg, x, ids, gates, recs, threads=1), full)
+    # the portable loops (negative thread count) agree with the SIMD ones
+    assert _max_rel(_host(cfg, x, ids, gates, recs, threads=-2), full) <= 1e-6
 
 
 def test_host_forward_reads_only_the_kept_experts_and_repeats_add():

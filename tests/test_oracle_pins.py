@@ -154,6 +154,32 @@ def test_mxfp8_zero_block_and_ties():
     assert q[0] == 256.0 and q[1] == 16.0 and q[2] == 20.0
 
 
+def test_mxfp8_two_term_is_the_value_plus_its_quantised_residual():
+    """Two terms: q1 is the one-term result; the second term is the one-term
+    quantisation of v - q1 (so it sits on its own block's E4M3 grid).  Each
+    term loses at most 1/8 of its block's largest magnitude (saturation at
+    448 of a block scaled up to just under 512, or half a step of 3
+    mantissa bits), so the sum is within 2^-6 of the block's largest
+    magnitude; it is exact when v is already on the first term's grid."""
+    g = np.random.default_rng(33)
+    v = formats.bf16_bits_to_f64(synth.f32_to_bf16_bits(g.standard_normal(32 * 50).astype(np.float32)))
+    two = mx.mxfp8_two_term(v)
+    q1 = mx.mxfp8_quantize(v)
+    r = v - q1
+    np.testing.assert_array_equal(two - q1, mx.mxfp8_quantize(r))
+    assert np.all(r.astype(np.float32).astype(np.float64) == r)   # the residual of a bf16 value is exact in fp32
+    for b in range(0, v.size, 32):
+        amax = np.abs(v[b:b + 32]).max()
+        assert np.abs(v[b:b + 32] - two[b:b + 32]).max() <= 2.0 ** -6 * amax
+    err1 = np.abs(v - q1).max() / np.abs(v).max()
+    err2 = np.abs(v - two).max() / np.abs(v).max()
+    assert err2 < err1 / 8
+    exact = mx.mxfp8_quantize(g.standard_normal(64))
+    np.testing.assert_array_equal(mx.mxfp8_two_term(exact), exact)
+    h = g.standard_normal(64) * 3
+    np.testing.assert_array_equal(mx.mxfp8_two_term_f32(h), mx.mxfp8_two_term(h.astype(np.float32).astype(np.float64)))
+
+
 def test_bf16_round_matches_torch_including_ties_and_subnormals():
     """The oracle's bf16 rounding of y (8 significant bits, ties to even) against
     torch's fp32 -> bfloat16 conversion: random values over many binades, exact

@@ -37,13 +37,15 @@ HBM_PEAK_GBS = 8000.0
 # plain 256 MiB device copy (FETCH_SIZE x 1.9997, WRITE_SIZE x 1.0).  Keyed by the
 # SHA-256 prefix of the kernel source the counters were taken on: any change to
 # that source reports null until the counters are taken again.
-DECODE_TRAFFIC = {"f556c2820f43b052": 75864238}
+DECODE_TRAFFIC = {"2a6d2b43498392c5": 75904234}
 DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_expert_softmax_amd", "csrc",
                           "decode_mfma.hip")
 # The same for the prefill workload (MXFP4, H4096, E256, top-6, 8,192 tokens):
-# every kernel of one ft_moe_forward call, keyed by the prefixes of the three
-# sources those kernels come from.
-PREFILL_TRAFFIC = {}
+# every kernel of one ft_moe_forward call, keyed by the activation terms of
+# the matrix-core path and the prefixes of the three sources those kernels
+# come from.
+PREFILL_TRAFFIC = {(2, "47e208f8e14a584b", "8564bd36b3d79a3c", "6d20609b6838d49c"): 5693658445,
+                   (1, "47e208f8e14a584b", "8564bd36b3d79a3c", "6d20609b6838d49c"): 4990215799}
 PREFILL_SRCS = [os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "csrc", f)
                 for f in ("mfma.hip", "permute.hip", "gemv.hip")]
 

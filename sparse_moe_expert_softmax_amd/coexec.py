@@ -11,8 +11,10 @@ section, decode passage; architecture guide, decode passage).
 
 Per layer, on one stream: route; residency probe of the selected ids; one
 host synchronisation to read the ids, gates and residency; the host picks
-the set C of missed experts it will compute (the highest-numbered
-round(q * misses) of them); the lookup runs on the ids with C's entries set
+the set C of missed experts it will compute (round(q * misses) of them:
+those selected least often so far, so that
+rarely used experts are computed in place and do not displace frequently
+used ones from the cache); the lookup runs on the ids with C's entries set
 to -1 (so C takes no slot and evicts nothing); the device copies the
 remaining misses from pinned host memory (ft_expert_fetch) and runs the
 forward on every selected expert except C (mask); meanwhile the host runs
@@ -89,6 +91,7 @@ class CoExecStep:
         self.h_lk = torch.empty((L, T, k), dtype=torch.int32, pin_memory=True)
         self.h_mask = torch.empty((L, (E + 31) // 32), dtype=torch.int32, pin_memory=True)
         self.h_out = torch.empty((T, H), dtype=torch.float32, pin_memory=True)
+        self.uses = np.zeros((L, E), dtype=np.int64)   # selections per (layer, expert) seen by this step
         self.host_sets = [[] for _ in range(L)]
         self.uploaded = [[] for _ in range(L)]
         self.host_ms = 0.0
@@ -140,9 +143,15 @@ class CoExecStep:
             self.h_x.copy_(x[l].view(self.h_x.dtype), non_blocking=True)
             st.synchronize()
             ids_h = self.h_ids.numpy()
+            sel = np.unique(ids_h[(ids_h >= 0) & (ids_h < E)])
+            self.uses[l, sel] += 1
             miss = sorted(set(int(e) for e in ids_h[self.h_res.numpy() == 0]))
             n_c = int(round(q * len(miss)))
-            C = miss[len(miss) - n_c:] if n_c else []
+            # the host takes the misses selected least often so far (ties:
+            # higher id): rarely used experts are computed in place and do not
+            # displace the cache's frequently used ones
+            by_use = sorted(miss, key=lambda e: (self.uses[l, e], -e))
+            C = sorted(by_use[:n_c])
             self.host_sets[l] = C
             self.uploaded[l] = [e for e in miss if e not in C]
             lk = ids_h.copy()

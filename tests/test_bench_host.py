@@ -62,5 +62,5 @@ def test_traffic_tables_are_keyed_by_source_hashes():
         assert 1.0 <= d / 75_509_760 <= 1.05
     for terms in (1, 2):
         p = bench.measured_prefill_traffic("prefill_mxfp4_h4096_e256", 8192, terms)
-        if p is not None:  # at least the weights, activations and outputs; at most 1.5x the minimum
-            assert 1.0 <= p / 3_620_000_000 <= 1.5
+        if p is not None:  # at least the weights, activations and outputs; the intermediates on top
+            assert 1.0 <= p / 3_620_000_000 <= 1.7

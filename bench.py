@@ -100,6 +100,9 @@ def parse():
     ap.add_argument("--coexec", action="store_true",
                     help="LRU decode: co-execution (a measured share of each layer's misses computed on the host, "
                          "the rest fetched on the device), against the graph-captured device-fetch step")
+    ap.add_argument("--lookahead", action="store_true",
+                    help="LRU decode routed by the routers on layer-to-layer drifting inputs: the graph-captured "
+                         "step with and without look-ahead prefetch of the next layer's predicted experts")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -315,6 +318,8 @@ def main():
         return run_prefill(args, cfg, torch)
     if args.policy_study:
         return run_policy_study(args, cfg, torch)
+    if cfg.name == "decode_mxfp4_h4096_e256_lru" and args.lookahead:
+        return run_decode_lookahead(args, cfg, torch)
     if cfg.name == "decode_mxfp4_h4096_e256_lru" and args.coexec:
         return run_decode_coexec(args, cfg, torch)
     if cfg.name == "decode_mxfp4_h4096_e256_lru":
@@ -1016,6 +1021,86 @@ def run_decode_coexec(args, cfg, torch):
     res["coexec"] = c
     res["device_fetch_graph"] = f
     res["speedup_vs_device_fetch"] = round(f["ms_per_step"] / c["ms_per_step"], 4)
+    print(json.dumps(res), flush=True)
+
+
+def run_decode_lookahead(args, cfg, torch):
+    """MXFP4 decode through the global LRU pool (43 layers, 2,752 slots), routed
+    by the layers' own routers on inputs that drift from layer to layer with
+    correlation alpha (synth.layer_correlated_activations), batch B.  For
+    each alpha, the graph-captured step without and with look-ahead prefetch
+    (the next layer's router on this layer's input predicts its experts,
+    which are copied on a side stream while this layer computes), each from
+    a cold cache: step time, misses of the real lookups, predicted experts
+    copied and the share of them the next layer used."""
+    from sparse_moe_expert_softmax_amd import ftmoe, synth
+    from sparse_moe_expert_softmax_amd.lookahead import LookaheadStep
+    L = args.layers or cfg.n_layers
+    B = args.batch
+    H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
+    S = int(cfg.pool_fraction * E * L)
+    stride = synth.record_stride(H, I, cfg.w_dtype)
+    rec = synth.record_bytes(H, I, cfg.w_dtype)
+    desc = ftmoe.make_desc(cfg, stride)
+    NH = max(1, min(args.host_layers, L))
+    n_steps = args.warmup + args.steps
+    host = []
+    for h in range(NH):
+        d_ = _fp4_layer_pool(cfg, h, torch, stride)
+        hb = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
+        hb.copy_(d_)
+        host.append(hb)
+        del d_
+    src_dev = [torch.tensor([host[h][e].data_ptr() for e in range(E)], dtype=torch.int64, device="cuda")
+               for h in range(NH)]
+    routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(L)]
+    results = {}
+    for alpha in (0.0, 0.9, 0.99):
+        xs = [torch.from_numpy(synth.layer_correlated_activations(cfg, s_, B, alpha).view(np.int16)).cuda()
+              for s_ in range(n_steps)]
+        for la in (False, True):
+            pool = torch.empty((S, stride), dtype=torch.uint8, device="cuda")
+            table = torch.zeros(ftmoe.ft_slot_table_bytes(L, E, S), dtype=torch.uint8, device="cuda")
+            ftmoe.ft_slot_table_init(table, L, E, S)
+            st = LookaheadStep(desc, L, B, table, S, pool, rec, routers, [src_dev[l % NH] for l in range(L)],
+                               lookahead=la)
+            st.capture()
+            torch.cuda.synchronize()
+            step_ms, miss, pmiss, used, pred = [], 0, 0, 0, 0
+            for s_ in range(n_steps):
+                st.x.view(torch.int16).copy_(xs[s_])
+                t0 = time.perf_counter()
+                st.run()
+                torch.cuda.current_stream().synchronize()
+                if s_ >= args.warmup:
+                    step_ms.append((time.perf_counter() - t0) * 1e3)
+                    miss += int(st.mlist[:, 0].sum())
+                    if la:
+                        pmiss += int(st.pmlist[1:, 0].sum())
+                        ids = st.ids.cpu().numpy()
+                        pr = st.pred_ids.cpu().numpy()
+                        for l in range(1, L):
+                            p_ = set(pr[l].ravel().tolist())
+                            used += len(p_ & set(ids[l].ravel().tolist()))
+                            pred += len(p_)
+            nt = len(step_ms)
+            r = {"ms_per_step": round(float(np.mean(step_ms)), 3),
+                 "tokens_per_s": round(B * L / (np.mean(step_ms) * 1e-3), 1),
+                 "real_misses_per_step": round(miss / nt, 2)}
+            if la:
+                r.update({"prefetched_per_step": round(pmiss / nt, 2),
+                          "predicted_used_share": round(used / max(pred, 1), 4)})
+            results[f"alpha_{alpha}_{'lookahead' if la else 'plain'}"] = r
+            print(f"[bench] alpha {alpha} lookahead={la}: {r}", file=sys.stderr, flush=True)
+            del st, pool, table
+            torch.cuda.empty_cache()
+    main_r = results["alpha_0.9_lookahead"]
+    res = _base_result(args, main_r["tokens_per_s"], "tokens/s", main_r["ms_per_step"],
+                       {"workload": cfg.name + "_routed_drift", "batch": B, "layers": L, "experts": E, "top_k": k,
+                        "slots": S, "inputs": "layer-to-layer correlation alpha (0, 0.9, 0.99), routed by the "
+                                              "layers' routers", "host_layer_images": NH,
+                        "launch": "one HIP graph per step (two streams with look-ahead)"}, "bf16")
+    res["lookahead"] = results
     print(json.dumps(res), flush=True)
 
 

@@ -23,7 +23,7 @@ import numpy as np
 from .configs import F32, BF16, MXFP4, NVFP4, MoEConfig
 
 ENTROPY = 20260817
-KIND_EXPERT, KIND_ROUTER, KIND_ACT, KIND_TRACE, KIND_MASK, KIND_PERM = 0, 1, 2, 3, 4, 5
+KIND_EXPERT, KIND_ROUTER, KIND_ACT, KIND_TRACE, KIND_MASK, KIND_PERM, KIND_DRIFT = 0, 1, 2, 3, 4, 5, 6
 RECORD_ALIGN = 4096
 
 
@@ -213,6 +213,22 @@ def activations(cfg: MoEConfig, step: int, layer: int, n_tokens: int) -> np.ndar
     g = rng(cfg.cid, KIND_ACT, step, layer, n_tokens)
     x = g.standard_normal((n_tokens, cfg.hidden), dtype=np.float32)
     return _as_dtype(x, cfg.act_dtype)
+
+
+def layer_correlated_activations(cfg: MoEConfig, step: int, n_tokens: int, alpha: float) -> np.ndarray:
+    """[layers, n_tokens, hidden] router inputs that drift from layer to layer
+    like a residual stream: x_0 ~ N(0, 1), x_{l+1} = alpha x_l + sqrt(1 -
+    alpha^2) z_l with fresh z_l ~ N(0, 1) (so every layer's input stays
+    N(0, 1), and consecutive layers' inputs have correlation alpha), each
+    stored in the activation dtype.  alpha = 0 gives independent layers."""
+    L, H = cfg.n_layers, cfg.hidden
+    out = []
+    x = rng(cfg.cid, KIND_DRIFT, step, 0, n_tokens).standard_normal((n_tokens, H))
+    for l in range(L):
+        out.append(_as_dtype(x.astype(np.float32), cfg.act_dtype))
+        z = rng(cfg.cid, KIND_DRIFT, step, l + 1, n_tokens).standard_normal((n_tokens, H))
+        x = alpha * x + np.sqrt(1.0 - alpha * alpha) * z
+    return np.stack(out)
 
 
 # ------------------------------------------------------- trace and masks ----

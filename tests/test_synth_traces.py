@@ -35,3 +35,16 @@ def test_sticky_trace_keeps_about_p_of_the_experts():
     b = synth.sticky_trace(C3, 50, 1, 0.0)
     kept0 = np.mean([len(set(b[s, 0, 0]) & set(b[s + 1, 0, 0])) / C3.top_k for s in range(49)])
     assert kept0 < 0.5
+
+
+def test_layer_correlated_activations_have_the_stated_correlation():
+    from sparse_moe_expert_softmax_amd import synth
+    from sparse_moe_expert_softmax_amd.configs import C3
+    from oracle.formats import bf16_bits_to_f64
+    for alpha in (0.0, 0.9):
+        x = bf16_bits_to_f64(synth.layer_correlated_activations(C3, 0, 4, alpha))   # [43, 4, 4096]
+        a, b = x[:-1].ravel(), x[1:].ravel()
+        assert abs(np.corrcoef(a, b)[0, 1] - alpha) < 0.01
+        assert abs(x.std() - 1.0) < 0.01
+    same = synth.layer_correlated_activations(C3, 3, 2, 0.9)
+    assert np.array_equal(same, synth.layer_correlated_activations(C3, 3, 2, 0.9))

@@ -109,18 +109,13 @@ def parse():
 
 
 def device_pool_bf16(cfg, layer, torch):
-    """All expert records of one layer, generated on the device: bf16 values of
-    N(0, std) draws (torch's seeded generator), laid out as packed records."""
+    """All expert records of one bf16 layer, generated on the device: bf16
+    values of N(0, std) draws (torch's seeded generator), laid out as packed
+    records."""
     from sparse_moe_expert_softmax_amd import synth
     stride = synth.record_stride(cfg.hidden, cfg.inter, cfg.w_dtype)
-    n = 3 * cfg.hidden * cfg.inter
-    assert stride == 2 * n
-    g = torch.Generator(device="cuda")
-    g.manual_seed(synth.ENTROPY * 1000 + cfg.cid * 100 + layer)
-    w = torch.empty((cfg.n_experts, n), dtype=torch.bfloat16, device="cuda")
-    for e in range(cfg.n_experts):
-        w[e].copy_(torch.randn(n, generator=g, device="cuda", dtype=torch.float32).mul_(cfg.weight_std))
-    return w.view(torch.uint8).view(cfg.n_experts, stride)
+    assert stride == 2 * 3 * cfg.hidden * cfg.inter
+    return synth.device_layer_pool(torch, cfg, layer, stride)
 
 
 def _cpu_model():

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libftmoe.so")
 BUILD = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.cpp", "route.hip", "slot.hip", "permute.hip", "gemv.hip", "decode_mfma.hip", "mfma.hip", "noalloc.hip", "pipeline.cpp", "hostfwd.cpp"]
+SOURCES = ["api.cpp", "route.hip", "slot.hip", "permute.hip", "gemv.hip", "decode_mfma.hip", "mfma.hip", "prefill_bf16.hip", "noalloc.hip", "pipeline.cpp", "hostfwd.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

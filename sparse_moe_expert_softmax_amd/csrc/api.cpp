@@ -67,9 +67,11 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T) {
   p.I = d.inter;
   p.nb = (p.P + PERM_CHUNK - 1) / PERM_CHUNK;
   if (p.nb < 1) p.nb = 1;
-  p.mfma = mfma_supported(d, T);
+  const bool mx = mfma_supported(d, T), bf = !mx && mfma_bf16_supported(d, T);
+  p.mfma = mx || bf;
+  p.mfma_w = mx ? FT_MXFP4 : (bf ? FT_BF16 : -1);
   p.path = p.mfma ? PATH_MFMA : (dec_supported(d, T) ? PATH_DEC : PATH_GEMV);
-  p.terms = (d.act_terms == 1) ? 1 : 2;
+  p.terms = (mx && d.act_terms != 1) ? 2 : 1;
   p.max_tiles = p.P / (256 / p.terms) + p.E + 1;
   size_t o = 0;
   p.off_hist = o;    o = align256(o + sizeof(int32_t) * (size_t)p.nb * p.E);
@@ -78,9 +80,13 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T) {
   p.off_perm = o;    o = align256(o + sizeof(int32_t) * (size_t)p.P);
   p.off_pos = o;     o = align256(o + sizeof(int32_t) * (size_t)p.P);
   p.off_cnt = o;     o = align256(o + sizeof(uint32_t) * (size_t)(p.H / 16 + 1));
-  p.off_h = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.I);   // fp32 h, bf16 hi/lo, or MXFP8 codes
-  p.off_y = o;       o = align256(o + (p.mfma ? 2 : 4) * (size_t)p.P * p.H);  // bf16 y on the matrix-core path
-  if (p.mfma) {
+  p.off_h = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.I);   // fp32 h, bf16 (hi/lo), or MXFP8 codes
+  p.off_y = o;       o = align256(o + (p.mfma ? 2 : 4) * (size_t)p.P * p.H);  // bf16 y on the matrix-core paths
+  if (bf) {
+    p.off_xq = p.off_xs = p.off_hs = o;
+    p.off_tiles = o; o = align256(o + sizeof(int32_t) * ((size_t)2 * p.max_tiles + 1 +
+                                                          (size_t)p.max_tiles * (p.I / 128 + p.H / 256)));
+  } else if (mx) {
     p.off_xq = o;    o = align256(o + (size_t)p.terms * T * p.H);             // MXFP8 x codes (per term)
     p.off_xs = o;    o = align256(o + (size_t)p.terms * T * p.H / 32);        // and scales
     p.off_hs = o;    o = align256(o + (size_t)p.terms * p.P * p.I / 32);      // h scales (h codes: off_h)
@@ -267,7 +273,9 @@ int ft_moe_forward(const ft_moe_desc* desc, const void* x, int32_t n_tokens, con
   }
   e = ft::launch_permute(pl, topk_ids, expert_mask, ws, st);
   if (e != hipSuccess) return hip_fail(e, "permute launch");
-  if (pl.mfma)
+  if (pl.mfma && pl.mfma_w == FT_BF16)
+    e = ft::launch_mfma_bf16_forward(*desc, pl, x, slot_ids, pool_base, topk_gates, out, ws, st);
+  else if (pl.mfma)
     e = ft::launch_mfma_forward(*desc, pl, x, slot_ids, pool_base, topk_gates, out, ws, st);
   else
     e = ft::launch_gemv_forward(*desc, pl, x, slot_ids, pool_base, topk_gates, out, ws, st);

@@ -43,8 +43,9 @@ constexpr int DEC_MAX_PAIRS = 64;  // decode path: T*k pairs grouped inside the 
 struct FwdPlan {
   int T, P, E, H, I, nb;       // tokens, pairs, experts, hidden, inter, permute blocks
   int path;                    // FwdPath
-  bool mfma;                   // large-batch MXFP4 path on scaled MFMA
-  int terms;                   // MXFP8 terms per activation on that path (1 or 2)
+  bool mfma;                   // large-batch matrix-core path (PATH_MFMA)
+  int mfma_w;                  // its weight format: FT_MXFP4 (scaled MFMA) or FT_BF16 (bf16 MFMA)
+  int terms;                   // MXFP8 terms per activation on the MXFP4 path (1 or 2); 1 on the bf16 path
   size_t off_hist, off_offsets, off_active, off_perm, off_pos, off_h, off_y, off_xq, off_xs, off_hs, off_cnt;
   size_t off_tiles;            // MFMA path: tile list (2 ints per tile) + count
   int max_tiles;               // upper bound of (expert, row chunk) tiles: P/(256/terms) + E + 1
@@ -79,9 +80,14 @@ hipError_t launch_permute(const FwdPlan& pl, const int32_t* ids, const uint32_t*
 hipError_t launch_gemv_forward(const ft_moe_desc& d, const FwdPlan& pl, const void* x, const int32_t* slot_ids,
                                const void* pool, const float* gates, float* out, char* ws, hipStream_t st);
 
-// large-batch MXFP4 path on gfx950 scaled MFMA
+// large-batch paths on gfx950 matrix cores: MXFP4 weights on the scaled
+// fp8 x fp4 MFMA, bf16 weights on the bf16 MFMA
 constexpr int MFMA_MIN_TOKENS = 256;
 bool mfma_supported(const ft_moe_desc& d, int T);
+bool mfma_bf16_supported(const ft_moe_desc& d, int T);
+// tile list and work items of the grouped GEMMs (one workgroup per expert)
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int32_t* tiles, int32_t* n_tiles, int32_t* work_a,
+                              int n_nt_a, int32_t* work_b, int n_nt_b, int chunk, hipStream_t st);
 // out += part over n floats
 hipError_t launch_add_partial(float* out, const float* part, int64_t n, hipStream_t st);
 // fixed-j-order fp32 combine over the bf16 expert outputs y [P, H] at off_y
@@ -89,6 +95,8 @@ hipError_t launch_combine(const FwdPlan& pl, const int32_t* pos, const float* ga
                           hipStream_t st);
 hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const void* x, const int32_t* slot_ids,
                                const void* pool, const float* gates, float* out, char* ws, hipStream_t st);
+hipError_t launch_mfma_bf16_forward(const ft_moe_desc& d, const FwdPlan& pl, const void* x, const int32_t* slot_ids,
+                                    const void* pool, const float* gates, float* out, char* ws, hipStream_t st);
 
 constexpr int PERM_CHUNK = 1024;  // pairs per permute block (one per thread)
 

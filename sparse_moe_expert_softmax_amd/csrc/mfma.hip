@@ -33,6 +33,7 @@
 // The combine (fixed j order, fp32) runs as its own kernel afterwards.
 #include "common.hpp"
 #include "internal.hpp"
+#include "lds_dma.hpp"
 
 namespace ft {
 
@@ -160,18 +161,6 @@ constexpr int BG_STG = BG_ASZ + BG_BN * 64;   // A + B bytes per step
 constexpr int BG_SCL = BG_BM * 16;            // bytes of one scale group of A (or B): 16-byte row slots
 constexpr int BG_HSTR = 33;                   // row stride (floats) of the h staging tile
 
-// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt at their no-wait maxima)
-#define BG_VMWAIT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
-// A workgroup barrier without the memory fence that __syncthreads() carries:
-// the fence would wait for every LDS-DMA load in flight.  The empty asm keeps
-// the compiler from moving memory accesses across it.
-#define BG_BARRIER()                          \
-  do {                                        \
-    asm volatile("" ::: "memory");            \
-    __builtin_amdgcn_s_barrier();             \
-    asm volatile("" ::: "memory");            \
-  } while (0)
-
 // ------------------------------------------------------------ tile list --
 // tiles[2*i] = expert, tiles[2*i+1] = first row (sorted position) of tile i
 // (chunks of up to BG_BM rows);
@@ -217,11 +206,14 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
   for (int j = t; j < mt * n_nt_b; j += blockDim.x) work_b[st * n_nt_b + j] = (st + j % mt) | ((j / mt) << 20);
 }
 
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int32_t* tiles, int32_t* n_tiles, int32_t* work_a,
+                              int n_nt_a, int32_t* work_b, int n_nt_b, int chunk, hipStream_t st) {
+  build_tiles_kernel<<<E, 1024, 0, st>>>(offsets, E, tiles, n_tiles, work_a, n_nt_a, work_b, n_nt_b, chunk);
+  return hipGetLastError();
+}
+
 // -------------------------------------------------------------- the GEMM --
 enum { GM_GATEUP = 0, GM_DOWN = 1 };
-
-// Buffer descriptor word 3 for untyped 32-bit accesses on gfx9-family parts.
-constexpr int GM_RSRC_WORD3 = 0x00020000;
 
 struct GemmArgs {
   const uint8_t* aq;       // A codes: x_q [T, K] (gate/up) or h_q [P, K] (down)
@@ -240,29 +232,6 @@ struct GemmArgs {
   int64_t a_bytes;         // size of the A code array (< 2^31)
   int H, I, k, n_ntiles;
 };
-
-typedef int bg_i32x4_t __attribute__((ext_vector_type(4)));
-
-// Buffer load of 16 (or 12) bytes per lane straight into LDS: lane l's bytes
-// land at lds + size * l.  Written as inline asm so that the compiler does not
-// add its own waits for these loads (its LDS-DMA tracking falls back to
-// waiting for all of them before any LDS read); the kernel waits for them
-// explicitly before each barrier.
-__device__ __forceinline__ void bg_dma16(bg_i32x4_t rsrc, uint32_t lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void bg_dma12(bg_i32x4_t rsrc, uint32_t lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx3 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ bg_i32x4_t bg_rsrc(const void* base, int64_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  return (bg_i32x4_t){(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xFFFFu), (int)bytes, GM_RSRC_WORD3};
-}
-__device__ __forceinline__ uint32_t bg_lds_addr(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
-}
 
 // A workgroup of eight waves computes up to 256 pair rows (one expert's rows,
 // or a 256-row chunk of them) x 256 weight rows; K advances 128 per step.
@@ -303,12 +272,15 @@ __global__ void __launch_bounds__(512, 1) mx_gemm256_kernel(GemmArgs ga) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv & 3, wn = wv >> 2;
 
+  // a failed lookup (negative slot) reads no weights (a buffer of zero bytes
+  // returns zeros) and the down epilogue stores NaN for the expert's rows
   const int slot = ga.slot_ids ? ga.slot_ids[ga.perm[m0]] : e;
-  const uint8_t* rec = ga.pool + (int64_t)slot * ga.stride;
+  const bool poisoned = slot < 0;
+  const uint8_t* rec = ga.pool + (poisoned ? 0 : (int64_t)slot * ga.stride);
   const RecordLayout L = record_layout(ga.H, ga.I, FT_MXFP4);
   const bg_i32x4_t rA = bg_rsrc(ga.aq, ga.a_bytes);
   const bg_i32x4_t rAs = bg_rsrc(ga.as, ga.a_bytes / 32);
-  const bg_i32x4_t rB = bg_rsrc(rec, L.bytes);
+  const bg_i32x4_t rB = bg_rsrc(rec, poisoned ? 0 : L.bytes);
 
   // activation row of tile row r (valid rows only); with two terms, tile
   // rows 2i and 2i+1 are the first and second term of pair row i
@@ -559,7 +531,7 @@ __global__ void __launch_bounds__(512, 1) mx_gemm256_kernel(GemmArgs ga) {
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
             const float yv = (TERMS == 1) ? acc[i][s][k] : acc[i][s][2 * k] + acc[i][s][2 * k + 1];
-            yr[nB(s)] = (__bf16)yv;
+            yr[nB(s)] = (__bf16)(poisoned ? __builtin_nanf("") : yv);
           }
         }
       }
@@ -592,9 +564,9 @@ hipError_t launch_mfma_forward(const ft_moe_desc& d, const FwdPlan& pl, const vo
                                                                       nblk, H / 32);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  build_tiles_kernel<<<E, 1024, 0, st>>>(offsets, E, tiles, n_tiles, work_a, I / 128, work_b, H / 256,
-                                         BG_BM / pl.terms);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = launch_build_tiles(offsets, E, tiles, n_tiles, work_a, I / 128, work_b, H / 256, BG_BM / pl.terms,
+                                st)) != hipSuccess)
+    return err;
 
   GemmArgs ga{};
   ga.perm = perm;

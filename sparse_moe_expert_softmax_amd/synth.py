@@ -365,10 +365,21 @@ def device_record_fp4(torch, gen, H: int, I: int, std: float, w_dtype: int, stri
 
 
 def device_layer_pool(torch, cfg: MoEConfig, layer: int, stride: int):
-    """[E, stride] u8 device pool holding every expert record of one fp4 layer,
-    generated on the device from a generator seeded by (workload, layer)."""
+    """[E, stride] u8 device pool holding every expert record of one layer,
+    generated on the device from a generator seeded by (workload, layer).
+    bf16 layers: bf16 values (torch's nearest-even conversion) of N(0, std)
+    draws, gate, up and down back to back; fp4 layers: device_record_fp4."""
     g = torch.Generator(device="cuda")
     g.manual_seed(ENTROPY * 1000 + cfg.cid * 100 + layer)
+    if cfg.w_dtype == BF16:
+        n = 3 * cfg.hidden * cfg.inter
+        if stride < 2 * n:
+            raise ValueError("stride below the bf16 record size")
+        pool = torch.zeros((cfg.n_experts, stride), dtype=torch.uint8, device="cuda")
+        for e in range(cfg.n_experts):
+            w = torch.randn(n, generator=g, device="cuda", dtype=torch.float32).mul_(cfg.weight_std)
+            pool[e, : 2 * n].copy_(w.to(torch.bfloat16).view(torch.uint8))
+        return pool
     pool = torch.empty((cfg.n_experts, stride), dtype=torch.uint8, device="cuda")
     for e in range(cfg.n_experts):
         pool[e].copy_(device_record_fp4(torch, g, cfg.hidden, cfg.inter, cfg.weight_std, cfg.w_dtype, stride))

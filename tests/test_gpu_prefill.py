@@ -116,6 +116,23 @@ def test_prefill_slot_indirection_matches_identity_slots():
     assert np.array_equal(moved, out)
 
 
+def test_prefill_failed_lookup_poisons_only_its_tokens():
+    """A negative slot for one expert (a failed lookup) makes exactly the
+    tokens routed to it NaN, reads nothing for it, and leaves every other
+    token bitwise unchanged (both activation modes)."""
+    cfg, T = SMALL, 320
+    for terms in (2, 1):
+        ld, ids, gates, out, _, _ = run_prefill(cfg, T, 0, 9, terms=terms)
+        ids_np = ids.cpu().numpy()
+        slots = ids_np.astype(np.int32).copy()         # identity slots
+        victim = int(ids_np[0, 0])
+        slots[ids_np == victim] = -1
+        got = ld.gpu_forward(ids, gates, slot_ids=dev(slots)).cpu().numpy()
+        hit = (ids_np == victim).any(axis=1)
+        assert np.isnan(got[hit]).all(axis=1).all()
+        assert np.array_equal(got[~hit], out[~hit])
+
+
 def test_prefill_masked_out_experts_are_never_read():
     """Poison (NaN) the records of the masked-out experts: the masked output
     stays finite and equals the masked output over the intact pool."""

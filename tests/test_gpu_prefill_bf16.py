@@ -1,0 +1,195 @@
+"""GPU parity of the prefill path for bf16 expert weights (bf16 matrix cores:
+x and the weights enter exactly, fp32 accumulation, h rounded once to bf16
+before the down projection, each expert output y rounded to bf16 before the
+fp32 combine) against the fp64 oracle.
+
+Each output is compared with the oracle that rounds h and y the same way
+(mirrored) and with the oracle on fp64 h and y (unmirrored).  Bars: routing
+ids bit-exact for every token; gates within 1e-6; outputs within max
+relative error 1e-2 of both."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import LayerData, dev, max_rel_err
+from oracle.moe import experts_forward_by_expert, route, to_f64
+from oracle.mx import bf16_round_f32
+from oracle.record import decode_record
+from sparse_moe_expert_softmax_amd import ftmoe, synth
+from sparse_moe_expert_softmax_amd.configs import BF16, C2, MoEConfig
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+
+def _cfg(name, cid, H, I, E, k):
+    return MoEConfig(name, cid, hidden=H, inter=I, n_experts=E, top_k=k, act_dtype=BF16, router_dtype=BF16,
+                     w_dtype=BF16, n_layers=1)
+
+
+SMALL = _cfg("prefill_small_bf16", 130, 256, 256, 8, 2)
+MID = _cfg("prefill_mid_bf16", 131, 512, 384, 16, 4)
+SPARSE = _cfg("prefill_sparse_bf16", 132, 768, 640, 128, 2)
+FAT = _cfg("prefill_fat_bf16", 133, 256, 128, 2, 1)
+
+MIRROR = dict(h_quant=bf16_round_f32, y_quant=bf16_round_f32)
+
+
+def check_outputs(out, ld, rows, mask=None):
+    ref, _, _ = ld.oracle_layer(mask=mask, tokens=rows, **MIRROR)
+    exact, _, _ = ld.oracle_layer(mask=mask, tokens=rows)
+    assert not np.isnan(out[rows]).any()
+    err = max_rel_err(out[rows], ref[rows])
+    e2 = max_rel_err(out[rows], exact[rows])
+    assert err <= 1e-2, f"max rel err {err:.3g} (h, y rounded to bf16)"
+    assert e2 <= 1e-2, f"max rel err {e2:.3g} (fp64 h and y)"
+    return err, e2
+
+
+def run_prefill(cfg, T, layer, step, mask=None):
+    ld = LayerData(cfg, layer, step, T)
+    ids, gates, _ = ld.gpu_route()
+    torch.cuda.synchronize()
+    o_ids, o_gates, _ = ld.oracle_route()
+    np.testing.assert_array_equal(ids.cpu().numpy(), o_ids)
+    np.testing.assert_allclose(gates.cpu().numpy(), o_gates, rtol=0, atol=1e-6)
+    ld.build_pool(o_ids.ravel())
+    out = ld.gpu_forward(ids, gates, mask=mask).cpu().numpy()
+    err, e2 = check_outputs(out, ld, list(range(T)), mask=mask)
+    return ld, ids, gates, out, err, e2
+
+
+@pytest.mark.parametrize("T", [256, 300, 1031])
+def test_bf16_prefill_every_output(T):
+    """16 experts / top-4, H 512 (16 K steps of gate/up), I 384 (three
+    gate/up weight tiles, 12 K steps of down), two down weight tiles."""
+    print(f"bf16 prefill mid T={T}", flush=True)
+    _, _, _, _, err, e2 = run_prefill(MID, T, 0, 3)
+    print(f"  max rel err {err:.3g} mirrored, {e2:.3g} exact")
+
+
+def test_bf16_prefill_sparse_experts():
+    """128 experts for 600 pairs: experts without rows and with 1-13 rows
+    (most waves of a row chunk hold no valid row), five gate/up and three down
+    weight tiles."""
+    print("bf16 prefill sparse T=300", flush=True)
+    _, ids, _, _, err, _ = run_prefill(SPARSE, 300, 0, 17)
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=SPARSE.n_experts)
+    assert counts.min() == 0 and counts.max() < 16, (counts.min(), counts.max())
+    print(f"  max rel err {err:.3g}")
+
+
+def test_bf16_prefill_experts_spanning_several_row_chunks():
+    """Two experts, top-1, 1,100 tokens: each expert's rows span three
+    256-row chunks (the last one partial); down has four K steps (I 128)."""
+    print("bf16 prefill fat T=1100", flush=True)
+    _, ids, _, _, err, _ = run_prefill(FAT, 1100, 0, 19)
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=2)
+    assert counts.min() > 512, counts
+    print(f"  rows per expert {counts.tolist()}, max rel err {err:.3g}")
+
+
+def test_bf16_prefill_partition_masks():
+    """Each part of three 50/50 expert partitions against the oracle's masked
+    layer; the parts add up to the unmasked output within 1e-5 (fp32 sums in
+    another order)."""
+    cfg, T = SMALL, 400
+    ld, ids, gates, full, _, _ = run_prefill(cfg, T, 0, 5)
+    rng = np.random.default_rng(21)
+    for _ in range(3):
+        chosen = rng.choice(cfg.n_experts, cfg.n_experts // 2, replace=False)
+        m = np.array([sum(1 << int(e) for e in chosen)], dtype=np.uint32)
+        c = np.array([(~int(m[0])) & ((1 << cfg.n_experts) - 1)], dtype=np.uint32)
+        a = ld.gpu_forward(ids, gates, mask=m).cpu().numpy()
+        b = ld.gpu_forward(ids, gates, mask=c).cpu().numpy()
+        check_outputs(a, ld, list(range(T)), mask=m)
+        check_outputs(b, ld, list(range(T)), mask=c)
+        assert max_rel_err(a + b, full) <= 1e-5
+
+
+def test_bf16_prefill_slots_and_a_failed_lookup():
+    """Records moved to other slots give bitwise the same output; a negative
+    slot for one expert makes exactly the tokens routed to it NaN (nothing is
+    read for it) and leaves every other token bitwise unchanged."""
+    cfg, T = SMALL, 320
+    ld, ids, gates, out, _, _ = run_prefill(cfg, T, 0, 9)
+    E = cfg.n_experts
+    perm = np.random.default_rng(5).permutation(E)
+    pool2 = torch.full((E, ld.stride), 0xFF, dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        pool2[perm[e]].copy_(ld.pool[e])
+    ids_np = ids.cpu().numpy()
+    slots = perm[ids_np].astype(np.int32)
+    moved = ld.gpu_forward(ids, gates, slot_ids=dev(slots), pool=pool2).cpu().numpy()
+    assert np.array_equal(moved, out)
+    victim = int(ids_np[0, 0])
+    slots[ids_np == victim] = -1
+    got = ld.gpu_forward(ids, gates, slot_ids=dev(slots), pool=pool2).cpu().numpy()
+    hit = (ids_np == victim).any(axis=1)
+    assert np.isnan(got[hit]).all(axis=1).all()
+    assert np.array_equal(got[~hit], out[~hit])
+
+
+def test_bf16_prefill_threshold():
+    """255 tokens take the general (fp32 GEMV) path, 256 the matrix cores;
+    both against the oracle."""
+    cfg = SMALL
+    ld = LayerData(cfg, 0, 13, 255)
+    ids, gates, _ = ld.gpu_route()
+    o_ids, _, _ = ld.oracle_route()
+    np.testing.assert_array_equal(ids.cpu().numpy(), o_ids)
+    ld.build_pool(o_ids.ravel())
+    out = ld.gpu_forward(ids, gates).cpu().numpy()
+    ref, _, _ = ld.oracle_layer()
+    assert max_rel_err(out, ref) <= 1e-2
+    run_prefill(cfg, 256, 0, 13)
+
+
+def _cover_all_experts(o_ids, E, seed):
+    order = np.random.default_rng(seed).permutation(o_ids.shape[0])
+    seen, rows = set(), []
+    for t in order:
+        new = set(int(e) for e in o_ids[t]) - seen
+        if new:
+            rows.append(int(t))
+            seen |= new
+        if len(seen) == E:
+            break
+    assert len(seen) == E
+    return sorted(rows)
+
+
+def test_bf16_prefill_full_chunk_covers_every_expert():
+    """The 35B-like bf16 layer (2,048 / 768 / 128 experts / top-8) with every
+    expert resident, one 8,192-token chunk (65,536 pairs): routing (the
+    bounded many-token router) bit-exact on every token; outputs on tokens
+    that together use all 128 experts, against the mirrored and the
+    unmirrored oracle."""
+    cfg, T, layer = C2, 8192, 1
+    ld = LayerData(cfg, layer, 0, T)
+    print("bf16 prefill full chunk: generating 128 expert records on the device", flush=True)
+    pool = synth.device_layer_pool(torch, cfg, layer, ld.stride)
+    ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, cfg.top_k), dtype=torch.float32, device="cuda")
+    rws = torch.empty(ftmoe.ft_route_workspace_bytes(ld.desc, T), dtype=torch.uint8, device="cuda")
+    ftmoe.ft_moe_route(ld.desc, dev(ld.x), dev(ld.wr), ids, gates, workspace=rws)
+    out = torch.empty((T, cfg.hidden), dtype=torch.float32, device="cuda")
+    fws = torch.empty(ftmoe.ft_moe_workspace_bytes(ld.desc, T), dtype=torch.uint8, device="cuda")
+    ftmoe.ft_moe_forward(ld.desc, dev(ld.x), ids, gates, pool, out, fws)
+    torch.cuda.synchronize()
+    x64 = to_f64(ld.x, cfg.act_dtype)
+    o_ids, o_gates, _ = route(x64, to_f64(ld.wr, cfg.router_dtype), cfg.top_k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), o_ids)
+    np.testing.assert_allclose(gates.cpu().numpy(), o_gates, rtol=0, atol=1e-6)
+    rows = _cover_all_experts(o_ids, cfg.n_experts, 43)
+    print(f"  routing bit-exact on all {T} tokens; {len(rows)} tokens cover all {cfg.n_experts} experts", flush=True)
+
+    def expert(e):
+        return decode_record(pool[e].cpu().numpy(), cfg.hidden, cfg.inter, cfg.w_dtype)
+
+    got = out.cpu().numpy()
+    assert not np.isnan(got[rows]).any()
+    ref = experts_forward_by_expert(x64, o_ids, o_gates, expert, rows, **MIRROR)
+    exact = experts_forward_by_expert(x64, o_ids, o_gates, expert, rows)
+    err, e2 = max_rel_err(got[rows], ref[rows]), max_rel_err(got[rows], exact[rows])
+    print(f"  max rel err {err:.3g} mirrored, {e2:.3g} exact", flush=True)
+    assert err <= 1e-2 and e2 <= 1e-2

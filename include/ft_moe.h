@@ -267,8 +267,12 @@ int ft_prefill_pipeline_layer(ft_prefill_pipeline* p, const void* const* next_la
  * A token may list an expert more than once; each listing adds its own term.
  * out: fp32 [T, H], fully overwritten; it must not overlap any input.
  * Decode-sized calls (few pairs per expert) run as bandwidth-bound grouped
- * GEMV; large MXFP4 calls run on gfx950 scaled MFMA with activations
- * quantised to MXFP8 (E4M3, E8M0 per 32) first.
+ * GEMV.  From 256 tokens on (bf16 activations, H a multiple of 256, I of
+ * 128), MXFP4 layers run on gfx950 scaled MFMA with x and h carried as
+ * MXFP8 (E4M3, E8M0 per 32; see act_terms), and bf16 layers on the bf16
+ * matrix cores with x exact and h rounded once to bf16; on both, each
+ * expert output is rounded to bf16 before the fp32 combine.  A negative
+ * slot (a failed lookup) reads nothing and makes its tokens' outputs NaN.
  * Errors: FT_EINVAL on nulls / sizes, FT_EUNSUPPORTED on dtype pairs,
  * FT_EWORKSPACE if ws_bytes < ft_moe_workspace_bytes(desc, T). */
 size_t ft_moe_workspace_bytes(const ft_moe_desc* desc, int32_t n_tokens);

@@ -40,14 +40,15 @@ HBM_PEAK_GBS = 8000.0
 DECODE_TRAFFIC = {"2a6d2b43498392c5": 75904234}
 DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_expert_softmax_amd", "csrc",
                           "decode_mfma.hip")
-# The same for the prefill workload (MXFP4, H4096, E256, top-6, 8,192 tokens):
-# every kernel of one ft_moe_forward call, keyed by the activation terms of
-# the matrix-core path and the prefixes of the three sources those kernels
-# come from.
-PREFILL_TRAFFIC = {(2, "47e208f8e14a584b", "8564bd36b3d79a3c", "6d20609b6838d49c"): 5693658445,
-                   (1, "47e208f8e14a584b", "8564bd36b3d79a3c", "6d20609b6838d49c"): 4990215799}
+# The same for the prefill workloads (8,192-token chunks: MXFP4 H4096 E256
+# top-6 in either activation mode, bf16 H2048 E128 top-8): every kernel of one
+# ft_moe_forward call, keyed by the workload, the activation terms of the
+# matrix-core path (1 for bf16 weights) and the prefixes of the sources those
+# kernels come from.
+PREFILL_TRAFFIC = {}
 PREFILL_SRCS = [os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "csrc", f)
-                for f in ("mfma.hip", "permute.hip", "gemv.hip")]
+                for f in ("mfma.hip", "prefill_bf16.hip", "lds_dma.hpp", "permute.hip", "gemv.hip")]
+PREFILL_WORKLOADS = ("prefill_mxfp4_h4096_e256", "prefill_bf16_h2048_e128")
 
 
 def measured_decode_traffic(cfg_name, batch):
@@ -61,13 +62,15 @@ def measured_decode_traffic(cfg_name, batch):
 
 def measured_prefill_traffic(cfg_name, chunk_tokens, terms=2):
     import hashlib
-    if cfg_name != "prefill_mxfp4_h4096_e256" or chunk_tokens != 8192:
+    if cfg_name not in PREFILL_WORKLOADS or chunk_tokens != 8192:
         return None
+    if cfg_name == "prefill_bf16_h2048_e128":
+        terms = 1
     key = []
     for p in PREFILL_SRCS:
         with open(p, "rb") as f:
             key.append(hashlib.sha256(f.read()).hexdigest()[:16])
-    return PREFILL_TRAFFIC.get((terms,) + tuple(key))
+    return PREFILL_TRAFFIC.get((cfg_name, terms) + tuple(key))
 
 
 def parse():
@@ -309,7 +312,7 @@ def main():
 
     cfg = CONFIGS[args.workload]
     torch.cuda.set_device(0)
-    if cfg.name == "prefill_mxfp4_h4096_e256":
+    if cfg.name in PREFILL_WORKLOADS:
         return run_prefill(args, cfg, torch)
     if args.policy_study:
         return run_policy_study(args, cfg, torch)
@@ -374,6 +377,7 @@ def main():
         del pools
         torch.cuda.empty_cache()
         res["prefill"] = prefill_figures(torch)
+        res["prefill_bf16"] = bf16_prefill_figures(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, B, args.cpu_seconds)
@@ -381,6 +385,7 @@ def main():
 
 
 MFMA_PEAK_TFLOPS = 5000.0   # dense fp8 rate; the f8 x f4 instruction issues at the fp8 rate
+BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix rate
 
 
 def _base_result(args, metric_value, unit, ms_per_step, config, dtype):
@@ -446,7 +451,7 @@ def run_policy_study(args, cfg, torch):
     print(json.dumps(res), flush=True)
 
 
-def _fp4_layer_pool(cfg, layer, torch, stride):
+def _layer_pool(cfg, layer, torch, stride):
     from sparse_moe_expert_softmax_amd import synth
     return synth.device_layer_pool(torch, cfg, layer, stride)
 
@@ -534,12 +539,51 @@ def prefill_figures(torch, n_meas=8):
     return res
 
 
-def run_prefill(args, cfg, torch):
-    """8,192-token chunks through the MXFP4 layers: compute with weights
-    resident, then the full pipeline where the next layer's whole expert set
-    is copied from pinned host memory on a side stream while the current
-    layer computes (two HBM layer buffers)."""
+def bf16_prefill_figures(torch, n_meas=8):
+    """The same for bf16 expert weights: one 8,192-token chunk through the
+    35B-like bf16 layer (2,048 / 768 / 128 experts / top-8) with its experts
+    resident, two layers generated on the device, alternated; bf16 matrix
+    cores, useful TFLOP/s against the dense bf16 rate."""
     from sparse_moe_expert_softmax_amd import ftmoe, synth
+    from sparse_moe_expert_softmax_amd.configs import C6
+    cfg, T = C6, 8192
+    H, I, k = cfg.hidden, cfg.inter, cfg.top_k
+    stride = synth.record_stride(H, I, cfg.w_dtype)
+    print("[bench] prefill figures: generating 2 bf16 layers on the device", file=sys.stderr, flush=True)
+    bufs = [synth.device_layer_pool(torch, cfg, l, stride) for l in range(2)]
+    routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(2)]
+    x = torch.from_numpy(synth.activations(cfg, 0, 0, T).view(np.int16)).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    desc = ftmoe.make_desc(cfg, stride)
+    ws = torch.empty(ftmoe.ft_moe_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+    rws = torch.empty(ftmoe.ft_route_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+    route_ms, fwd_ms = _prefill_resident_times(torch, desc, x, routers, bufs, ids, gates, out, ws, rws,
+                                               torch.cuda.current_stream(), 2, n_meas)
+    useful = 6.0 * T * k * H * I
+    tflops = useful / (float(np.mean(fwd_ms)) * 1e-3) / 1e12
+    t_layer = float(np.mean(route_ms + fwd_ms))
+    print(f"[bench] prefill (bf16 weights): route {route_ms.mean():.3f} ms, forward {fwd_ms.mean():.3f} ms per "
+          "layer", file=sys.stderr, flush=True)
+    res = {"workload": cfg.name, "tokens": T, "weights": "bf16 resident", "useful_flops_per_forward": useful,
+           "issued": "v_mfma_f32_16x16x32_bf16, bf16 activations x bf16 weights",
+           "tokens_per_s": round(T / (t_layer * 1e-3), 1),
+           "route_us": round(float(route_ms.mean()) * 1e3, 1), "forward_us": round(float(fwd_ms.mean()) * 1e3, 1),
+           "useful_tflops": round(tflops, 1), "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+           "traffic": measured_prefill_traffic(cfg.name, T)}
+    del bufs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_prefill(args, cfg, torch):
+    """8,192-token chunks through the MXFP4 or the bf16 layers: compute with
+    weights resident, then the full pipeline where the next layer's whole
+    expert set is copied from pinned host memory on a side stream while the
+    current layer computes (two HBM layer buffers)."""
+    from sparse_moe_expert_softmax_amd import ftmoe, synth
+    from sparse_moe_expert_softmax_amd.configs import BF16
     CH = 8192
     T = CH
     chunks = max(1, args.tokens // CH)
@@ -548,13 +592,15 @@ def run_prefill(args, cfg, torch):
     stride = synth.record_stride(H, I, cfg.w_dtype)
     rec = synth.record_bytes(H, I, cfg.w_dtype)
     layer_bytes = E * stride
-    desc = ftmoe.make_desc(cfg, stride, act_terms=args.act_terms)
+    bf = cfg.w_dtype == BF16
+    terms = 1 if bf else args.act_terms
+    desc = ftmoe.make_desc(cfg, stride, act_terms=0 if bf else args.act_terms)
     NH = max(1, min(args.host_layers, L))
     print(f"[bench] prefill: {L} layers, {chunks} chunk(s) of {CH}; {NH} pinned host layer images "
           f"of {layer_bytes / 1e9:.2f} GB", file=sys.stderr, flush=True)
     host = []
     for h in range(NH):
-        dev = _fp4_layer_pool(cfg, h, torch, stride)
+        dev = _layer_pool(cfg, h, torch, stride)
         hb = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
         hb.copy_(dev)
         host.append(hb)
@@ -624,11 +670,13 @@ def run_prefill(args, cfg, torch):
 
     useful = 6.0 * T * k * H * I  # gate/up 4*P*H*I + down 2*P*H*I
     tflops = useful / (float(np.mean(fwd_ms)) * 1e-3) / 1e12
+    peak = BF16_PEAK_TFLOPS if bf else MFMA_PEAK_TFLOPS
     res = _base_result(args, T / (t_layer * 1e-3), "tokens/s", t_layer * L,
                        {"workload": cfg.name, "tokens_per_chunk": CH, "chunks": chunks, "layers": L, "hidden": H,
-                        "experts": E, "top_k": k, "inter": I, "weights": "mxfp4",
-                        "activations": f"bf16, as {args.act_terms} MXFP8 term(s) for the matrix cores",
-                        "act_terms": args.act_terms}, "f8xf4 (f32 accumulate)")
+                        "experts": E, "top_k": k, "inter": I, "weights": "bf16" if bf else "mxfp4",
+                        "activations": "bf16, exact on the bf16 matrix cores; h rounded to bf16" if bf else
+                        f"bf16, as {terms} MXFP8 term(s) for the matrix cores",
+                        "act_terms": terms}, "bf16 (f32 accumulate)" if bf else "f8xf4 (f32 accumulate)")
     res["note"] = "value = tokens/s through one MoE layer with its experts resident (route + forward)"
     res["per_layer_ms"] = {"route": round(float(route_ms.mean()), 4), "forward": round(float(fwd_ms.mean()), 4)}
     res["pipeline"] = {"wall_ms": round(wall_ms, 2), "upload_ms_sum": round(copy_sum, 2),
@@ -638,11 +686,13 @@ def run_prefill(args, cfg, torch):
                        "host_link_gbs": round(upload_gbs, 2),
                        "tokens_per_s_end_to_end": round(T * chunks / (wall_ms * 1e-3), 1),
                        "host_layer_images": NH}
-    res["roofline"] = {"bound": "mfma", "kernel": "ft_moe_forward (grouped scaled-MFMA expert GEMM)",
-                       "achieved": round(tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                       "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
-                       "issued_frac": round(tflops * args.act_terms / MFMA_PEAK_TFLOPS, 4),
-                       "traffic": measured_prefill_traffic(cfg.name, CH, args.act_terms),
+    res["roofline"] = {"bound": "mfma",
+                       "kernel": "ft_moe_forward (grouped bf16-MFMA expert GEMM)" if bf else
+                       "ft_moe_forward (grouped scaled-MFMA expert GEMM)",
+                       "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                       "frac": round(tflops / peak, 4),
+                       "issued_frac": round(tflops * terms / peak, 4),
+                       "traffic": measured_prefill_traffic(cfg.name, CH, terms),
                        "flops_per_launch": useful, "avg_launch_us": round(float(np.mean(fwd_ms)) * 1e3, 1)}
     print(json.dumps(res), flush=True)
 
@@ -750,7 +800,7 @@ def run_decode_lru(args, cfg, torch):
           f"images, {n_steps} trace steps at batch {B}", file=sys.stderr, flush=True)
     host = []
     for h in range(NH):
-        dev = _fp4_layer_pool(cfg, h, torch, stride)
+        dev = _layer_pool(cfg, h, torch, stride)
         hb = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
         hb.copy_(dev)
         host.append(hb)

@@ -54,8 +54,8 @@ def test_traffic_tables_are_keyed_by_source_hashes():
     for key, v in bench.DECODE_TRAFFIC.items():
         assert len(key) == 16 and int(key, 16) >= 0 and v > 0
     for key, v in bench.PREFILL_TRAFFIC.items():
-        assert key[0] in (1, 2) and len(key) == len(bench.PREFILL_SRCS) + 1
-        assert all(len(h) == 16 for h in key[1:]) and v > 0
+        assert key[0] in bench.PREFILL_WORKLOADS and key[1] in (1, 2) and len(key) == len(bench.PREFILL_SRCS) + 2
+        assert all(len(h) == 16 for h in key[2:]) and v > 0
     # a figure, when reported, is within a few per cent of the workload's design bytes
     d = bench.measured_decode_traffic("decode_bf16_h2048_e128", 1)
     if d is not None:
@@ -64,3 +64,6 @@ def test_traffic_tables_are_keyed_by_source_hashes():
         p = bench.measured_prefill_traffic("prefill_mxfp4_h4096_e256", 8192, terms)
         if p is not None:  # at least the weights, activations and outputs; the intermediates on top
             assert 1.0 <= p / 3_620_000_000 <= 1.7
+    p = bench.measured_prefill_traffic("prefill_bf16_h2048_e128", 8192)
+    if p is not None:  # weights 1.208 GB, x 33.6 MB, out 67.1 MB; h and y on top
+        assert 1.0 <= p / 1_309_000_000 <= 1.7

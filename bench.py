@@ -45,7 +45,10 @@ DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_mo
 # ft_moe_forward call, keyed by the workload, the activation terms of the
 # matrix-core path (1 for bf16 weights) and the prefixes of the sources those
 # kernels come from.
-PREFILL_TRAFFIC = {}
+_PH = ("4db791fc00a312b7", "bf75881915902b28", "509e27cfdfa24281", "8564bd36b3d79a3c", "6d20609b6838d49c")
+PREFILL_TRAFFIC = {("prefill_mxfp4_h4096_e256", 2) + _PH: 5685784994,
+                   ("prefill_mxfp4_h4096_e256", 1) + _PH: 4990800130,
+                   ("prefill_bf16_h2048_e128", 1) + _PH: 2725676948}
 PREFILL_SRCS = [os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "csrc", f)
                 for f in ("mfma.hip", "prefill_bf16.hip", "lds_dma.hpp", "permute.hip", "gemv.hip")]
 PREFILL_WORKLOADS = ("prefill_mxfp4_h4096_e256", "prefill_bf16_h2048_e128")

@@ -65,5 +65,5 @@ def test_traffic_tables_are_keyed_by_source_hashes():
         if p is not None:  # at least the weights, activations and outputs; the intermediates on top
             assert 1.0 <= p / 3_620_000_000 <= 1.7
     p = bench.measured_prefill_traffic("prefill_bf16_h2048_e128", 8192)
-    if p is not None:  # weights 1.208 GB, x 33.6 MB, out 67.1 MB; h and y on top
-        assert 1.0 <= p / 1_309_000_000 <= 1.7
+    if p is not None:  # weights 1.208 GB, x 33.6 MB, out 67.1 MB, h and y written and read: 2.05 GB by design
+        assert 1.0 <= p / 2_046_000_000 <= 1.5

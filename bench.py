@@ -109,6 +109,8 @@ def parse():
     ap.add_argument("--lookahead", action="store_true",
                     help="LRU decode routed by the routers on layer-to-layer drifting inputs: the graph-captured "
                          "step with and without look-ahead prefetch of the next layer's predicted experts")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only the ceiling probes (streaming read, launch floor, matrix cores, LDS-DMA), one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -122,6 +124,74 @@ def device_pool_bf16(cfg, layer, torch):
     stride = synth.record_stride(cfg.hidden, cfg.inter, cfg.w_dtype)
     assert stride == 2 * 3 * cfg.hidden * cfg.inter
     return synth.device_layer_pool(torch, cfg, layer, stride)
+
+
+def ceilings(torch, reps=5):
+    """Achievable ceilings on this GPU, from the probe library (libftprobe.so,
+    not the MoE path): streaming reads from HBM (1 GiB), from the Infinity
+    Cache (64 MiB read again) and from L2 (2 MiB); back-to-back empty launches;
+    dense matrix-core loops (bf16, MXFP8 x MXFP4, MXFP4 x MXFP4); LDS-DMA from
+    an L2-resident buffer.  HIP events on the launch stream; median of reps."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "libftprobe.so"))
+    st = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(st.cuda_stream)
+    EV = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        fn()
+        ms = []
+        for _ in range(reps):
+            a, b = EV(), EV()
+            a.record(st)
+            fn()
+            b.record(st)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return float(np.median(ms))
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed ({rc})")
+
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    sptr = ctypes.c_void_p(sink.data_ptr())
+    res = {"source": "libftprobe.so (sparse_moe_expert_softmax_amd/csrc/probe.hip)"}
+    rd = {}
+    for name, nbytes, passes in (("hbm_1GiB", 1 << 30, 1), ("infinity_cache_64MiB", 64 << 20, 16),
+                                 ("l2_2MiB", 2 << 20, 256)):
+        buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        ms = timed(lambda: check(lib.ftp_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_int64(nbytes),
+                                                       ctypes.c_int32(passes), sptr, ctypes.c_int32(8192), sp)))
+        rd[name] = round(nbytes * passes / (ms * 1e-3) / 1e9, 1)
+        del buf
+    res["stream_read_gbs"] = rd
+    n = 200
+    ms = timed(lambda: check(lib.ftp_empty(ctypes.c_int32(n), sp)))
+    res["empty_launch_us"] = round(ms * 1e3 / n, 2)
+    mf = {}
+    grid = 1024
+    for kind, name, flop, iters, peak in ((0, "bf16_16x16x32", 16384, 4096, BF16_PEAK_TFLOPS),
+                                          (3, "bf16_32x32x16", 32768, 2048, BF16_PEAK_TFLOPS),
+                                          (1, "mxfp8_x_mxfp4_16x16x128", 65536, 2048, MFMA_PEAK_TFLOPS),
+                                          (4, "mxfp8_x_mxfp4_32x32x64", 131072, 1024, MFMA_PEAK_TFLOPS),
+                                          (2, "mxfp4_x_mxfp4_16x16x128", 65536, 2048, MXFP4_PEAK_TFLOPS),
+                                          (5, "mxfp4_x_mxfp4_32x32x64", 131072, 1024, MXFP4_PEAK_TFLOPS)):
+        ms = timed(lambda: check(lib.ftp_mfma(ctypes.c_int32(kind), sptr, ctypes.c_int32(grid), ctypes.c_int32(iters),
+                                              sp)))
+        tf = grid * 4 * iters * 8 * flop / (ms * 1e-3) / 1e12
+        mf[name] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4)}
+    res["mfma"] = mf
+    nb, grid, iters = 2 << 20, 1024, 512
+    buf = torch.ones(nb, dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: check(lib.ftp_lds_dma(ctypes.c_void_p(buf.data_ptr()), ctypes.c_int64(nb), sptr,
+                                             ctypes.c_int32(grid), ctypes.c_int32(iters), sp)))
+    moved = grid * 8 * iters * 4096
+    res["lds_dma_gbs"] = round(moved / (ms * 1e-3) / 1e9, 1)
+    res["lds_dma_gbs_per_cu"] = round(moved / (ms * 1e-3) / 1e9 / 256, 1)
+    del buf, sink
+    return res
 
 
 def _cpu_model():
@@ -315,6 +385,9 @@ def main():
 
     cfg = CONFIGS[args.workload]
     torch.cuda.set_device(0)
+    if args.ceilings:
+        print(json.dumps({"ceilings": ceilings(torch)}), flush=True)
+        return
     if cfg.name in PREFILL_WORKLOADS:
         return run_prefill(args, cfg, torch)
     if args.policy_study:
@@ -381,6 +454,7 @@ def main():
         torch.cuda.empty_cache()
         res["prefill"] = prefill_figures(torch)
         res["prefill_bf16"] = bf16_prefill_figures(torch)
+        res["ceilings"] = ceilings(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, B, args.cpu_seconds)

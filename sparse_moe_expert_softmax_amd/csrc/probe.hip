@@ -1,0 +1,214 @@
+// Ceiling probes on gfx950, for reading the hot path's measurements against
+// what this chip achieves rather than only against its published peaks:
+//  - a plain streaming read (HBM, or L2 / Infinity Cache for small buffers);
+//  - back-to-back empty kernels (the per-launch floor);
+//  - dense matrix-core loops, operands in registers, eight independent
+//    accumulators per wave: bf16 (v_mfma_f32_16x16x32_bf16 and
+//    v_mfma_f32_32x32x16_bf16), MXFP8 x MXFP4 and MXFP4 x MXFP4
+//    (v_mfma_scale_f32_16x16x128_f8f6f4 and _32x32x64_f8f6f4);
+//  - global -> LDS loads through the buffer unit (LDS-DMA) from an L2-resident
+//    buffer, the path the prefill GEMMs feed their operands through.
+// Not part of the MoE path: a separate library (libftprobe.so) that the
+// benchmark times with HIP events.  Each kernel writes its sink only when a
+// data-dependent value takes a value it never takes, so nothing is optimised
+// away and nothing is stored.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lds_dma.hpp"
+
+namespace {
+
+typedef __bf16 pbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float pf32x4_t __attribute__((ext_vector_type(4)));
+typedef int pi32x8_t __attribute__((ext_vector_type(8)));
+typedef float pf32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kUnroll = 4;  // 16-byte loads in flight per thread and pass
+
+__global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restrict__ p, int64_t n16, int passes,
+                                                          uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  for (int pass = 0; pass < passes; ++pass)
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += kUnroll * stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t j = i + u * stride;
+      v[u] = p[j < n16 ? j : n16 - 1];  // clamped: every load issues, the extra ones repeat the last line
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (i + u * stride < n16) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+__global__ void empty_kernel() {}
+
+__global__ void __launch_bounds__(256) mfma_bf16_kernel(float* __restrict__ sink, int iters) {
+  pbf16x8_t a, b;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    a[q] = (__bf16)(1e-3f * (float)((threadIdx.x + q) & 7));
+    b[q] = (__bf16)(1e-3f * (float)((threadIdx.x * 3 + q) & 7));
+  }
+  pf32x4_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = (pf32x4_t){0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  if (s == -1234.5f) sink[blockIdx.x] = s;
+}
+
+__global__ void __launch_bounds__(256) mfma_bf16_32_kernel(float* __restrict__ sink, int iters) {
+  pbf16x8_t a, b;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    a[q] = (__bf16)(1e-3f * (float)((threadIdx.x + q) & 7));
+    b[q] = (__bf16)(1e-3f * (float)((threadIdx.x * 3 + q) & 7));
+  }
+  pf32x16_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][7] + acc[i][15];
+  if (s == -1234.5f) sink[blockIdx.x] = s;
+}
+
+template <int A_FMT, int B_FMT>
+__global__ void __launch_bounds__(256) mfma_scaled_32_kernel(float* __restrict__ sink, int iters) {
+  pi32x8_t a, b;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    a[q] = (int)(0x38383838u ^ (threadIdx.x * 0x01010101u & 0x03030303u));
+    b[q] = (int)(0x22222222u ^ ((threadIdx.x + q) * 0x11111111u & 0x11111111u));
+  }
+  const int sa = 127, sb = 127;
+  pf32x16_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i], A_FMT, B_FMT, 0, sa, 0, sb);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][7] + acc[i][15];
+  if (s == -1234.5f) sink[blockIdx.x] = s;
+}
+
+// A_FMT / B_FMT: 0 = fp8 E4M3, 4 = fp4 E2M1 (the instruction's format codes)
+template <int A_FMT, int B_FMT>
+__global__ void __launch_bounds__(256) mfma_scaled_kernel(float* __restrict__ sink, int iters) {
+  pi32x8_t a, b;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    a[q] = (int)(0x38383838u ^ (threadIdx.x * 0x01010101u & 0x03030303u));
+    b[q] = (int)(0x22222222u ^ ((threadIdx.x + q) * 0x11111111u & 0x11111111u));
+  }
+  const int sa = 127, sb = 127;  // E8M0 scales of 1
+  pf32x4_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = (pf32x4_t){0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i], A_FMT, B_FMT, 0, sa, 0, sb);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  if (s == -1234.5f) sink[blockIdx.x] = s;
+}
+
+// Eight waves per workgroup; per iteration each wave moves four 1 KB slabs
+// (16 bytes per lane) from the buffer into its own 4 KB of LDS, with up to
+// two iterations of loads in flight.  The buffer is small enough to stay in
+// L2; the slab origins walk through it.
+__global__ void __launch_bounds__(512) lds_dma_kernel(const uint8_t* __restrict__ buf, int64_t bytes, int iters,
+                                                      uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[8 * 4096];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const ft::bg_i32x4_t rs = ft::bg_rsrc(buf, bytes);
+  const uint32_t l0 = ft::bg_lds_addr(smem) + 4096 * wv;
+  const int nslab = (int)(bytes / 4096);
+  int slab = (int)((blockIdx.x * 8 + wv) % nslab);
+  for (int it = 0; it < iters; ++it) {
+    const int so = slab * 4096;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ft::bg_dma16(rs, l0 + 1024 * t, 16 * lane + 1024 * t, so);
+    BG_VMWAIT(8);
+    slab = slab + 1 < nslab ? slab + 1 : 0;
+  }
+  BG_VMWAIT(0);
+  __syncthreads();
+  const uint32_t v = reinterpret_cast<const uint32_t*>(smem)[threadIdx.x];
+  if (v == 0x9E3779B9u) sink[blockIdx.x] = v;
+}
+
+int status(hipError_t e) { return e == hipSuccess ? 0 : -4; }
+
+}  // namespace
+
+extern "C" {
+
+// Read `bytes` (a multiple of 16, 16-byte aligned) `passes` times with `grid` workgroups of 256 threads.
+int ftp_stream_read(const void* buf, int64_t bytes, int32_t passes, uint32_t* sink, int32_t grid, void* stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 || grid < 1 || passes < 1) return -1;
+  stream_read_kernel<<<grid, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      reinterpret_cast<const uint4*>(buf), bytes / 16, passes, sink);
+  return status(hipGetLastError());
+}
+
+// n launches of an empty kernel (one workgroup of 64 threads each).
+int ftp_empty(int32_t n, void* stream) {
+  if (n < 0) return -1;
+  for (int i = 0; i < n; ++i) empty_kernel<<<1, 64, 0, reinterpret_cast<hipStream_t>(stream)>>>();
+  return status(hipGetLastError());
+}
+
+// Dense matrix-core loops: `grid` workgroups of 4 waves, each wave `iters` x 8
+// instructions.  kind 0: bf16 16x16x32 (16,384 FLOP each); 1: MXFP8 x MXFP4
+// 16x16x128 (65,536 FLOP); 2: MXFP4 x MXFP4 16x16x128 (65,536 FLOP);
+// 3: bf16 32x32x16 (32,768 FLOP); 4: MXFP8 x MXFP4 32x32x64 (131,072 FLOP);
+// 5: MXFP4 x MXFP4 32x32x64 (131,072 FLOP).  sink: grid floats.
+int ftp_mfma(int32_t kind, float* sink, int32_t grid, int32_t iters, void* stream) {
+  if (!sink || grid < 1 || iters < 1 || kind < 0 || kind > 5) return -1;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (kind == 0) mfma_bf16_kernel<<<grid, 256, 0, st>>>(sink, iters);
+  else if (kind == 1) mfma_scaled_kernel<0, 4><<<grid, 256, 0, st>>>(sink, iters);
+  else if (kind == 2) mfma_scaled_kernel<4, 4><<<grid, 256, 0, st>>>(sink, iters);
+  else if (kind == 3) mfma_bf16_32_kernel<<<grid, 256, 0, st>>>(sink, iters);
+  else if (kind == 4) mfma_scaled_32_kernel<0, 4><<<grid, 256, 0, st>>>(sink, iters);
+  else mfma_scaled_32_kernel<4, 4><<<grid, 256, 0, st>>>(sink, iters);
+  return status(hipGetLastError());
+}
+
+// LDS-DMA from an L2-resident buffer (a multiple of 4 KB): `grid`
+// workgroups of 8 waves, each wave 4 KB per iteration.  sink: grid words.
+int ftp_lds_dma(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, int32_t iters, void* stream) {
+  if (!buf || !sink || bytes < 4096 || bytes % 4096 || bytes >= (1ll << 31) || grid < 1 || iters < 1) return -1;
+  lds_dma_kernel<<<grid, 512, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      reinterpret_cast<const uint8_t*>(buf), bytes, iters, sink);
+  return status(hipGetLastError());
+}
+
+}  // extern "C"

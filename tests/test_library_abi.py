@@ -77,3 +77,20 @@ def test_prefill_pipeline_refuses_bad_state_without_gpu():
     rc = ftmoe.lib().ft_prefill_pipeline_layer(ctypes.byref(s), None, ctypes.byref(d), buf, 4, buf, buf, buf, buf,
                                                buf, 1 << 30)
     assert rc == ftmoe.FT_EINVAL and "not uploaded" in ftmoe.ft_last_error()
+
+
+def test_probe_library_exports_and_refuses_bad_arguments_without_gpu():
+    """The ceiling-probe library (benchmark only, not the MoE path) loads,
+    exports its four launchers, and refuses bad arguments before any launch."""
+    path = os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "libftprobe.so")
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    L = ctypes.CDLL(path)
+    for n in ("ftp_stream_read", "ftp_empty", "ftp_mfma", "ftp_lds_dma"):
+        assert hasattr(L, n), n
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    assert L.ftp_stream_read(p, ctypes.c_int64(8), ctypes.c_int32(1), p, ctypes.c_int32(1), None) == -1
+    assert L.ftp_empty(ctypes.c_int32(-1), None) == -1
+    assert L.ftp_mfma(ctypes.c_int32(6), p, ctypes.c_int32(1), ctypes.c_int32(1), None) == -1
+    assert L.ftp_lds_dma(p, ctypes.c_int64(100), p, ctypes.c_int32(1), ctypes.c_int32(1), None) == -1

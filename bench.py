@@ -128,10 +128,11 @@ def device_pool_bf16(cfg, layer, torch):
 
 def ceilings(torch, reps=5):
     """Achievable ceilings on this GPU, from the probe library (libftprobe.so,
-    not the MoE path): streaming reads from HBM (1 GiB), from the Infinity
-    Cache (64 MiB read again) and from L2 (2 MiB); back-to-back empty launches;
-    dense matrix-core loops (bf16, MXFP8 x MXFP4, MXFP4 x MXFP4); LDS-DMA from
-    an L2-resident buffer.  HIP events on the launch stream; median of reps."""
+    not the MoE path): streaming reads from HBM (1 GiB) and from the Infinity
+    Cache (64 MiB read again); back-to-back empty launches; dense matrix-core
+    loops (bf16, MXFP8 x MXFP4, MXFP4 x MXFP4, both instruction shapes);
+    LDS-DMA from an L2-resident 2 MiB buffer (the L2 -> LDS path).  HIP events
+    on the launch stream; median of reps."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "libftprobe.so"))
     st = torch.cuda.current_stream()
@@ -159,8 +160,7 @@ def ceilings(torch, reps=5):
     sptr = ctypes.c_void_p(sink.data_ptr())
     res = {"source": "libftprobe.so (sparse_moe_expert_softmax_amd/csrc/probe.hip)"}
     rd = {}
-    for name, nbytes, passes in (("hbm_1GiB", 1 << 30, 1), ("infinity_cache_64MiB", 64 << 20, 16),
-                                 ("l2_2MiB", 2 << 20, 256)):
+    for name, nbytes, passes in (("hbm_1GiB", 1 << 30, 1), ("infinity_cache_64MiB", 64 << 20, 16)):
         buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
         ms = timed(lambda: check(lib.ftp_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_int64(nbytes),
                                                        ctypes.c_int32(passes), sptr, ctypes.c_int32(8192), sp)))

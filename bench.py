@@ -787,7 +787,7 @@ def run_decode_resident_fp4(args, cfg, torch):
     desc = ftmoe.make_desc(cfg, stride)
     print(f"[bench] generating {L} NVFP4 layers ({L * E * stride / 1e9:.1f} GB) on the device", file=sys.stderr,
           flush=True)
-    pools = [_fp4_layer_pool(cfg, l, torch, stride) for l in range(L)]
+    pools = [_layer_pool(cfg, l, torch, stride) for l in range(L)]
     routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(L)]
     n_steps = args.warmup + args.steps
     xs = torch.stack([torch.stack([torch.from_numpy(synth.activations(cfg, s, l, B).view(np.int16))
@@ -1070,7 +1070,7 @@ def run_decode_coexec(args, cfg, torch):
           flush=True)
     host = []
     for h in range(NH):
-        d_ = _fp4_layer_pool(cfg, h, torch, stride)
+        d_ = _layer_pool(cfg, h, torch, stride)
         hb = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
         hb.copy_(d_)
         host.append(hb)
@@ -1168,7 +1168,7 @@ def run_decode_lookahead(args, cfg, torch):
     n_steps = args.warmup + args.steps
     host = []
     for h in range(NH):
-        d_ = _fp4_layer_pool(cfg, h, torch, stride)
+        d_ = _layer_pool(cfg, h, torch, stride)
         hb = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
         hb.copy_(d_)
         host.append(hb)

@@ -43,15 +43,22 @@ DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_mo
 # The same for the prefill workloads (8,192-token chunks: MXFP4 H4096 E256
 # top-6 in either activation mode, bf16 H2048 E128 top-8): every kernel of one
 # ft_moe_forward call, keyed by the workload, the activation terms of the
-# matrix-core path (1 for bf16 weights) and the prefixes of the sources those
-# kernels come from.
-_PH = ("4db791fc00a312b7", "bf75881915902b28", "509e27cfdfa24281", "8564bd36b3d79a3c", "6d20609b6838d49c")
-PREFILL_TRAFFIC = {("prefill_mxfp4_h4096_e256", 2) + _PH: 5685784994,
-                   ("prefill_mxfp4_h4096_e256", 1) + _PH: 4990800130,
-                   ("prefill_bf16_h2048_e128", 1) + _PH: 2725676948}
-PREFILL_SRCS = [os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "csrc", f)
-                for f in ("mfma.hip", "prefill_bf16.hip", "lds_dma.hpp", "permute.hip", "gemv.hip")]
-PREFILL_WORKLOADS = ("prefill_mxfp4_h4096_e256", "prefill_bf16_h2048_e128")
+# matrix-core path (1 for bf16 weights) and the prefixes of the sources the
+# workload's kernels come from.
+_CSRC = os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "csrc")
+PREFILL_SRCS = {
+    "prefill_mxfp4_h4096_e256": [os.path.join(_CSRC, f) for f in ("mfma.hip", "lds_dma.hpp", "permute.hip",
+                                                                   "gemv.hip")],
+    "prefill_bf16_h2048_e128": [os.path.join(_CSRC, f) for f in ("prefill_bf16.hip", "mfma.hip", "lds_dma.hpp",
+                                                                  "permute.hip", "gemv.hip")],
+}
+PREFILL_WORKLOADS = tuple(PREFILL_SRCS)
+PREFILL_TRAFFIC = {
+    ("prefill_mxfp4_h4096_e256", 2, "4db791fc00a312b7", "509e27cfdfa24281", "8564bd36b3d79a3c",
+     "6d20609b6838d49c"): 5685784994,
+    ("prefill_mxfp4_h4096_e256", 1, "4db791fc00a312b7", "509e27cfdfa24281", "8564bd36b3d79a3c",
+     "6d20609b6838d49c"): 4990800130,
+}
 
 
 def measured_decode_traffic(cfg_name, batch):
@@ -70,7 +77,7 @@ def measured_prefill_traffic(cfg_name, chunk_tokens, terms=2):
     if cfg_name == "prefill_bf16_h2048_e128":
         terms = 1
     key = []
-    for p in PREFILL_SRCS:
+    for p in PREFILL_SRCS[cfg_name]:
         with open(p, "rb") as f:
             key.append(hashlib.sha256(f.read()).hexdigest()[:16])
     return PREFILL_TRAFFIC.get((cfg_name, terms) + tuple(key))

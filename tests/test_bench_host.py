@@ -54,7 +54,8 @@ def test_traffic_tables_are_keyed_by_source_hashes():
     for key, v in bench.DECODE_TRAFFIC.items():
         assert len(key) == 16 and int(key, 16) >= 0 and v > 0
     for key, v in bench.PREFILL_TRAFFIC.items():
-        assert key[0] in bench.PREFILL_WORKLOADS and key[1] in (1, 2) and len(key) == len(bench.PREFILL_SRCS) + 2
+        assert key[0] in bench.PREFILL_WORKLOADS and key[1] in (1, 2)
+        assert len(key) == len(bench.PREFILL_SRCS[key[0]]) + 2
         assert all(len(h) == 16 for h in key[2:]) and v > 0
     # a figure, when reported, is within a few per cent of the workload's design bytes
     d = bench.measured_decode_traffic("decode_bf16_h2048_e128", 1)

@@ -1,7 +1,9 @@
-"""GPU parity of the prefill path for bf16 expert weights (bf16 matrix cores:
-x and the weights enter exactly, fp32 accumulation, h rounded once to bf16
-before the down projection, each expert output y rounded to bf16 before the
-fp32 combine) against the fp64 oracle.
+"""GPU parity of the prefill path for bf16 and NVFP4-like expert weights
+(bf16 matrix cores: x enters exactly, bf16 weights as stored, NVFP4 weights
+expanded exactly to bf16 with the per-matrix fp32 scale on the
+accumulators; fp32 accumulation, h rounded once to bf16 before the down
+projection, each expert output y rounded to bf16 before the fp32 combine)
+against the fp64 oracle.
 
 Each output is compared with the oracle that rounds h and y the same way
 (mirrored) and with the oracle on fp64 h and y (unmirrored).  Bars: routing
@@ -16,20 +18,24 @@ from oracle.moe import experts_forward_by_expert, route, to_f64
 from oracle.mx import bf16_round_f32
 from oracle.record import decode_record
 from sparse_moe_expert_softmax_amd import ftmoe, synth
-from sparse_moe_expert_softmax_amd.configs import BF16, C2, MoEConfig
+from sparse_moe_expert_softmax_amd.configs import BF16, C2, C5, NVFP4, MoEConfig
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
 
-def _cfg(name, cid, H, I, E, k):
+def _cfg(name, cid, H, I, E, k, wd=BF16):
     return MoEConfig(name, cid, hidden=H, inter=I, n_experts=E, top_k=k, act_dtype=BF16, router_dtype=BF16,
-                     w_dtype=BF16, n_layers=1)
+                     w_dtype=wd, n_layers=1)
 
 
 SMALL = _cfg("prefill_small_bf16", 130, 256, 256, 8, 2)
 MID = _cfg("prefill_mid_bf16", 131, 512, 384, 16, 4)
 SPARSE = _cfg("prefill_sparse_bf16", 132, 768, 640, 128, 2)
 FAT = _cfg("prefill_fat_bf16", 133, 256, 128, 2, 1)
+SMALL_NV = _cfg("prefill_small_nvfp4", 134, 256, 256, 8, 2, NVFP4)
+MID_NV = _cfg("prefill_mid_nvfp4", 135, 512, 384, 16, 4, NVFP4)
+SPARSE_NV = _cfg("prefill_sparse_nvfp4", 136, 768, 640, 128, 2, NVFP4)
+FAT_NV = _cfg("prefill_fat_nvfp4", 137, 256, 128, 2, 1, NVFP4)
 
 MIRROR = dict(h_quant=bf16_round_f32, y_quant=bf16_round_f32)
 
@@ -58,41 +64,45 @@ def run_prefill(cfg, T, layer, step, mask=None):
     return ld, ids, gates, out, err, e2
 
 
+@pytest.mark.parametrize("cfg", [MID, MID_NV], ids=["bf16", "nvfp4"])
 @pytest.mark.parametrize("T", [256, 300, 1031])
-def test_bf16_prefill_every_output(T):
+def test_bf16_prefill_every_output(T, cfg):
     """16 experts / top-4, H 512 (16 K steps of gate/up), I 384 (three
     gate/up weight tiles, 12 K steps of down), two down weight tiles."""
-    print(f"bf16 prefill mid T={T}", flush=True)
-    _, _, _, _, err, e2 = run_prefill(MID, T, 0, 3)
+    print(f"prefill {cfg.name} T={T}", flush=True)
+    _, _, _, _, err, e2 = run_prefill(cfg, T, 0, 3)
     print(f"  max rel err {err:.3g} mirrored, {e2:.3g} exact")
 
 
-def test_bf16_prefill_sparse_experts():
+@pytest.mark.parametrize("cfg", [SPARSE, SPARSE_NV], ids=["bf16", "nvfp4"])
+def test_bf16_prefill_sparse_experts(cfg):
     """128 experts for 600 pairs: experts without rows and with 1-13 rows
     (most waves of a row chunk hold no valid row), five gate/up and three down
     weight tiles."""
-    print("bf16 prefill sparse T=300", flush=True)
-    _, ids, _, _, err, _ = run_prefill(SPARSE, 300, 0, 17)
-    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=SPARSE.n_experts)
+    print(f"prefill {cfg.name} T=300", flush=True)
+    _, ids, _, _, err, _ = run_prefill(cfg, 300, 0, 17)
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=cfg.n_experts)
     assert counts.min() == 0 and counts.max() < 16, (counts.min(), counts.max())
     print(f"  max rel err {err:.3g}")
 
 
-def test_bf16_prefill_experts_spanning_several_row_chunks():
+@pytest.mark.parametrize("cfg", [FAT, FAT_NV], ids=["bf16", "nvfp4"])
+def test_bf16_prefill_experts_spanning_several_row_chunks(cfg):
     """Two experts, top-1, 1,100 tokens: each expert's rows span three
     256-row chunks (the last one partial); down has four K steps (I 128)."""
-    print("bf16 prefill fat T=1100", flush=True)
-    _, ids, _, _, err, _ = run_prefill(FAT, 1100, 0, 19)
+    print(f"prefill {cfg.name} T=1100", flush=True)
+    _, ids, _, _, err, _ = run_prefill(cfg, 1100, 0, 19)
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=2)
     assert counts.min() > 512, counts
     print(f"  rows per expert {counts.tolist()}, max rel err {err:.3g}")
 
 
-def test_bf16_prefill_partition_masks():
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_NV], ids=["bf16", "nvfp4"])
+def test_bf16_prefill_partition_masks(cfg):
     """Each part of three 50/50 expert partitions against the oracle's masked
     layer; the parts add up to the unmasked output within 1e-5 (fp32 sums in
     another order)."""
-    cfg, T = SMALL, 400
+    T = 400
     ld, ids, gates, full, _, _ = run_prefill(cfg, T, 0, 5)
     rng = np.random.default_rng(21)
     for _ in range(3):
@@ -106,11 +116,12 @@ def test_bf16_prefill_partition_masks():
         assert max_rel_err(a + b, full) <= 1e-5
 
 
-def test_bf16_prefill_slots_and_a_failed_lookup():
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_NV], ids=["bf16", "nvfp4"])
+def test_bf16_prefill_slots_and_a_failed_lookup(cfg):
     """Records moved to other slots give bitwise the same output; a negative
     slot for one expert makes exactly the tokens routed to it NaN (nothing is
     read for it) and leaves every other token bitwise unchanged."""
-    cfg, T = SMALL, 320
+    T = 320
     ld, ids, gates, out, _, _ = run_prefill(cfg, T, 0, 9)
     E = cfg.n_experts
     perm = np.random.default_rng(5).permutation(E)
@@ -129,10 +140,10 @@ def test_bf16_prefill_slots_and_a_failed_lookup():
     assert np.array_equal(got[~hit], out[~hit])
 
 
-def test_bf16_prefill_threshold():
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_NV], ids=["bf16", "nvfp4"])
+def test_bf16_prefill_threshold(cfg):
     """255 tokens take the general (fp32 GEMV) path, 256 the matrix cores;
     both against the oracle."""
-    cfg = SMALL
     ld = LayerData(cfg, 0, 13, 255)
     ids, gates, _ = ld.gpu_route()
     o_ids, _, _ = ld.oracle_route()
@@ -181,6 +192,43 @@ def test_bf16_prefill_full_chunk_covers_every_expert():
     np.testing.assert_array_equal(ids.cpu().numpy(), o_ids)
     np.testing.assert_allclose(gates.cpu().numpy(), o_gates, rtol=0, atol=1e-6)
     rows = _cover_all_experts(o_ids, cfg.n_experts, 43)
+    print(f"  routing bit-exact on all {T} tokens; {len(rows)} tokens cover all {cfg.n_experts} experts", flush=True)
+
+    def expert(e):
+        return decode_record(pool[e].cpu().numpy(), cfg.hidden, cfg.inter, cfg.w_dtype)
+
+    got = out.cpu().numpy()
+    assert not np.isnan(got[rows]).any()
+    ref = experts_forward_by_expert(x64, o_ids, o_gates, expert, rows, **MIRROR)
+    exact = experts_forward_by_expert(x64, o_ids, o_gates, expert, rows)
+    err, e2 = max_rel_err(got[rows], ref[rows]), max_rel_err(got[rows], exact[rows])
+    print(f"  max rel err {err:.3g} mirrored, {e2:.3g} exact", flush=True)
+    assert err <= 1e-2 and e2 <= 1e-2
+
+
+def test_nvfp4_prefill_full_chunk_covers_every_expert():
+    """The 753B-like NVFP4 layer (6,144 / 2,048 / 256 experts / top-8) with
+    every expert resident, one 8,192-token chunk (65,536 pairs): routing (the
+    bounded many-token router) bit-exact on every token; outputs on tokens
+    that together use all 256 experts, against the mirrored and the
+    unmirrored oracle."""
+    cfg, T, layer = C5, 8192, 1
+    ld = LayerData(cfg, layer, 0, T)
+    print("nvfp4 prefill full chunk: generating 256 expert records on the device", flush=True)
+    pool = synth.device_layer_pool(torch, cfg, layer, ld.stride)
+    ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, cfg.top_k), dtype=torch.float32, device="cuda")
+    rws = torch.empty(ftmoe.ft_route_workspace_bytes(ld.desc, T), dtype=torch.uint8, device="cuda")
+    ftmoe.ft_moe_route(ld.desc, dev(ld.x), dev(ld.wr), ids, gates, workspace=rws)
+    out = torch.empty((T, cfg.hidden), dtype=torch.float32, device="cuda")
+    fws = torch.empty(ftmoe.ft_moe_workspace_bytes(ld.desc, T), dtype=torch.uint8, device="cuda")
+    ftmoe.ft_moe_forward(ld.desc, dev(ld.x), ids, gates, pool, out, fws)
+    torch.cuda.synchronize()
+    x64 = to_f64(ld.x, cfg.act_dtype)
+    o_ids, o_gates, _ = route(x64, to_f64(ld.wr, cfg.router_dtype), cfg.top_k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), o_ids)
+    np.testing.assert_allclose(gates.cpu().numpy(), o_gates, rtol=0, atol=1e-6)
+    rows = _cover_all_experts(o_ids, cfg.n_experts, 47)
     print(f"  routing bit-exact on all {T} tokens; {len(rows)} tokens cover all {cfg.n_experts} experts", flush=True)
 
     def expert(e):

@@ -51,6 +51,8 @@ PREFILL_SRCS = {
                                                                    "gemv.hip")],
     "prefill_bf16_h2048_e128": [os.path.join(_CSRC, f) for f in ("prefill_bf16.hip", "mfma.hip", "lds_dma.hpp",
                                                                   "permute.hip", "gemv.hip")],
+    "prefill_nvfp4_h6144_e256": [os.path.join(_CSRC, f) for f in ("prefill_bf16.hip", "mfma.hip", "lds_dma.hpp",
+                                                                   "permute.hip", "gemv.hip")],
 }
 PREFILL_WORKLOADS = tuple(PREFILL_SRCS)
 PREFILL_TRAFFIC = {
@@ -74,7 +76,7 @@ def measured_prefill_traffic(cfg_name, chunk_tokens, terms=2):
     import hashlib
     if cfg_name not in PREFILL_WORKLOADS or chunk_tokens != 8192:
         return None
-    if cfg_name == "prefill_bf16_h2048_e128":
+    if cfg_name != "prefill_mxfp4_h4096_e256":
         terms = 1
     key = []
     for p in PREFILL_SRCS[cfg_name]:
@@ -667,7 +669,7 @@ def run_prefill(args, cfg, torch):
     expert set is copied from pinned host memory on a side stream while the
     current layer computes (two HBM layer buffers)."""
     from sparse_moe_expert_softmax_amd import ftmoe, synth
-    from sparse_moe_expert_softmax_amd.configs import BF16
+    from sparse_moe_expert_softmax_amd.configs import BF16, DTYPE_NAMES, NVFP4
     CH = 8192
     T = CH
     chunks = max(1, args.tokens // CH)
@@ -676,7 +678,7 @@ def run_prefill(args, cfg, torch):
     stride = synth.record_stride(H, I, cfg.w_dtype)
     rec = synth.record_bytes(H, I, cfg.w_dtype)
     layer_bytes = E * stride
-    bf = cfg.w_dtype == BF16
+    bf = cfg.w_dtype in (BF16, NVFP4)   # bf16 matrix cores (NVFP4 weights expanded to bf16 on the way in)
     terms = 1 if bf else args.act_terms
     desc = ftmoe.make_desc(cfg, stride, act_terms=0 if bf else args.act_terms)
     NH = max(1, min(args.host_layers, L))
@@ -757,7 +759,7 @@ def run_prefill(args, cfg, torch):
     peak = BF16_PEAK_TFLOPS if bf else MFMA_PEAK_TFLOPS
     res = _base_result(args, T / (t_layer * 1e-3), "tokens/s", t_layer * L,
                        {"workload": cfg.name, "tokens_per_chunk": CH, "chunks": chunks, "layers": L, "hidden": H,
-                        "experts": E, "top_k": k, "inter": I, "weights": "bf16" if bf else "mxfp4",
+                        "experts": E, "top_k": k, "inter": I, "weights": DTYPE_NAMES[cfg.w_dtype],
                         "activations": "bf16, exact on the bf16 matrix cores; h rounded to bf16" if bf else
                         f"bf16, as {terms} MXFP8 term(s) for the matrix cores",
                         "act_terms": terms}, "bf16 (f32 accumulate)" if bf else "f8xf4 (f32 accumulate)")

@@ -61,5 +61,9 @@ C6 = MoEConfig("prefill_bf16_h2048_e128", 6, hidden=2048, inter=768, n_experts=1
                act_dtype=BF16, router_dtype=BF16, w_dtype=BF16, n_layers=40,
                batches=(8192,), note="prefill chunk of 8,192 tokens through the 35B-like bf16 layer")
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C6)}
-BY_ID = {c.cid: c for c in (C1, C2, C3, C4, C5, C6)}
+C7 = MoEConfig("prefill_nvfp4_h6144_e256", 7, hidden=6144, inter=2048, n_experts=256, top_k=8,
+               act_dtype=BF16, router_dtype=BF16, w_dtype=NVFP4, n_layers=8,
+               batches=(8192,), note="prefill chunk of 8,192 tokens through the 753B-like NVFP4 layer")
+
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7)}
+BY_ID = {c.cid: c for c in (C1, C2, C3, C4, C5, C6, C7)}

@@ -55,11 +55,14 @@ PREFILL_SRCS = {
                                                                    "permute.hip", "gemv.hip")],
 }
 PREFILL_WORKLOADS = tuple(PREFILL_SRCS)
+_BH = ("21722fc7d9eb7cb4", "4db791fc00a312b7", "509e27cfdfa24281", "8564bd36b3d79a3c", "6d20609b6838d49c")
 PREFILL_TRAFFIC = {
     ("prefill_mxfp4_h4096_e256", 2, "4db791fc00a312b7", "509e27cfdfa24281", "8564bd36b3d79a3c",
      "6d20609b6838d49c"): 5685784994,
     ("prefill_mxfp4_h4096_e256", 1, "4db791fc00a312b7", "509e27cfdfa24281", "8564bd36b3d79a3c",
      "6d20609b6838d49c"): 4990800130,
+    ("prefill_bf16_h2048_e128", 1) + _BH: 2714547561,
+    ("prefill_nvfp4_h6144_e256", 1) + _BH: 10476768711,
 }
 
 
@@ -462,7 +465,9 @@ def main():
         del pools
         torch.cuda.empty_cache()
         res["prefill"] = prefill_figures(torch)
-        res["prefill_bf16"] = bf16_prefill_figures(torch)
+        from sparse_moe_expert_softmax_amd.configs import C6, C7
+        res["prefill_bf16"] = bf16_prefill_figures(torch, C6)
+        res["prefill_nvfp4"] = bf16_prefill_figures(torch, C7)
         res["ceilings"] = ceilings(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
@@ -625,17 +630,19 @@ def prefill_figures(torch, n_meas=8):
     return res
 
 
-def bf16_prefill_figures(torch, n_meas=8):
-    """The same for bf16 expert weights: one 8,192-token chunk through the
-    35B-like bf16 layer (2,048 / 768 / 128 experts / top-8) with its experts
-    resident, two layers generated on the device, alternated; bf16 matrix
-    cores, useful TFLOP/s against the dense bf16 rate."""
+def bf16_prefill_figures(torch, cfg, n_meas=8):
+    """The same for the layers on the bf16 matrix cores: one 8,192-token chunk
+    through the 35B-like bf16 layer (2,048 / 768 / 128 experts / top-8) or the
+    753B-like NVFP4 layer (6,144 / 2,048 / 256 / top-8) with its experts
+    resident, two layers generated on the device, alternated; useful
+    TFLOP/s against the dense bf16 rate."""
     from sparse_moe_expert_softmax_amd import ftmoe, synth
-    from sparse_moe_expert_softmax_amd.configs import C6
-    cfg, T = C6, 8192
+    from sparse_moe_expert_softmax_amd.configs import DTYPE_NAMES
+    T = 8192
     H, I, k = cfg.hidden, cfg.inter, cfg.top_k
     stride = synth.record_stride(H, I, cfg.w_dtype)
-    print("[bench] prefill figures: generating 2 bf16 layers on the device", file=sys.stderr, flush=True)
+    print(f"[bench] prefill figures: generating 2 {DTYPE_NAMES[cfg.w_dtype]} layers on the device", file=sys.stderr,
+          flush=True)
     bufs = [synth.device_layer_pool(torch, cfg, l, stride) for l in range(2)]
     routers = [torch.from_numpy(synth.router_weights(cfg, l).view(np.int16)).cuda() for l in range(2)]
     x = torch.from_numpy(synth.activations(cfg, 0, 0, T).view(np.int16)).cuda()
@@ -650,10 +657,12 @@ def bf16_prefill_figures(torch, n_meas=8):
     useful = 6.0 * T * k * H * I
     tflops = useful / (float(np.mean(fwd_ms)) * 1e-3) / 1e12
     t_layer = float(np.mean(route_ms + fwd_ms))
-    print(f"[bench] prefill (bf16 weights): route {route_ms.mean():.3f} ms, forward {fwd_ms.mean():.3f} ms per "
-          "layer", file=sys.stderr, flush=True)
-    res = {"workload": cfg.name, "tokens": T, "weights": "bf16 resident", "useful_flops_per_forward": useful,
-           "issued": "v_mfma_f32_16x16x32_bf16, bf16 activations x bf16 weights",
+    print(f"[bench] prefill ({DTYPE_NAMES[cfg.w_dtype]} weights): route {route_ms.mean():.3f} ms, forward "
+          f"{fwd_ms.mean():.3f} ms per layer", file=sys.stderr, flush=True)
+    res = {"workload": cfg.name, "tokens": T, "weights": f"{DTYPE_NAMES[cfg.w_dtype]} resident",
+           "useful_flops_per_forward": useful,
+           "issued": "v_mfma_f32_16x16x32_bf16, bf16 activations x bf16 weights" +
+                     (" (NVFP4 expanded exactly to bf16 in LDS)" if DTYPE_NAMES[cfg.w_dtype] == "nvfp4" else ""),
            "tokens_per_s": round(T / (t_layer * 1e-3), 1),
            "route_us": round(float(route_ms.mean()) * 1e3, 1), "forward_us": round(float(fwd_ms.mean()) * 1e3, 1),
            "useful_tflops": round(tflops, 1), "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),

@@ -269,8 +269,9 @@ int ft_prefill_pipeline_layer(ft_prefill_pipeline* p, const void* const* next_la
  * Decode-sized calls (few pairs per expert) run as bandwidth-bound grouped
  * GEMV.  From 256 tokens on (bf16 activations, H a multiple of 256, I of
  * 128), MXFP4 layers run on gfx950 scaled MFMA with x and h carried as
- * MXFP8 (E4M3, E8M0 per 32; see act_terms), and bf16 layers on the bf16
- * matrix cores with x exact and h rounded once to bf16; on both, each
+ * MXFP8 (E4M3, E8M0 per 32; see act_terms), and bf16 and NVFP4 layers on
+ * the bf16 matrix cores with x exact, NVFP4 weights expanded exactly to bf16
+ * and h rounded once to bf16; on both, each
  * expert output is rounded to bf16 before the fp32 combine.  A negative
  * slot (a failed lookup) reads nothing and makes its tokens' outputs NaN.
  * Errors: FT_EINVAL on nulls / sizes, FT_EUNSUPPORTED on dtype pairs,

@@ -68,3 +68,6 @@ def test_traffic_tables_are_keyed_by_source_hashes():
     p = bench.measured_prefill_traffic("prefill_bf16_h2048_e128", 8192)
     if p is not None:  # weights 1.208 GB, x 33.6 MB, out 67.1 MB, h and y written and read: 2.05 GB by design
         assert 1.0 <= p / 2_046_000_000 <= 1.5
+    p = bench.measured_prefill_traffic("prefill_nvfp4_h6144_e256", 8192)
+    if p is not None:  # weights 5.44 GB, x 100.7 MB, out 201.3 MB, h and y written and read: 7.89 GB by design
+        assert 1.0 <= p / 7_890_000_000 <= 1.5

@@ -11,7 +11,7 @@ import torch
 from gpu_util import LayerData, dev, max_rel_err
 from oracle.mx import bf16_round_f32, mxfp8_two_term, mxfp8_two_term_f32
 from sparse_moe_expert_softmax_amd import ftmoe, synth
-from sparse_moe_expert_softmax_amd.configs import BF16, MXFP4, MoEConfig
+from sparse_moe_expert_softmax_amd.configs import BF16, MXFP4, NVFP4, MoEConfig
 from sparse_moe_expert_softmax_amd.prefill_pipeline import PrefillPipeline
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
@@ -20,6 +20,8 @@ PIPE_MX = MoEConfig("pipeline_mxfp4", 95, hidden=256, inter=256, n_experts=8, to
                     router_dtype=BF16, w_dtype=MXFP4, n_layers=5)
 PIPE_BF16 = MoEConfig("pipeline_bf16", 96, hidden=512, inter=256, n_experts=16, top_k=4, act_dtype=BF16,
                       router_dtype=BF16, w_dtype=BF16, n_layers=4)
+PIPE_NV = MoEConfig("pipeline_nvfp4", 138, hidden=512, inter=256, n_experts=16, top_k=4, act_dtype=BF16,
+                    router_dtype=BF16, w_dtype=NVFP4, n_layers=3)
 
 
 def _host_layers(cfg):
@@ -50,10 +52,11 @@ def _run(cfg, T, host, lds):
     return ids.cpu().numpy(), gates.cpu().numpy(), out.cpu().numpy()
 
 
-@pytest.mark.parametrize("cfg,T", [(PIPE_MX, 300), (PIPE_BF16, 3)])
+@pytest.mark.parametrize("cfg,T", [(PIPE_MX, 300), (PIPE_BF16, 3), (PIPE_BF16, 300), (PIPE_NV, 300)])
 def test_pipeline_layers_match_oracle_and_a_corrupted_record_shows(cfg, T):
-    """MXFP4 at 300 tokens (matrix-core path, five layers) and bf16 at 3
-    tokens (decode path with in-kernel selection, four layers)."""
+    """MXFP4 at 300 tokens (scaled matrix cores, five layers), bf16 at 3
+    tokens (decode path with in-kernel selection, four layers), bf16 and
+    NVFP4 at 300 tokens (bf16 matrix cores)."""
     print(f"prefill pipeline {cfg.name} T={T} layers={cfg.n_layers}", flush=True)
     host = _host_layers(cfg)
     lds = [LayerData(cfg, l, 7 + l, T) for l in range(cfg.n_layers)]

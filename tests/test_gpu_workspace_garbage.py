@@ -3,7 +3,8 @@ zero-filled workspaces and once with workspaces full of 0xFF bytes (NaN in
 every float view, -1 in every integer view); ids, gates and outputs must be
 bitwise equal.  Covers the decode route and GEMV path, the general path,
 the many-token bounded router, the fp64 matrix-core router (fp32 inputs, or
-a logits output), the prefill MFMA path, masked forwards through slot
+a logits output), the prefill matrix-core paths (MXFP4 on the scaled MFMA,
+bf16 and NVFP4 on the bf16 MFMA), masked forwards through slot
 indirection, and the fused route + forward call (in-kernel selection at one
 token, the two-call branch at four)."""
 import numpy as np
@@ -12,12 +13,16 @@ import torch
 
 from gpu_util import LayerData, dev
 from sparse_moe_expert_softmax_amd import ftmoe
-from sparse_moe_expert_softmax_amd.configs import BF16, C1, C2, C3, C5, MXFP4, MoEConfig
+from sparse_moe_expert_softmax_amd.configs import BF16, C1, C2, C3, C5, MXFP4, NVFP4, MoEConfig
 
 pytestmark = pytest.mark.gpu
 
 MID = MoEConfig("prefill_mid_mxfp4", 91, hidden=512, inter=384, n_experts=16, top_k=4, act_dtype=BF16,
                 router_dtype=BF16, w_dtype=MXFP4, n_layers=1)
+MID_BF = MoEConfig("prefill_mid_bf16", 131, hidden=512, inter=384, n_experts=16, top_k=4, act_dtype=BF16,
+                   router_dtype=BF16, w_dtype=BF16, n_layers=1)
+MID_NV = MoEConfig("prefill_mid_nvfp4", 135, hidden=512, inter=384, n_experts=16, top_k=4, act_dtype=BF16,
+                   router_dtype=BF16, w_dtype=NVFP4, n_layers=1)
 
 
 def run(ld, fill, logits=False, mask=None, slots=None):
@@ -45,7 +50,7 @@ def run(ld, fill, logits=False, mask=None, slots=None):
     return (ids, gates, out) + ((lg,) if logits else ())
 
 
-@pytest.mark.parametrize("cfg,T", [(C2, 1), (C2, 4), (C2, 17), (C3, 2), (MID, 300)])
+@pytest.mark.parametrize("cfg,T", [(C2, 1), (C2, 4), (C2, 17), (C3, 2), (MID, 300), (MID_BF, 300), (MID_NV, 300)])
 def test_results_do_not_depend_on_workspace_contents(cfg, T):
     print(f"workspace garbage {cfg.name} T={T}", flush=True)
     ld = LayerData(cfg, 0, 3, T)

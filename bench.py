@@ -469,6 +469,9 @@ def main():
         res["prefill_bf16"] = bf16_prefill_figures(torch, C6)
         res["prefill_nvfp4"] = bf16_prefill_figures(torch, C7)
         res["ceilings"] = ceilings(torch)
+        # the same forward rate against the streaming read this chip sustained in this run
+        res["roofline"]["frac_of_stream_ceiling"] = round(
+            m["achieved_gbs"] / res["ceilings"]["stream_read_gbs"]["hbm_1GiB"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, B, args.cpu_seconds)

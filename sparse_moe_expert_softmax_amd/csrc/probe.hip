@@ -26,22 +26,43 @@ typedef float pf32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kUnroll = 4;  // 16-byte loads in flight per thread and pass
 
-__global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restrict__ p, int64_t n16, int passes,
-                                                          uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+typedef unsigned int pu32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const uint4* p) {
+  if constexpr (NT) {
+    const pu32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const pu32x4_t*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+  } else {
+    return *p;
+  }
+}
+
+// Reads n16 16-byte words `passes` times.  BLOCK: workgroup b owns the
+// contiguous range [b*chunk, (b+1)*chunk) (each wave streams whole 4 KB
+// spans); otherwise the grid strides over the buffer.  NT: loads carry the
+// nontemporal hint.  Out-of-range slots are clamped to the range's last word,
+// so every load issues and the extra ones hit a line already fetched.
+template <bool BLOCK, bool NT>
+__global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restrict__ p, int64_t n16, int64_t chunk,
+                                                          int passes, uint32_t* __restrict__ sink) {
+  const int64_t lo = BLOCK ? (int64_t)blockIdx.x * chunk : 0;
+  const int64_t hi = BLOCK ? (lo + chunk < n16 ? lo + chunk : n16) : n16;
+  const int64_t first = BLOCK ? lo + threadIdx.x : (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = BLOCK ? (int64_t)blockDim.x : (int64_t)gridDim.x * blockDim.x;
   uint32_t acc = 0;
   for (int pass = 0; pass < passes; ++pass)
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += kUnroll * stride) {
-    uint4 v[kUnroll];
+    for (int64_t i = first; i < hi; i += kUnroll * stride) {
+      uint4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t j = i + u * stride;
-      v[u] = p[j < n16 ? j : n16 - 1];  // clamped: every load issues, the extra ones repeat the last line
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t j = i + u * stride;
+        v[u] = ld16<NT>(p + (j < hi ? j : hi - 1));
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (i + u * stride < hi) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (i + u * stride < n16) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
@@ -171,10 +192,19 @@ int status(hipError_t e) { return e == hipSuccess ? 0 : -4; }
 extern "C" {
 
 // Read `bytes` (a multiple of 16, 16-byte aligned) `passes` times with `grid` workgroups of 256 threads.
-int ftp_stream_read(const void* buf, int64_t bytes, int32_t passes, uint32_t* sink, int32_t grid, void* stream) {
-  if (!buf || !sink || bytes < 16 || bytes % 16 || grid < 1 || passes < 1) return -1;
-  stream_read_kernel<<<grid, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
-      reinterpret_cast<const uint4*>(buf), bytes / 16, passes, sink);
+// flags bit 0: nontemporal loads; bit 1: each workgroup reads one contiguous range (else grid-stride).
+int ftp_stream_read(const void* buf, int64_t bytes, int32_t passes, uint32_t* sink, int32_t grid, int32_t flags,
+                    void* stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 || grid < 1 || passes < 1 || (flags & ~3)) return -1;
+  const int64_t n16 = bytes / 16, chunk = (n16 + grid - 1) / grid;
+  const uint4* p = reinterpret_cast<const uint4*>(buf);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  switch (flags) {
+    case 0: stream_read_kernel<false, false><<<grid, 256, 0, st>>>(p, n16, chunk, passes, sink); break;
+    case 1: stream_read_kernel<false, true><<<grid, 256, 0, st>>>(p, n16, chunk, passes, sink); break;
+    case 2: stream_read_kernel<true, false><<<grid, 256, 0, st>>>(p, n16, chunk, passes, sink); break;
+    default: stream_read_kernel<true, true><<<grid, 256, 0, st>>>(p, n16, chunk, passes, sink); break;
+  }
   return status(hipGetLastError());
 }
 

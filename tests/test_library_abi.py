@@ -90,7 +90,8 @@ def test_probe_library_exports_and_refuses_bad_arguments_without_gpu():
         assert hasattr(L, n), n
     buf = ctypes.create_string_buffer(64)
     p = ctypes.cast(buf, ctypes.c_void_p)
-    assert L.ftp_stream_read(p, ctypes.c_int64(8), ctypes.c_int32(1), p, ctypes.c_int32(1), None) == -1
+    assert L.ftp_stream_read(p, ctypes.c_int64(8), ctypes.c_int32(1), p, ctypes.c_int32(1), ctypes.c_int32(0), None) == -1
+    assert L.ftp_stream_read(p, ctypes.c_int64(16), ctypes.c_int32(1), p, ctypes.c_int32(1), ctypes.c_int32(4), None) == -1
     assert L.ftp_empty(ctypes.c_int32(-1), None) == -1
     assert L.ftp_mfma(ctypes.c_int32(6), p, ctypes.c_int32(1), ctypes.c_int32(1), None) == -1
     assert L.ftp_lds_dma(p, ctypes.c_int64(100), p, ctypes.c_int32(1), ctypes.c_int32(1), None) == -1

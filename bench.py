@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 # plain 256 MiB device copy (FETCH_SIZE x 1.9997, WRITE_SIZE x 1.0).  Keyed by the
 # SHA-256 prefix of the kernel source the counters were taken on: any change to
 # that source reports null until the counters are taken again.
-DECODE_TRAFFIC = {"2a6d2b43498392c5": 75904234}
+DECODE_TRAFFIC = {"67a01b1625890854": 75916447}
 DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_expert_softmax_amd", "csrc",
                           "decode_mfma.hip")
 # The same for the prefill workloads (8,192-token chunks: MXFP4 H4096 E256
@@ -140,8 +140,9 @@ def device_pool_bf16(cfg, layer, torch):
 
 def ceilings(torch, reps=5):
     """Achievable ceilings on this GPU, from the probe library (libftprobe.so,
-    not the MoE path): streaming reads from HBM (1 GiB) and from the Infinity
-    Cache (64 MiB read again); back-to-back empty launches; dense matrix-core
+    not the MoE path): streaming reads from HBM (1 GiB, and 75 MB launches the
+    size of one bf16 decode layer's expert bytes, each cold) and from the
+    Infinity Cache (64 MiB read again); back-to-back empty launches; dense matrix-core
     loops (bf16, MXFP8 x MXFP4, MXFP4 x MXFP4, both instruction shapes);
     LDS-DMA from an L2-resident 2 MiB buffer (the L2 -> LDS path).  HIP events
     on the launch stream; median of reps."""
@@ -171,13 +172,42 @@ def ceilings(torch, reps=5):
     sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
     sptr = ctypes.c_void_p(sink.data_ptr())
     res = {"source": "libftprobe.so (sparse_moe_expert_softmax_amd/csrc/probe.hip)"}
+    def read_gbs(bufs, nbytes, passes, flags, grid):
+        # median over launches, each bracketed by its own events, rotating over `bufs`
+        EV = lambda: torch.cuda.Event(enable_timing=True)
+        run = lambda b: check(lib.ftp_stream_read(ctypes.c_void_p(b.data_ptr()), ctypes.c_int64(nbytes),
+                                                  ctypes.c_int32(passes), sptr, ctypes.c_int32(grid),
+                                                  ctypes.c_int32(flags), sp))
+        for b in bufs:
+            run(b)
+        evs = []
+        for r in range(max(10, len(bufs))):
+            a, z = EV(), EV()
+            a.record(st)
+            run(bufs[r % len(bufs)])
+            z.record(st)
+            evs.append((a, z))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(z) for a, z in evs]))
+        return round(nbytes * passes / (ms * 1e-3) / 1e9, 1)
+
+    # flags: bit 0 nontemporal hint, bit 1 one contiguous range per workgroup
     rd = {}
-    for name, nbytes, passes in (("hbm_1GiB", 1 << 30, 1), ("infinity_cache_64MiB", 64 << 20, 16)):
-        buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
-        ms = timed(lambda: check(lib.ftp_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_int64(nbytes),
-                                                       ctypes.c_int32(passes), sptr, ctypes.c_int32(8192), sp)))
-        rd[name] = round(nbytes * passes / (ms * 1e-3) / 1e9, 1)
-        del buf
+    gib = [torch.ones(1 << 30, dtype=torch.uint8, device="cuda") for _ in range(3)]  # 3 GiB: cold in the 256 MB cache
+    rd["hbm_1GiB"] = read_gbs(gib, 1 << 30, 1, 3, 8192)
+    rd["hbm_1GiB_plain_loads"] = read_gbs(gib, 1 << 30, 1, 2, 8192)
+    rd["hbm_1GiB_grid_stride"] = read_gbs(gib, 1 << 30, 1, 0, 8192)
+    del gib
+    # one decode layer's expert bytes (8 experts x 3 bf16 matrices of 2048 x 768), 40 layers rotating,
+    # each launch cold: the streaming rate a launch of that size can reach
+    nb = 8 * 3 * 2048 * 768 * 2
+    lay = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(40)]
+    rd["hbm_75MB_per_launch_cold"] = read_gbs(lay, nb, 1, 3, nb // 16 // 1024)
+    del lay
+    mall = [torch.ones(64 << 20, dtype=torch.uint8, device="cuda")]
+    rd["infinity_cache_64MiB"] = read_gbs(mall, 64 << 20, 16, 2, 8192)
+    rd["infinity_cache_64MiB_grid_stride"] = read_gbs(mall, 64 << 20, 16, 0, 8192)
+    del mall
     res["stream_read_gbs"] = rd
     n = 200
     ms = timed(lambda: check(lib.ftp_empty(ctypes.c_int32(n), sp)))
@@ -470,8 +500,9 @@ def main():
         res["prefill_nvfp4"] = bf16_prefill_figures(torch, C7)
         res["ceilings"] = ceilings(torch)
         # the same forward rate against the streaming read this chip sustained in this run
-        res["roofline"]["frac_of_stream_ceiling"] = round(
-            m["achieved_gbs"] / res["ceilings"]["stream_read_gbs"]["hbm_1GiB"], 4)
+        rd = res["ceilings"]["stream_read_gbs"]
+        res["roofline"]["frac_of_stream_ceiling"] = round(m["achieved_gbs"] / rd["hbm_1GiB"], 4)
+        res["roofline"]["frac_of_same_size_stream"] = round(m["achieved_gbs"] / rd["hbm_75MB_per_launch_cold"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, B, args.cpu_seconds)

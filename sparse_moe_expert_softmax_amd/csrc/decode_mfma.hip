@@ -52,10 +52,14 @@ struct PairInfo {
   int expert;       // expert handled by this workgroup (valid if d < n_distinct)
   int npairs;       // pairs routed to it
   int ntok;         // distinct tokens among them (<= T)
-  int pair[DEC_MAX_PAIRS];  // their pair indices t*k + j, ascending
-  int rank[DEC_MAX_PAIRS];  // rank of each pair's token among the distinct tokens
-  int tok[DEC_MAX_PAIRS];   // token of each rank
+  // bytes, not ints: the table sits beside up to 16 staged activation rows in
+  // LDS, and at hidden 6144 with 4 tokens 768 more bytes per workgroup cost a
+  // third resident workgroup per CU (NVFP4 decode measured 14% slower)
+  uint8_t pair[DEC_MAX_PAIRS];  // their pair indices t*k + j, ascending
+  uint8_t rank[DEC_MAX_PAIRS];  // rank of each pair's token among the distinct tokens
+  uint8_t tok[DEC_MAX_PAIRS];   // token of each rank
 };
+static_assert(DEC_MAX_PAIRS <= 256, "pair table entries are bytes");
 
 __device__ __forceinline__ bool dm_in_mask(const uint32_t* mask, int e) {
   return mask == nullptr || ((mask[e >> 5] >> (e & 31)) & 1u);
@@ -95,9 +99,9 @@ __device__ __forceinline__ void dm_group_pairs(const int32_t* __restrict__ ids, 
   const uint64_t first = __ballot(in && (mine & same_below) == 0ull);
   if (in) {
     const int q = __popcll(mine & below), r = __popcll(first & below);
-    pi->pair[q] = lane;
-    pi->rank[q] = r - (((first >> lane) & 1ull) ? 0 : 1);
-    if ((first >> lane) & 1ull) pi->tok[r] = lane / k;
+    pi->pair[q] = (uint8_t)lane;
+    pi->rank[q] = (uint8_t)(r - (((first >> lane) & 1ull) ? 0 : 1));
+    if ((first >> lane) & 1ull) pi->tok[r] = (uint8_t)(lane / k);
   }
   if (lane == 0) {
     pi->n_distinct = n;
@@ -310,13 +314,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
   const int cpw = nchunk / DM_WAVES;
   const int cbeg = GRP ? wv * cpw : wv, cend = GRP ? cbeg + cpw : nchunk;
   const int cstep = GRP ? UNROLL : DM_WAVES * UNROLL, ustep = GRP ? 1 : DM_WAVES;
-  if constexpr (XL) {  // stage the activation rows of the expert's distinct tokens (at most T <= 16), once
-    for (int q = tid; q < pi.ntok * (H / 8); q += DM_THREADS) {
-      const int r = q / (H / 8), c8 = q % (H / 8);
-      const int tr = pi.tok[r];
-      *reinterpret_cast<uint4*>(xs + r * XS + 8 * c8) = *reinterpret_cast<const uint4*>(x + (int64_t)tr * H + 8 * c8);
-    }
-  }
+  bool staged = false;  // activation rows of the expert's distinct tokens (at most 16) in LDS, once
   for (int tg = 0; tg < np; tg += 16) {
     const bool tok_ok = tg + col < np;
     const int t = tok_ok ? pi.pair[tg + col] / k : 0;
@@ -398,7 +396,17 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
               }
             }
           } else {
-            if (c0 == cbeg) __syncthreads();  // staged activations visible (first pass only)
+            if (c0 == cbeg) {
+              if (!staged) {  // after the first pass's weight loads are issued: the two latencies overlap
+                for (int q = tid; q < pi.ntok * (H / 8); q += DM_THREADS) {
+                  const int r = q / (H / 8), c8 = q % (H / 8);
+                  *reinterpret_cast<uint4*>(xs + r * XS + 8 * c8) =
+                      *reinterpret_cast<const uint4*>(x + (int64_t)pi.tok[r] * H + 8 * c8);
+                }
+                staged = true;
+              }
+              __syncthreads();  // staged activations visible (first pass only)
+            }
           }
     #pragma unroll
           for (int u = 0; u < UNROLL; ++u) {
@@ -608,14 +616,20 @@ DecGateupShape dec_gateup_shape(const ft_moe_desc& d, int T) {
   const int H = d.hidden, I = d.inter, E = d.n_experts, P = T * d.top_k;
   const int nd_max = P < E ? P : E;
   const int nchunk = H / ((d.w_dtype == FT_BF16) ? 64 : 128);
-  // two 8-row tiles per workgroup when at least DM_MERGE_MIN workgroups
-  // remain (each workgroup groups the pairs, and stages activations, once
-  // for both).  Measured: 10-15% faster on MXFP4 and NVFP4 layers with 1536
-  // and more tiles; on a bf16 layer with 768 tiles the halved grid keeps too
-  // few loads in flight (12% slower), so that one keeps a tile each.
+  // Staged activations (XL: the expert's token rows in LDS, each wave a
+  // contiguous quarter of the chunks) with two 8-row tiles per workgroup when
+  // at least 2 * DM_MERGE_MIN tiles exist (each workgroup groups the pairs,
+  // and stages activations, once for both).  Measured, same box: MXFP4 and
+  // NVFP4 layers with 1,536 and more tiles 10-15% faster; the bf16 layer at
+  // 2 and 4 tokens (1,536 and 3,072 tiles) 3% and 7% faster than its strided
+  // register-fed loop, which it keeps at one token (768 tiles, equal there).
   DecGateupShape sh;
-  sh.xl = d.w_dtype != FT_BF16 && dec_xl_bytes(T, H) <= 56 * 1024 && nchunk % 16 == 0;  // staged activations
-  sh.ntw = (sh.xl && (I / 8) % 2 == 0 && (int64_t)nd_max * (I / 8) >= 2 * DM_MERGE_MIN) ? 2 : 1;
+  const bool many = (int64_t)nd_max * (I / 8) >= 2 * DM_MERGE_MIN && (I / 8) % 2 == 0;
+  if (d.w_dtype == FT_BF16)
+    sh.xl = many && dec_xl_bytes(T, H) <= 56 * 1024 && nchunk % 32 == 0;  // one pass of 8 chunks per wave at H 2048
+  else
+    sh.xl = dec_xl_bytes(T, H) <= 56 * 1024 && nchunk % 16 == 0;
+  sh.ntw = (sh.xl && many) ? 2 : 1;
   sh.grid = (unsigned)(nd_max * (I / 8 / sh.ntw));
   return sh;
 }
@@ -652,6 +666,11 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
   if constexpr (WD != FT_BF16) {
     if (xl) {
       DM_GATEUP(4, true, true, xl_bytes);
+      done = true;
+    }
+  } else {
+    if (xl) {
+      DM_GATEUP(8, true, true, xl_bytes);
       done = true;
     }
   }

@@ -272,9 +272,17 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
   if constexpr (RPER > 0) {
     __shared__ int32_t s_ids[DEC_MAX_PAIRS];
     __shared__ float s_gates[DEC_MAX_PAIRS];
-    for (int t = wv; t < T; t += DM_WAVES)
-      topk_one_token<RPER>(route.logits + (int64_t)t * E, route.sel_bias ? route.sel_bias + (int64_t)t * E : nullptr,
-                           E, k, route.renormalize, s_ids + t * k, s_gates + t * k);
+    // one token with renormalised gates: the whole workgroup ranks the
+    // experts (its LDS scratch is the reduction buffer, unused until the
+    // streaming loop ends); else, or where high halves tie, a wave per token
+    static_assert(sizeof(red) >= 3364, "selection scratch");
+    const bool ranked = (T == 1 && route.renormalize) &&
+                        topk_wg_one_token<RPER, DM_THREADS>(route.logits, route.sel_bias, E, k, s_ids, s_gates,
+                                                            reinterpret_cast<unsigned char*>(&red[0][0]));
+    if (!ranked)
+      for (int t = wv; t < T; t += DM_WAVES)
+        topk_one_token<RPER>(route.logits + (int64_t)t * E, route.sel_bias ? route.sel_bias + (int64_t)t * E : nullptr,
+                             E, k, route.renormalize, s_ids + t * k, s_gates + t * k);
     __syncthreads();
     if (blockIdx.x == 0)
       for (int q = tid; q < P; q += DM_THREADS) {

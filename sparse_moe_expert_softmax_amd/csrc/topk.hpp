@@ -198,6 +198,94 @@ __device__ void topk_one_token(const double* __restrict__ lt, const float* __res
   topk_core<PER>(lv, sv, bias_t != nullptr, E, k, renormalize, ids_t, gates_t);
 }
 
+// Top-k of ONE token by a whole workgroup of NTHR threads (E <= 64 * PER),
+// with renormalised gates.  Each expert's rank is the number of experts whose
+// key has a larger high half, counted by NTHR / (64 PER) threads, each over
+// an equal share of the experts, from high halves broadcast out of LDS: a
+// few hundred cycles of independent compares instead of k dependent rounds.
+// Where the high halves within the top k are distinct, the ranks below k name
+// k different experts in the order of topk_core's rounds.  Where one is shared
+// (scores equal, or equal to about one part in a million, or NaN scores and
+// absent experts needed to fill k), two experts claim one rank and another
+// rank stays empty; the function then returns false with nothing stored, and
+// the caller runs topk_one_token, which breaks such ties exactly.  The gates
+// are topk_core's: the same exponentials, summed in ascending expert id order,
+// so every result is bitwise that of topk_one_token.  `scr`: 3,364 bytes of
+// LDS the caller does not need meanwhile.  All NTHR threads call it together.
+template <int PER, int NTHR>
+__device__ bool topk_wg_one_token(const double* __restrict__ lt, const float* __restrict__ bias_t, int E, int k,
+                                  int32_t* __restrict__ ids_t, float* __restrict__ gates_t, unsigned char* scr) {
+  constexpr int EP = 64 * PER, NT = NTHR / EP, SPAN = EP / NT;
+  static_assert(NT * EP == NTHR && SPAN % 4 == 0 && EP <= 256, "workgroup shape");
+  uint32_t* s_hi = reinterpret_cast<uint32_t*>(scr);          // [EP]   high halves of the keys
+  int* s_cnt = reinterpret_cast<int*>(scr + 1024);             // [NTHR] partial counts
+  double* s_ex = reinterpret_cast<double*>(scr + 2048);        // [k]    exponentials, ascending id
+  double* s_lw = reinterpret_cast<double*>(scr + 2560);        // [k]    winners' logits by rank
+  int* s_win = reinterpret_cast<int*>(scr + 3072);             // [k]    winner of each rank
+  uint64_t* s_wm = reinterpret_cast<uint64_t*>(scr + 3328);    // [PER]  winners, one word per 64 ids
+  int* s_bad = reinterpret_cast<int*>(scr + 3360);
+  const int tid = threadIdx.x, lane = tid & 63, i = tid % EP, part = tid / EP;
+  const int ic = i < E ? i : E - 1;  // clamped: every load issues at once
+  const double l = lt[ic];
+  const float b = bias_t ? bias_t[ic] : 0.f;
+  double sc = l;
+  if (bias_t) sc += (double)b;
+  const uint32_t hi = (i < E) ? (uint32_t)((dkey(sc) + 1ull) >> 32) : 0u;
+  if (part == 0) s_hi[i] = hi;
+  if (tid < k) s_win[tid] = -1;
+  if (tid == 0) *s_bad = 0;
+  __syncthreads();
+  int cnt = 0;
+  const uint4* h4 = reinterpret_cast<const uint4*>(s_hi + part * SPAN);
+#pragma unroll
+  for (int q = 0; q < SPAN / 4; ++q) {
+    const uint4 v = h4[q];
+    cnt += (v.x > hi ? 1 : 0) + (v.y > hi ? 1 : 0) + (v.z > hi ? 1 : 0) + (v.w > hi ? 1 : 0);
+  }
+  s_cnt[tid] = cnt;
+  __syncthreads();
+  int rank = 0;
+  bool win = false;
+  if (part == 0) {
+#pragma unroll
+    for (int p = 0; p < NT; ++p) rank += s_cnt[i + p * EP];
+    win = i < E && rank < k;
+    if (win) {
+      s_win[rank] = i;
+      s_lw[rank] = l;
+    }
+  }
+  const uint64_t wm = __ballot(win);  // part 0 is waves 0 .. PER-1, expert i = tid
+  if (part == 0 && lane == 0) s_wm[tid >> 6] = wm;
+  __syncthreads();
+  // two claimants of one rank: one of them reads the other's id; an empty rank reads -1
+  if ((win && s_win[rank] != i) || (tid < k && s_win[tid] < 0)) *s_bad = 1;
+  __syncthreads();
+  if (*s_bad) return false;
+  double ex = 0.0;
+  if (win) {
+    double mx = -__builtin_inf();  // topk_core: the rank-0 logit, or the largest winner logit with a bias
+    if (bias_t) {
+      for (int q = 0; q < k; ++q) mx = fmax(mx, s_lw[q]);
+    } else {
+      mx = fmax(mx, s_lw[0]);
+    }
+    ex = exp(l - mx);
+    const int w = tid >> 6;
+    int pos = __popcll(s_wm[w] & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+    for (int q = 0; q < w; ++q) pos += __popcll(s_wm[q]);
+    s_ex[pos] = ex;
+  }
+  __syncthreads();
+  if (win) {
+    double den = 0.0;
+    for (int q = 0; q < k; ++q) den += s_ex[q];
+    ids_t[rank] = i;
+    gates_t[rank] = (float)(ex / den);
+  }
+  return true;
+}
+
 // The k-th largest of the wave's keys (key + 1 per expert, 0 = absent),
 // by the same rounds of wave maxima.
 template <int PER>

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import LayerData, dev, max_rel_err
+from gpu_util import LayerData, dev, max_rel_err, to_f64
 from sparse_moe_expert_softmax_amd import ftmoe
 from sparse_moe_expert_softmax_amd.configs import BF16, C1, C2, C3, C5, MXFP4, NVFP4, MoEConfig
 
@@ -30,8 +30,8 @@ NV_SM = MoEConfig("decode_nvfp4_h2048_e64", 87, hidden=2048, inter=256, n_expert
                   router_dtype=BF16, w_dtype=NVFP4, n_layers=1)
 
 
-def fused_vs_separate(cfg, T, step, bias=None, mask=None):
-    ld = LayerData(cfg, 0, step, T)
+def fused_vs_separate(cfg, T, step, bias=None, mask=None, x=None, wr=None):
+    ld = LayerData(cfg, 0, step, T, x=x, wr=wr)
     ids, gates, _ = ld.gpu_route(bias=bias)
     ld.build_pool(ids.cpu().numpy().ravel())
     out = ld.gpu_forward(ids, gates, mask=mask)
@@ -88,6 +88,38 @@ def test_fused_full_softmax_gates_and_oracle():
     np.testing.assert_allclose(f_gates.cpu().numpy(), o_gates, rtol=0, atol=1e-6)
     ref, _, _ = ld.oracle_layer()
     assert max_rel_err(f_out.cpu().numpy(), ref) <= 1e-3
+
+
+def test_fused_one_token_ties_take_the_exact_rounds():
+    """At one token the gate/up workgroup ranks the experts by the high 32
+    bits of their keys.  Where those tie inside the top k it must hand over to
+    the exact rounds: a zero router (every logit equal), and two experts whose
+    logits differ only below the high half (one bf16 ulp of one router weight,
+    times the smallest activation).  Both against the separate calls, bit for
+    bit, and against the oracle's selection."""
+    cfg = C2
+    print("fused C2 T=1, zero router", flush=True)
+    zero = np.zeros((cfg.n_experts, cfg.hidden), dtype=np.uint16)
+    _, f_ids, f_gates, _ = fused_vs_separate(cfg, 1, 150, wr=zero)
+    np.testing.assert_array_equal(f_ids.cpu().numpy(), np.arange(cfg.top_k)[None, :])
+    np.testing.assert_allclose(f_gates.cpu().numpy(), 1.0 / cfg.top_k, rtol=0, atol=1e-7)
+
+    print("fused C2 T=1, logits tied in their high 32 bits", flush=True)
+    base = LayerData(cfg, 0, 151, 1)
+    o_ids, _, o_logits = base.oracle_route()
+    ea, eb = int(o_ids[0, 0]), int(o_ids[0, 2])
+    x64 = to_f64(base.x, cfg.act_dtype)[0]
+    w = base.wr.copy()
+    w[eb] = w[ea]
+    nz = np.flatnonzero((x64 != 0) & (to_f64(w[ea], cfg.router_dtype) != 0))
+    j = int(nz[np.argmin(np.abs(x64[nz]))])
+    w[eb, j] = w[ea, j] + 1  # one bf16 ulp away (same sign and exponent: the low mantissa bit)
+    ld = LayerData(cfg, 0, 151, 1, wr=w)
+    o_ids2, _, o_logits2 = ld.oracle_route()
+    la, lb = np.float64(o_logits2[0, ea]), np.float64(o_logits2[0, eb])
+    assert la != lb and (la.view(np.uint64) >> 32) == (lb.view(np.uint64) >> 32), (la, lb)
+    _, f_ids, _, _ = fused_vs_separate(cfg, 1, 151, wr=w)
+    np.testing.assert_array_equal(f_ids.cpu().numpy(), o_ids2)
 
 
 @pytest.mark.parametrize("cfg,T", [(C1, 16), (SMALL, 300), (C2, 17), (C2, 12), (C5, 9)])

@@ -56,20 +56,23 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
 }
 
 // E8M0 -> fp32: 2^(v-127); 0 -> 2^-127 (fp32 subnormal); 255 -> NaN.
+// Selects on values, not branches: per-lane branches here compile to
+// exec-mask blocks of a dozen scalar instructions at every use.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t v) {
-  if (v == 0u) return __uint_as_float(0x00400000u);
-  if (v == 255u) return __uint_as_float(0x7FC00000u);
-  return __uint_as_float(v << 23);
+  uint32_t b = v << 23;
+  b = (v == 0u) ? 0x00400000u : b;
+  b = (v == 255u) ? 0x7FC00000u : b;
+  return __uint_as_float(b);
 }
 
-// E4M3 (OCP FN: bias 7, no inf, S.1111.111 = NaN) -> fp32.
+// E4M3 (OCP FN: bias 7, no inf, S.1111.111 = NaN) -> fp32, by selects.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float mag;
-  if (e == 0u) mag = (float)m * 0.001953125f;                 // m/8 * 2^-6
-  else if (e == 15u && m == 7u) mag = __uint_as_float(0x7FC00000u);
-  else mag = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1+m/8) * 2^(e-7)
-  return (c & 0x80u) ? -mag : mag;
+  const float sub = (float)m * 0.001953125f;                       // e == 0: m/8 * 2^-6
+  uint32_t mag = ((e + 120u) << 23) | (m << 20);                   // (1+m/8) * 2^(e-7)
+  mag = (e == 0u) ? __float_as_uint(sub) : mag;
+  mag = (e == 15u && m == 7u) ? 0x7FC00000u : mag;
+  return __uint_as_float(mag | ((c & 0x80u) << 24));
 }
 
 // ------------------------------------------------------------ reductions ---

@@ -196,17 +196,32 @@ __device__ __forceinline__ bf16x8_t fp4x8_bf16_mul(uint32_t q, float s) {
 }
 
 // A operand (weights) of MFMA j of a chunk.
+// A lane's block scale(s) for one chunk, converted once before the chunk's
+// products (MXFP4: one E8M0 scale; NVFP4: the E4M3 scales of its two blocks
+// of 16), not once per product.
+struct ChunkScale { float s0, s1; };
 template <int WD>
-__device__ __forceinline__ bf16x8_t decode_a(const RawW<WD>& r, int j) {
+__device__ __forceinline__ ChunkScale chunk_scale(const RawW<WD>& r) {
+  if constexpr (WD == FT_MXFP4) {
+    const float s = e8m0_to_f32(r.s);
+    return {s, s};
+  } else if constexpr (WD == FT_NVFP4) {
+    return {e4m3_to_f32(r.s & 0xFFu), e4m3_to_f32(r.s >> 8)};
+  } else {
+    return {1.f, 1.f};
+  }
+}
+
+template <int WD>
+__device__ __forceinline__ bf16x8_t decode_a(const RawW<WD>& r, int j, ChunkScale cs) {
   if constexpr (WD == FT_BF16) {
     return as_bf16x8(r.q[j]);
   } else if constexpr (WD == FT_MXFP4) {
     const uint32_t q = (j == 0) ? r.q.x : (j == 1) ? r.q.y : (j == 2) ? r.q.z : r.q.w;
-    return fp4x8_bf16(q, e8m0_to_f32(r.s));
+    return fp4x8_bf16(q, cs.s0);
   } else {
     const uint32_t q = (j == 0) ? r.q.x : (j == 1) ? r.q.y : (j == 2) ? r.q.z : r.q.w;
-    const float s = e4m3_to_f32((j < 2) ? (r.s & 0xFFu) : (r.s >> 8));
-    return fp4x8_bf16_mul(q, s);
+    return fp4x8_bf16_mul(q, (j < 2) ? cs.s0 : cs.s1);
   }
 }
 
@@ -350,8 +365,9 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
           for (int u = 0; u < UNROLL; ++u) {
             const int c = c0 + u * DM_WAVES;
             if (c < nchunk) {
+              const ChunkScale cs = chunk_scale<WD>(rw[u]);
   #pragma unroll
-              for (int j = 0; j < NM; ++j) acc = mfma(decode_a<WD>(rw[u], j), as_bf16x8(xb[u][j]), acc);
+              for (int j = 0; j < NM; ++j) acc = mfma(decode_a<WD>(rw[u], j, cs), as_bf16x8(xb[u][j]), acc);
             }
           }
         }
@@ -420,12 +436,13 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
           for (int u = 0; u < UNROLL; ++u) {
             const int c = c0 + u * ustep;
             if (c < cend) {
+              const ChunkScale cs = chunk_scale<WD>(rw[u]);
     #pragma unroll
               for (int j = 0; j < NM; ++j) {
                 uint4 xv;
                 if constexpr (XL) xv = tok_ok ? *reinterpret_cast<const uint4*>(xs + xrow * XS + kofs<WD>(c, j, g)) : make_uint4(0, 0, 0, 0);
                 else xv = xb[u][j];
-                acc = mfma(decode_a<WD>(rw[u], j), as_bf16x8(xv), acc);
+                acc = mfma(decode_a<WD>(rw[u], j, cs), as_bf16x8(xv), acc);
               }
             }
           }
@@ -580,9 +597,10 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
       for (int u = 0; u < UNROLL; ++u) {
         if (ts[u] != 0.f) {
           f32x4_t part = {0.f, 0.f, 0.f, 0.f};
+          const ChunkScale cs = chunk_scale<WD>(rw[u]);
   #pragma unroll
           for (int jj = 0; jj < NM; ++jj) {
-            const bf16x8_t a = decode_a<WD>(rw[u], jj);
+            const bf16x8_t a = decode_a<WD>(rw[u], jj, cs);
             part = mfma(a, as_bf16x8(bh[u][jj]), part);
             if constexpr (!PACK) part = mfma(a, as_bf16x8(bl[u][jj]), part);
           }

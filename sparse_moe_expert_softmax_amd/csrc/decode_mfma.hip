@@ -195,7 +195,6 @@ __device__ __forceinline__ bf16x8_t fp4x8_bf16_mul(uint32_t q, float s) {
   return r;
 }
 
-// A operand (weights) of MFMA j of a chunk.
 // A lane's block scale(s) for one chunk, converted once before the chunk's
 // products (MXFP4: one E8M0 scale; NVFP4: the E4M3 scales of its two blocks
 // of 16), not once per product.
@@ -212,6 +211,7 @@ __device__ __forceinline__ ChunkScale chunk_scale(const RawW<WD>& r) {
   }
 }
 
+// A operand (weights) of MFMA j of a chunk.
 template <int WD>
 __device__ __forceinline__ bf16x8_t decode_a(const RawW<WD>& r, int j, ChunkScale cs) {
   if constexpr (WD == FT_BF16) {

@@ -34,58 +34,53 @@ HBM_PEAK_GBS = 8000.0
 # Measured HBM bytes per ft_moe_forward call of the default decode workload
 # (bf16, H2048, E128, top-8, batch 1): rocprofv3 FETCH_SIZE and WRITE_SIZE of
 # the two decode kernels per call, scaled by what the same counters read for a
-# plain 256 MiB device copy (FETCH_SIZE x 1.9997, WRITE_SIZE x 1.0).  Keyed by the
-# SHA-256 prefix of the kernel source the counters were taken on: any change to
-# that source reports null until the counters are taken again.
-DECODE_TRAFFIC = {"67a01b1625890854": 75916447}
-DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_moe_expert_softmax_amd", "csrc",
-                          "decode_mfma.hip")
-# The same for the prefill workloads (8,192-token chunks: MXFP4 H4096 E256
-# top-6 in either activation mode, bf16 H2048 E128 top-8): every kernel of one
-# ft_moe_forward call, keyed by the workload, the activation terms of the
-# matrix-core path (1 for bf16 weights) and the prefixes of the sources the
-# workload's kernels come from.
+# plain 256 MiB device copy (FETCH_SIZE x 1.9997, WRITE_SIZE x 1.0).  Keyed by
+# one SHA-256 prefix over the kernel source and every header it includes: any
+# change to them reports null until the counters are taken again.
 _CSRC = os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "csrc")
+_HEADERS = [os.path.join(_CSRC, "common.hpp"), os.path.join(_CSRC, "internal.hpp"),
+            os.path.join(ROOT, "include", "ft_moe.h")]
+DECODE_SRCS = [os.path.join(_CSRC, f) for f in ("decode_mfma.hip", "topk.hpp")] + _HEADERS
+DECODE_TRAFFIC = {}
+# The same for the prefill workloads (8,192-token chunks: MXFP4 H4096 E256
+# top-6 in either activation mode, bf16 H2048 E128 top-8, NVFP4 H6144 E256
+# top-8): every kernel of one ft_moe_forward call, keyed by the workload, the
+# activation terms of the matrix-core path (1 for bf16 and NVFP4 weights) and
+# the prefix over the sources the workload's kernels come from.
 PREFILL_SRCS = {
     "prefill_mxfp4_h4096_e256": [os.path.join(_CSRC, f) for f in ("mfma.hip", "lds_dma.hpp", "permute.hip",
-                                                                   "gemv.hip")],
+                                                                   "gemv.hip")] + _HEADERS,
     "prefill_bf16_h2048_e128": [os.path.join(_CSRC, f) for f in ("prefill_bf16.hip", "mfma.hip", "lds_dma.hpp",
-                                                                  "permute.hip", "gemv.hip")],
+                                                                  "permute.hip", "gemv.hip")] + _HEADERS,
     "prefill_nvfp4_h6144_e256": [os.path.join(_CSRC, f) for f in ("prefill_bf16.hip", "mfma.hip", "lds_dma.hpp",
-                                                                   "permute.hip", "gemv.hip")],
+                                                                   "permute.hip", "gemv.hip")] + _HEADERS,
 }
 PREFILL_WORKLOADS = tuple(PREFILL_SRCS)
-_BH = ("21722fc7d9eb7cb4", "4db791fc00a312b7", "509e27cfdfa24281", "8564bd36b3d79a3c", "6d20609b6838d49c")
-PREFILL_TRAFFIC = {
-    ("prefill_mxfp4_h4096_e256", 2, "4db791fc00a312b7", "509e27cfdfa24281", "8564bd36b3d79a3c",
-     "6d20609b6838d49c"): 5685784994,
-    ("prefill_mxfp4_h4096_e256", 1, "4db791fc00a312b7", "509e27cfdfa24281", "8564bd36b3d79a3c",
-     "6d20609b6838d49c"): 4990800130,
-    ("prefill_bf16_h2048_e128", 1) + _BH: 2714547561,
-    ("prefill_nvfp4_h6144_e256", 1) + _BH: 10476768711,
-}
+PREFILL_TRAFFIC = {}
+
+
+def sources_hash(paths):
+    """SHA-256 prefix (16 hex digits) over the files' bytes, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_decode_traffic(cfg_name, batch):
-    import hashlib
     if cfg_name != "decode_bf16_h2048_e128" or batch != 1:
         return None
-    with open(DECODE_SRC, "rb") as f:
-        h = hashlib.sha256(f.read()).hexdigest()[:16]
-    return DECODE_TRAFFIC.get(h)
+    return DECODE_TRAFFIC.get(sources_hash(DECODE_SRCS))
 
 
 def measured_prefill_traffic(cfg_name, chunk_tokens, terms=2):
-    import hashlib
     if cfg_name not in PREFILL_WORKLOADS or chunk_tokens != 8192:
         return None
     if cfg_name != "prefill_mxfp4_h4096_e256":
         terms = 1
-    key = []
-    for p in PREFILL_SRCS[cfg_name]:
-        with open(p, "rb") as f:
-            key.append(hashlib.sha256(f.read()).hexdigest()[:16])
-    return PREFILL_TRAFFIC.get((cfg_name, terms) + tuple(key))
+    return PREFILL_TRAFFIC.get((cfg_name, terms, sources_hash(PREFILL_SRCS[cfg_name])))
 
 
 def parse():

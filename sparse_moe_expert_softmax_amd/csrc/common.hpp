@@ -68,9 +68,10 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t v) {
 // E4M3 (OCP FN: bias 7, no inf, S.1111.111 = NaN) -> fp32, by selects.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float sub = (float)m * 0.001953125f;                       // e == 0: m/8 * 2^-6
-  uint32_t mag = ((e + 120u) << 23) | (m << 20);                   // (1+m/8) * 2^(e-7)
-  mag = (e == 0u) ? __float_as_uint(sub) : mag;
+  const uint32_t sub = __float_as_uint((float)m * 0.001953125f);   // e == 0: m/8 * 2^-6
+  const uint32_t nrm = ((e + 120u) << 23) | (m << 20);             // (1+m/8) * 2^(e-7)
+  const uint32_t keep = 0u - (uint32_t)(e != 0u);                  // a mask blend, not a branch
+  uint32_t mag = (nrm & keep) | (sub & ~keep);
   mag = (e == 15u && m == 7u) ? 0x7FC00000u : mag;
   return __uint_as_float(mag | ((c & 0x80u) << 24));
 }

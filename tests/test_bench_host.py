@@ -55,8 +55,12 @@ def test_traffic_tables_are_keyed_by_source_hashes():
         assert len(key) == 16 and int(key, 16) >= 0 and v > 0
     for key, v in bench.PREFILL_TRAFFIC.items():
         assert key[0] in bench.PREFILL_WORKLOADS and key[1] in (1, 2)
-        assert len(key) == len(bench.PREFILL_SRCS[key[0]]) + 2
-        assert all(len(h) == 16 for h in key[2:]) and v > 0
+        assert len(key) == 3 and len(key[2]) == 16 and int(key[2], 16) >= 0 and v > 0
+    # the keys cover the headers the kernels include, not only their .hip files
+    for srcs in [bench.DECODE_SRCS] + list(bench.PREFILL_SRCS.values()):
+        names = [os.path.basename(p) for p in srcs]
+        assert "common.hpp" in names and "internal.hpp" in names and "ft_moe.h" in names
+        assert all(os.path.exists(p) for p in srcs)
     # a figure, when reported, is within a few per cent of the workload's design bytes
     d = bench.measured_decode_traffic("decode_bf16_h2048_e128", 1)
     if d is not None:

@@ -82,6 +82,7 @@ FwdPlan plan_forward(const ft_moe_desc& d, int T) {
   p.off_cnt = o;     o = align256(o + sizeof(uint32_t) * (size_t)(p.H / 16 + 1));
   p.off_h = o;       o = align256(o + sizeof(float) * (size_t)p.P * p.I);   // fp32 h, bf16 (hi/lo), or MXFP8 codes
   p.off_y = o;       o = align256(o + (p.mfma ? 2 : 4) * (size_t)p.P * p.H);  // bf16 y on the matrix-core paths
+  p.off_dtab = o;    o = align256(o + (p.path == PATH_DEC ? DEC_DTAB_BYTES : 0));
   if (bf) {
     p.off_xq = p.off_xs = p.off_hs = o;
     p.off_tiles = o; o = align256(o + sizeof(int32_t) * ((size_t)2 * p.max_tiles + 1 +

@@ -111,6 +111,59 @@ __device__ __forceinline__ void dm_group_pairs(const int32_t* __restrict__ ids, 
   }
 }
 
+constexpr int DD_WAVES = 16;
+constexpr int DD_THREADS = DD_WAVES * 64;
+constexpr int DD_MAXT = 16;  // token columns of the accumulator
+constexpr int DD_MAX_GRID = 256;  // down-projection workgroups at most (one per CU)
+
+struct DownInfo {
+  int n_distinct;
+  int slot[DEC_MAX_PAIRS];                 // record slot of each distinct expert (-1: failed lookup)
+  int pair[DEC_MAX_PAIRS][DD_MAXT];        // pair index of (expert d, token t), -1 if t not routed to d
+};
+
+// One wave: every kept (expert, token) pair, grouped by (expert, occurrence)
+// in order of first appearance.  A group holds at most one pair per token:
+// a token that lists an expert twice puts its second pair in a group of its
+// own (same expert and slot), so every pair's term reaches the output.
+__device__ __forceinline__ void dd_group_all(const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask,
+                                             const int32_t* __restrict__ slot_ids, int P, int k, int E,
+                                             DownInfo* di) {
+  const int lane = threadIdx.x & 63;
+  int e = -1;
+  bool valid = false;
+  if (lane < P) {
+    e = ids[lane];
+    valid = e >= 0 && e < E && dm_in_mask(mask, e);
+  }
+  // occurrence of e among this token's earlier ranks
+  const int j = lane % k;
+  int occ = 0;
+  for (int jj = 1; jj < k; ++jj) {
+    const int prev = __shfl(e, lane - jj, 64);
+    occ += (jj <= j && prev == e) ? 1 : 0;
+  }
+  const int key = valid ? (e | (occ << 16)) : -1;
+  for (int q = lane; q < DEC_MAX_PAIRS * DD_MAXT; q += 64) (&di->pair[0][0])[q] = -1;
+  uint64_t todo = __ballot(valid);
+  int n = 0;
+  int my_d = -1;
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const int el = __builtin_amdgcn_readlane(e, leader);
+    const int kl = __builtin_amdgcn_readlane(key, leader);
+    const uint64_t m = __ballot(valid && key == kl);
+    if ((m >> lane) & 1ull) my_d = n;
+    if (lane == leader) di->slot[n] = slot_ids ? slot_ids[leader] : el;
+    todo &= ~m;
+    ++n;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  if (valid) di->pair[my_d][lane / k] = lane;
+  if (lane == 0) di->n_distinct = n;
+}
+
 // ------------------------------------------------------------ weight tiles --
 // Chunk = the K extent one lane group covers per step: 64 for bf16 (two
 // MFMAs, 8 contiguous K each), 128 for the fp4 formats (one 32-element block
@@ -271,7 +324,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P,
     int k, const void* __restrict__ pool, int64_t stride, const int32_t* __restrict__ slot_ids,
     const float* __restrict__ gates, uint16_t* __restrict__ hbuf, float* __restrict__ out, int T, int H, int I,
-    int E, DecRoute route, int ntw) {
+    int E, DecRoute route, int ntw, DownInfo* __restrict__ dtab) {
   __shared__ PairInfo pi;
   __shared__ f32x4_t red[DM_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
@@ -284,6 +337,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
   if constexpr (!XL) ntw = 1;
   const int n_rtg = I / 8 / ntw;
   const int d = blockIdx.x / n_rtg, rt0 = (blockIdx.x % n_rtg) * ntw;
+  bool ranked = false;  // one token ranked by the whole workgroup (below)
   if constexpr (RPER > 0) {
     __shared__ int32_t s_ids[DEC_MAX_PAIRS];
     __shared__ float s_gates[DEC_MAX_PAIRS];
@@ -291,9 +345,9 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     // experts (its LDS scratch is the reduction buffer, unused until the
     // streaming loop ends); else, or where high halves tie, a wave per token
     static_assert(sizeof(red) >= 3364, "selection scratch");
-    const bool ranked = (T == 1 && route.renormalize) &&
-                        topk_wg_one_token<RPER, DM_THREADS>(route.logits, route.sel_bias, E, k, s_ids, s_gates,
-                                                            reinterpret_cast<unsigned char*>(&red[0][0]));
+    ranked = (T == 1 && route.renormalize) &&
+             topk_wg_one_token<RPER, DM_THREADS>(route.logits, route.sel_bias, E, k, s_ids, s_gates,
+                                                 reinterpret_cast<unsigned char*>(&red[0][0]));
     if (!ranked)
       for (int t = wv; t < T; t += DM_WAVES)
         topk_one_token<RPER>(route.logits + (int64_t)t * E, route.sel_bias ? route.sel_bias + (int64_t)t * E : nullptr,
@@ -307,7 +361,26 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     ids = s_ids;
     gates = s_gates;
   }
-  if (wv == 0) dm_group_pairs(ids, mask, P, k, E, d, &pi);
+  if (ranked && mask == nullptr) {
+    // one token, no mask: pair j is rank j, and the k ranked experts are
+    // distinct, so group d is pair d alone (what dm_group_pairs would find,
+    // without its serial ballot rounds)
+    if (tid == 0) {
+      pi.n_distinct = k;
+      pi.expert = (d < k) ? ids[d] : -1;
+      pi.npairs = 1;
+      pi.ntok = 1;
+      pi.pair[0] = (uint8_t)d;
+      pi.rank[0] = 0;
+      pi.tok[0] = 0;
+    }
+  } else if (wv == 0) {
+    dm_group_pairs(ids, mask, P, k, E, d, &pi);
+  }
+  // the down kernel's grouping, built here beside wave 0's so that the down
+  // kernel starts its weight loads after one table copy instead of a
+  // dependent load of the ids and the grouping rounds
+  if (blockIdx.x == 0 && wv == 1) dd_group_all(ids, mask, slot_ids, P, k, E, dtab);
   __syncthreads();
   if (d >= pi.n_distinct) return;
   const int e = pi.expert, np = pi.npairs;
@@ -481,72 +554,21 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
 }
 
 // ---------------------------------------------------------- down + combine --
-constexpr int DD_WAVES = 16;
-constexpr int DD_THREADS = DD_WAVES * 64;
-constexpr int DD_MAXT = 16;  // token columns of the accumulator
-constexpr int DD_MAX_GRID = 256;  // down-projection workgroups at most (one per CU)
-
-struct DownInfo {
-  int n_distinct;
-  int slot[DEC_MAX_PAIRS];                 // record slot of each distinct expert (-1: failed lookup)
-  int pair[DEC_MAX_PAIRS][DD_MAXT];        // pair index of (expert d, token t), -1 if t not routed to d
-};
-
-// Wave 0: every kept (expert, token) pair, grouped by (expert, occurrence)
-// in order of first appearance.  A group holds at most one pair per token:
-// a token that lists an expert twice puts its second pair in a group of its
-// own (same expert and slot), so every pair's term reaches the output.
-__device__ __forceinline__ void dd_group_all(const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask,
-                                             const int32_t* __restrict__ slot_ids, int P, int k, int E,
-                                             DownInfo* di) {
-  const int lane = threadIdx.x & 63;
-  int e = -1;
-  bool valid = false;
-  if (lane < P) {
-    e = ids[lane];
-    valid = e >= 0 && e < E && dm_in_mask(mask, e);
-  }
-  // occurrence of e among this token's earlier ranks
-  const int j = lane % k;
-  int occ = 0;
-  for (int jj = 1; jj < k; ++jj) {
-    const int prev = __shfl(e, lane - jj, 64);
-    occ += (jj <= j && prev == e) ? 1 : 0;
-  }
-  const int key = valid ? (e | (occ << 16)) : -1;
-  for (int q = lane; q < DEC_MAX_PAIRS * DD_MAXT; q += 64) (&di->pair[0][0])[q] = -1;
-  uint64_t todo = __ballot(valid);
-  int n = 0;
-  int my_d = -1;
-  while (todo) {
-    const int leader = __ffsll((unsigned long long)todo) - 1;
-    const int el = __builtin_amdgcn_readlane(e, leader);
-    const int kl = __builtin_amdgcn_readlane(key, leader);
-    const uint64_t m = __ballot(valid && key == kl);
-    if ((m >> lane) & 1ull) my_d = n;
-    if (lane == leader) di->slot[n] = slot_ids ? slot_ids[leader] : el;
-    todo &= ~m;
-    ++n;
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  if (valid) di->pair[my_d][lane / k] = lane;
-  if (lane == 0) di->n_distinct = n;
-}
-
 // PACK (T <= 8): the MFMA's 16 token columns carry h's hi terms in columns
 // 0 .. T-1 and its lo terms in columns T .. 2T-1, so one product per K slice
 // covers both (and every h load fills twice the lanes); the two column
 // groups are added once at the end.  Otherwise hi and lo take a product each.
 template <int WD, int UNROLL, bool PACK>
 __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
-    const uint16_t* __restrict__ hbuf, const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P,
-    int k, const void* __restrict__ pool, int64_t stride, const int32_t* __restrict__ slot_ids,
-    float* __restrict__ out, int T, int H, int I, int E) {
+    const uint16_t* __restrict__ hbuf, const DownInfo* __restrict__ dtab, const void* __restrict__ pool,
+    int64_t stride, float* __restrict__ out, int T, int H, int I) {
   __shared__ DownInfo di;
   __shared__ f32x4_t red[DD_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
-  if (wv == 0) dd_group_all(ids, mask, slot_ids, P, k, E, &di);
+  // the grouping the gate/up kernel's first workgroup stored
+  static_assert(sizeof(DownInfo) % 4 == 0 && sizeof(DownInfo) <= DEC_DTAB_BYTES, "down table");
+  for (int q = tid; q < (int)(sizeof(DownInfo) / 4); q += DD_THREADS)
+    reinterpret_cast<int32_t*>(&di)[q] = reinterpret_cast<const int32_t*>(dtab)[q];
   __syncthreads();
   const int nd = di.n_distinct;
   constexpr int CK = Chunk<WD>::K, NM = Chunk<WD>::NM;
@@ -666,6 +688,7 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
                                 float* out, char* ws, const DecRoute& route, hipStream_t st) {
   const int H = d.hidden, I = d.inter, E = d.n_experts, k = d.top_k;
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + pl.off_h);
+  DownInfo* dtab = reinterpret_cast<DownInfo*>(ws + pl.off_dtab);
   const size_t xl_bytes = dec_xl_bytes(pl.T, H);
   const DecGateupShape shp = dec_gateup_shape(d, pl.T);
   const bool xl = shp.xl;
@@ -677,16 +700,16 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
   do {                                                                                               \
     if (rper == 0)                                                                                   \
       dec_gateup_kernel<WD, UN, XL_, GRP_, 0><<<grid, DM_THREADS, SH, st>>>(                         \
-          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw); \
+          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw, dtab); \
     else if (rper == 1)                                                                              \
       dec_gateup_kernel<WD, UN, XL_, GRP_, 1><<<grid, DM_THREADS, SH, st>>>(                         \
-          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw); \
+          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw, dtab); \
     else if (rper == 2)                                                                              \
       dec_gateup_kernel<WD, UN, XL_, GRP_, 2><<<grid, DM_THREADS, SH, st>>>(                         \
-          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw); \
+          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw, dtab); \
     else                                                                                             \
       dec_gateup_kernel<WD, UN, XL_, GRP_, 4><<<grid, DM_THREADS, SH, st>>>(                         \
-          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw); \
+          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw, dtab); \
   } while (0)
   bool done = false;
   if constexpr (WD != FT_BF16) {
@@ -704,17 +727,14 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
 #undef DM_GATEUP
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int32_t* ids_down = route.logits ? route.ids_out : ids;  // the selection the gate/up kernel stored
-  constexpr int DU = (WD == FT_BF16) ? 3 : 2;
   // one workgroup of 16 waves per CU: cap the grid at the CU count and let
   // each workgroup loop over its (tile, half) items
   const unsigned dgrid = (H / 16) * 2 < DD_MAX_GRID ? (H / 16) * 2 : DD_MAX_GRID;
+  constexpr int DU = (WD == FT_BF16) ? 3 : 2;
   if (pl.T <= 8)
-    dec_down_kernel<WD, DU, true><<<dgrid, DD_THREADS, 0, st>>>(hbuf, ids_down, mask, pl.P, k, pool, d.expert_stride,
-                                                                 slot_ids, out, pl.T, H, I, E);
+    dec_down_kernel<WD, DU, true><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H, I);
   else
-    dec_down_kernel<WD, DU, false><<<dgrid, DD_THREADS, 0, st>>>(hbuf, ids_down, mask, pl.P, k, pool, d.expert_stride,
-                                                                  slot_ids, out, pl.T, H, I, E);
+    dec_down_kernel<WD, DU, false><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H, I);
   return hipGetLastError();
 }
 

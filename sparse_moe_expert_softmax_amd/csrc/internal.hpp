@@ -38,6 +38,7 @@ int slot_max_experts();
 // forward paths
 enum FwdPath { PATH_DEC = 0, PATH_GEMV = 1, PATH_MFMA = 2 };
 constexpr int DEC_MAX_PAIRS = 64;  // decode path: T*k pairs grouped inside the kernels
+constexpr size_t DEC_DTAB_BYTES = 8192;  // decode path: the down kernel's (expert, token) table, built by gate/up
 
 // forward workspace: every region 256-byte aligned
 struct FwdPlan {
@@ -48,6 +49,7 @@ struct FwdPlan {
   int terms;                   // MXFP8 terms per activation on the MXFP4 path (1 or 2); 1 on the bf16 path
   size_t off_hist, off_offsets, off_active, off_perm, off_pos, off_h, off_y, off_xq, off_xs, off_hs, off_cnt;
   size_t off_tiles;            // MFMA path: tile list (2 ints per tile) + count
+  size_t off_dtab;             // decode path: DEC_DTAB_BYTES
   int max_tiles;               // upper bound of (expert, row chunk) tiles: P/(256/terms) + E + 1
   size_t bytes;
 };

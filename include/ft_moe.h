@@ -320,7 +320,7 @@ int ft_moe_add_partial(float* out, const float* part, int64_t n, void* stream);
  * resident at its own slot (slot = expert id), for callers whose pool holds
  * all experts: the results (topk_ids, topk_gates, out) are bitwise those of
  * the two calls.  For decode-sized calls (at most 16 tokens on the grouped
- * GEMV path, at most 256 experts, a gate/up grid of at most 1,024
+ * GEMV path, at most 128 experts, a gate/up grid of at most 1,024
  * workgroups: min(T k, E) experts x I/8 row tiles, halved where two tiles
  * share a workgroup) the selection runs inside the gate/up kernel instead of
  * as a launch of its own (the routing rule itself is unchanged: pages,

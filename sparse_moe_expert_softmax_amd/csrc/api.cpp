@@ -308,7 +308,8 @@ int ft_moe_route_forward(const ft_moe_desc* desc, const void* x, int32_t n_token
   // workgroup: bf16 2048/768/128 top-8 measured 1.108 against 1.152 ms per
   // 40 layers at 1 token (768 workgroups), and 1.762 against 1.726 ms at 2
   // tokens, 3.097 against 2.867 ms at 4 (1,536 and 3,072 workgroups)
-  const bool fuse = pl.path == ft::PATH_DEC && n_tokens <= ft::ROUTE_DECODE_MAX_T && desc->n_experts <= 256 &&
+  const bool fuse = pl.path == ft::PATH_DEC && n_tokens <= ft::ROUTE_DECODE_MAX_T &&
+                    desc->n_experts <= ft::DEC_FUSE_MAX_E &&
                     ft::dec_gateup_shape(*desc, n_tokens).grid <= ft::DEC_FUSE_MAX_GRID;
   if (!fuse) {
     rc = ft_moe_route(desc, x, n_tokens, w_router, sel_bias, topk_ids, topk_gates, nullptr, rws, rbytes, stream);

@@ -704,11 +704,8 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
     else if (rper == 1)                                                                              \
       dec_gateup_kernel<WD, UN, XL_, GRP_, 1><<<grid, DM_THREADS, SH, st>>>(                         \
           xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw, dtab); \
-    else if (rper == 2)                                                                              \
-      dec_gateup_kernel<WD, UN, XL_, GRP_, 2><<<grid, DM_THREADS, SH, st>>>(                         \
-          xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw, dtab); \
     else                                                                                             \
-      dec_gateup_kernel<WD, UN, XL_, GRP_, 4><<<grid, DM_THREADS, SH, st>>>(                         \
+      dec_gateup_kernel<WD, UN, XL_, GRP_, 2><<<grid, DM_THREADS, SH, st>>>(                         \
           xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw, dtab); \
   } while (0)
   bool done = false;

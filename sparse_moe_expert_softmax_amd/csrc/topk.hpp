@@ -174,7 +174,7 @@ __device__ void topk_core(const double (&lv)[PER], const double (&sv)[PER], bool
 }
 
 template <int PER>
-__device__ void topk_one_token(const double* __restrict__ lt, const float* __restrict__ bias_t, int E, int k,
+__device__ __forceinline__ void topk_one_token(const double* __restrict__ lt, const float* __restrict__ bias_t, int E, int k,
                                int renormalize, int32_t* __restrict__ ids_t, float* __restrict__ gates_t) {
   const int lane = threadIdx.x & 63;
   double lv[PER], sv[PER];
@@ -213,7 +213,7 @@ __device__ void topk_one_token(const double* __restrict__ lt, const float* __res
 // so every result is bitwise that of topk_one_token.  `scr`: 3,364 bytes of
 // LDS the caller does not need meanwhile.  All NTHR threads call it together.
 template <int PER, int NTHR>
-__device__ bool topk_wg_one_token(const double* __restrict__ lt, const float* __restrict__ bias_t, int E, int k,
+__device__ __forceinline__ bool topk_wg_one_token(const double* __restrict__ lt, const float* __restrict__ bias_t, int E, int k,
                                   int32_t* __restrict__ ids_t, float* __restrict__ gates_t, unsigned char* scr) {
   constexpr int EP = 64 * PER, NT = NTHR / EP, SPAN = EP / NT;
   static_assert(NT * EP == NTHR && SPAN % 4 == 0 && EP <= 256, "workgroup shape");
@@ -235,12 +235,21 @@ __device__ bool topk_wg_one_token(const double* __restrict__ lt, const float* __
   if (tid < k) s_win[tid] = -1;
   if (tid == 0) *s_bad = 0;
   __syncthreads();
+  // eight 16-byte broadcast reads in flight, then their compares (left to
+  // itself the compiler waited for each read before the next one: 64
+  // serialised LDS round trips at 256 experts)
+  constexpr int NQ = SPAN / 4, QB = NQ < 8 ? NQ : 8;
+  static_assert(NQ % QB == 0, "batches");
   int cnt = 0;
   const uint4* h4 = reinterpret_cast<const uint4*>(s_hi + part * SPAN);
 #pragma unroll
-  for (int q = 0; q < SPAN / 4; ++q) {
-    const uint4 v = h4[q];
-    cnt += (v.x > hi ? 1 : 0) + (v.y > hi ? 1 : 0) + (v.z > hi ? 1 : 0) + (v.w > hi ? 1 : 0);
+  for (int q0 = 0; q0 < NQ; q0 += QB) {
+    uint4 v[QB];
+#pragma unroll
+    for (int u = 0; u < QB; ++u) v[u] = h4[q0 + u];
+#pragma unroll
+    for (int u = 0; u < QB; ++u)
+      cnt += (v[u].x > hi ? 1 : 0) + (v[u].y > hi ? 1 : 0) + (v[u].z > hi ? 1 : 0) + (v[u].w > hi ? 1 : 0);
   }
   s_cnt[tid] = cnt;
   __syncthreads();

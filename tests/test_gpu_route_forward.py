@@ -7,7 +7,7 @@ halved when two tiles share a workgroup) stays within 1,024 workgroups, the
 selection runs inside the gate/up kernel; otherwise the entry point runs the
 two calls in sequence.  Both branches are covered: the *_SM shapes below keep
 several tokens, a selection bias, a partition mask and full-softmax gates on
-the in-kernel branch."""
+the in-kernel branch, which takes layers of at most 128 experts."""
 import numpy as np
 import pytest
 import torch
@@ -60,8 +60,10 @@ def test_fused_bf16_decode_matches_separate_calls(T):
     fused_vs_separate(C2, T, 100 + T)
 
 
-@pytest.mark.parametrize("cfg,T", [(C3, 1), (C3, 3), (MX_SM, 3)])
+@pytest.mark.parametrize("cfg,T", [(C2, 1), (C3, 1), (C3, 3), (MX_SM, 3)])
 def test_fused_mxfp4_decode_with_selection_bias(cfg, T):
+    """(C2 at one token: the workgroup-wide ranking with a bias; C3 has 256
+    experts, above the in-kernel selection's limit: the two calls.)"""
     print(f"fused {cfg.name} T={T} with selection bias", flush=True)
     bias = np.random.default_rng(3 + T).normal(0.0, 0.5, (T, cfg.n_experts))
     fused_vs_separate(cfg, T, 110 + T, bias=bias)

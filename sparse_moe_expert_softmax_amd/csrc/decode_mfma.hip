@@ -727,7 +727,10 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
   // one workgroup of 16 waves per CU: cap the grid at the CU count and let
   // each workgroup loop over its (tile, half) items
   const unsigned dgrid = (H / 16) * 2 < DD_MAX_GRID ? (H / 16) * 2 : DD_MAX_GRID;
-  constexpr int DU = (WD == FT_BF16) ? 3 : 2;
+  // three jobs' loads per wave and pass for every format (fp4, per-call
+  // forwards: two 40.4 / 232.7 us, three 39.7 / 229.6, four 39.8 / 232.7,
+  // five spill; MXFP4 4096/2048/256 at one token, NVFP4 6144/2048/256 at four)
+  constexpr int DU = 3;
   if (pl.T <= 8)
     dec_down_kernel<WD, DU, true><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H, I);
   else

@@ -67,9 +67,13 @@ __device__ __forceinline__ bool dm_in_mask(const uint32_t* mask, int e) {
 
 // Wave 0: group the P <= 64 pairs by expert; the d-th group in order of first
 // appearance goes to this workgroup.  Any fixed order works: d only chooses
-// which workgroup computes which expert.
+// which workgroup computes which expert.  A pair starts a group when it is
+// its expert's lowest pair: an LDS atomic minimum per expert (in `scr`, room
+// for scr_n expert ids the caller does not need meanwhile) finds that in
+// three LDS round trips, where one ballot round per distinct expert took up
+// to 32 rounds; layers with more experts than scr_n take the rounds.
 __device__ __forceinline__ void dm_group_pairs(const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask,
-                                               int P, int k, int E, int d, PairInfo* pi) {
+                                               int P, int k, int E, int d, PairInfo* pi, int* scr, int scr_n) {
   const int lane = threadIdx.x & 63;
   int e = -1;
   bool valid = false;
@@ -77,17 +81,35 @@ __device__ __forceinline__ void dm_group_pairs(const int32_t* __restrict__ ids, 
     e = ids[lane];
     valid = e >= 0 && e < E && dm_in_mask(mask, e);
   }
-  uint64_t todo = __ballot(valid);
   int n = 0;
   uint64_t mine = 0;
   int my_e = -1;
-  while (todo) {
-    const int leader = __ffsll((unsigned long long)todo) - 1;
-    const int el = __builtin_amdgcn_readlane(e, leader);
-    const uint64_t m = __ballot(valid && e == el);
-    if (n == d) { mine = m; my_e = el; }
-    todo &= ~m;
-    ++n;
+  if (E <= scr_n) {
+    if (valid) scr[e] = 64;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stores land before the minima
+    __builtin_amdgcn_wave_barrier();
+    if (valid) atomicMin(&scr[e], lane);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    const bool lead = valid && scr[e] == lane;
+    const uint64_t fm = __ballot(lead);
+    const uint64_t blw = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    n = __popcll(fm);
+    const uint64_t ld = __ballot(lead && __popcll(fm & blw) == d);  // the lane that starts group d
+    if (ld) {
+      my_e = __builtin_amdgcn_readlane(e, __builtin_ctzll(ld));
+      mine = __ballot(valid && e == my_e);
+    }
+  } else {
+    uint64_t todo = __ballot(valid);
+    while (todo) {
+      const int leader = __ffsll((unsigned long long)todo) - 1;
+      const int el = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t m = __ballot(valid && e == el);
+      if (n == d) { mine = m; my_e = el; }
+      todo &= ~m;
+      ++n;
+    }
   }
   // pairs ascend, so their tokens do not decrease; a pair is its token's
   // first when no pair of the same token sits below it (a token lists an
@@ -375,7 +397,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
       pi.tok[0] = 0;
     }
   } else if (wv == 0) {
-    dm_group_pairs(ids, mask, P, k, E, d, &pi);
+    dm_group_pairs(ids, mask, P, k, E, d, &pi, reinterpret_cast<int*>(&red[0][0]), (int)(sizeof(red) / sizeof(int)));
   }
   // the down kernel's grouping, built here beside wave 0's so that the down
   // kernel starts its weight loads after one table copy instead of a
@@ -727,14 +749,15 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
   // one workgroup of 16 waves per CU: cap the grid at the CU count and let
   // each workgroup loop over its (tile, half) items
   const unsigned dgrid = (H / 16) * 2 < DD_MAX_GRID ? (H / 16) * 2 : DD_MAX_GRID;
-  // three jobs' loads per wave and pass for every format (fp4, per-call
-  // forwards: two 40.4 / 232.7 us, three 39.7 / 229.6, four 39.8 / 232.7,
-  // five spill; MXFP4 4096/2048/256 at one token, NVFP4 6144/2048/256 at four)
-  constexpr int DU = 3;
+  // three jobs' loads per wave and pass (fp4, per-call forwards: two 40.4 /
+  // 232.7 us, three 39.7 / 229.6, four 39.8 / 232.7, five spill; MXFP4
+  // 4096/2048/256 at one token, NVFP4 6144/2048/256 at four); two for fp4
+  // without the packed h columns (its separate lo loads spill at three)
+  constexpr int DU = 3, DUL = (WD == FT_BF16) ? 3 : 2;
   if (pl.T <= 8)
     dec_down_kernel<WD, DU, true><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H, I);
   else
-    dec_down_kernel<WD, DU, false><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H, I);
+    dec_down_kernel<WD, DUL, false><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H, I);
   return hipGetLastError();
 }
 

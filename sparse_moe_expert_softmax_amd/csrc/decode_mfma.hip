@@ -696,7 +696,7 @@ DecGateupShape dec_gateup_shape(const ft_moe_desc& d, int T) {
   DecGateupShape sh;
   const bool many = (int64_t)nd_max * (I / 8) >= 2 * DM_MERGE_MIN && (I / 8) % 2 == 0;
   if (d.w_dtype == FT_BF16)
-    sh.xl = many && dec_xl_bytes(T, H) <= 56 * 1024 && nchunk % 32 == 0;  // one pass of 8 chunks per wave at H 2048
+    sh.xl = many && dec_xl_bytes(T, H) <= 56 * 1024 && nchunk % 16 == 0;
   else
     sh.xl = dec_xl_bytes(T, H) <= 56 * 1024 && nchunk % 16 == 0;
   sh.ntw = (sh.xl && many) ? 2 : 1;
@@ -730,19 +730,13 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
       dec_gateup_kernel<WD, UN, XL_, GRP_, 2><<<grid, DM_THREADS, SH, st>>>(                         \
           xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw, dtab); \
   } while (0)
-  bool done = false;
-  if constexpr (WD != FT_BF16) {
-    if (xl) {
-      DM_GATEUP(4, true, true, xl_bytes);
-      done = true;
-    }
-  } else {
-    if (xl) {
-      DM_GATEUP(8, true, true, xl_bytes);
-      done = true;
-    }
-  }
-  if (!done) DM_GATEUP((WD == FT_BF16) ? 6 : 4, false, false, 0);
+  // staged loop: four chunks per wave and pass (bf16 at H 2048: two passes
+  // at 74 VGPRs, six waves per SIMD, measured 0.5-1% faster than one pass of
+  // eight at 110 VGPRs, four waves per SIMD)
+  if (xl)
+    DM_GATEUP(4, true, true, xl_bytes);
+  else
+    DM_GATEUP((WD == FT_BF16) ? 6 : 4, false, false, 0);
 #undef DM_GATEUP
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -41,7 +41,7 @@ _CSRC = os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "csrc")
 _HEADERS = [os.path.join(_CSRC, "common.hpp"), os.path.join(_CSRC, "internal.hpp"),
             os.path.join(ROOT, "include", "ft_moe.h")]
 DECODE_SRCS = [os.path.join(_CSRC, f) for f in ("decode_mfma.hip", "topk.hpp")] + _HEADERS
-DECODE_TRAFFIC = {}
+DECODE_TRAFFIC = {"22297064b70d47e7": 75965101}
 # The same for the prefill workloads (8,192-token chunks: MXFP4 H4096 E256
 # top-6 in either activation mode, bf16 H2048 E128 top-8, NVFP4 H6144 E256
 # top-8): every kernel of one ft_moe_forward call, keyed by the workload, the
@@ -56,7 +56,12 @@ PREFILL_SRCS = {
                                                                    "permute.hip", "gemv.hip")] + _HEADERS,
 }
 PREFILL_WORKLOADS = tuple(PREFILL_SRCS)
-PREFILL_TRAFFIC = {}
+PREFILL_TRAFFIC = {
+    ("prefill_mxfp4_h4096_e256", 2, "fede5405306ea7b4"): 5699135373,
+    ("prefill_mxfp4_h4096_e256", 1, "fede5405306ea7b4"): 4989481371,
+    ("prefill_bf16_h2048_e128", 1, "7d8e1e5fe1ebc036"): 2705608519,
+    ("prefill_nvfp4_h6144_e256", 1, "7d8e1e5fe1ebc036"): 10380571040,
+}
 
 
 def sources_hash(paths):

@@ -125,7 +125,11 @@ __global__ void __launch_bounds__(256) route_decode_kernel(const void* __restric
       }
     }
   }
-  const double r = multi_reduce<NT>(acc);
+  // one token: a fixed-order wave sum by DPP row operations (a few cycles
+  // per step) instead of six dependent LDS permutes
+  double r;
+  if constexpr (NT == 1) r = tk_wave_sum_f64(acc[0]);
+  else r = multi_reduce<NT>(acc);
   constexpr int SH = (NT == 1) ? 6 : (NT == 2) ? 5 : (NT == 4) ? 4 : (NT == 8) ? 3 : 2;
   if ((lane & ((1 << SH) - 1)) == 0) part[wv][lane >> SH] = r;
   __syncthreads();

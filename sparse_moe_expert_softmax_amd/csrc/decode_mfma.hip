@@ -326,13 +326,15 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 //       byte loads per chunk.
 // Weight scales of MXFP4 for chunk c, lane group g: byte 4c + g of the row;
 // NVFP4: bytes 8c + 2g and 8c + 2g + 1.
-// In-kernel routing for the fused route + forward call: the fp64 logits come
-// from the router's logit kernel; every gate/up workgroup selects the top-k
-// of each token itself (one wave per token) instead of waiting for a separate
-// selection launch, and workgroup 0 stores the selection as the call's
-// outputs.  logits == nullptr: ids and gates are inputs.  The kernel is
-// instantiated per logits-per-lane count (E <= 64 * RPER) so that the
-// selection code does not raise the register count of the streaming loop.
+// In-kernel routing for the fused route + forward call (at most 128
+// experts): the fp64 logits come from the router's logit kernel; every
+// gate/up workgroup selects the top-k of each token itself instead of waiting
+// for a separate selection launch (one token with renormalised gates: all
+// four waves rank the experts; otherwise one wave per token), and workgroup 0
+// stores the selection as the call's outputs.  logits == nullptr: ids and
+// gates are inputs.  The kernel is instantiated per logits-per-lane count
+// (E <= 64 * RPER) so that the selection code does not raise the register
+// count of the streaming loop.
 struct DecRoute {
   const double* logits;   // [T, E] fp64
   const float* sel_bias;  // [T, E] selection-only bias, nullable

@@ -80,6 +80,21 @@ def test_fused_nvfp4_decode_with_partition_mask(cfg):
         assert max_rel_err(f_out.cpu().numpy(), ref) <= 1e-2
 
 
+def test_fused_one_token_ranked_with_partition_masks():
+    """One token ranked by the whole workgroup, with a partition mask (the
+    grouping then takes the general path): each part against the separate
+    calls bit for bit, the two parts summing to the full output."""
+    cfg = C2
+    print("fused C2 T=1 with masks", flush=True)
+    m = np.array([0xF0F0F0F0, 0x0F0F0F0F, 0xAAAA5555, 0x12345678], dtype=np.uint32)
+    ld, _, _, part_a = fused_vs_separate(cfg, 1, 160, mask=m)
+    _, _, _, part_b = fused_vs_separate(cfg, 1, 160, mask=~m)
+    _, _, _, full = fused_vs_separate(cfg, 1, 160)
+    ref, _, _ = ld.oracle_layer()
+    assert max_rel_err((part_a + part_b).cpu().numpy(), ref) <= 1e-3
+    assert max_rel_err(full.cpu().numpy(), ref) <= 1e-3
+
+
 def test_fused_full_softmax_gates_and_oracle():
     """renormalize off (gates are full-softmax probabilities), 16 tokens:
     the largest decode batch the fused kernel selects for."""

@@ -417,7 +417,7 @@ def _measure_decode_bf16(args, cfg, torch, B, pools, routers, desc, calibrate):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "bench.py measures one GPU: the path runs on one device, and --gpus above 1 is not supported",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

@@ -45,6 +45,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 constexpr int DM_WAVES = 4;
 constexpr int DM_MERGE_MIN = 768;  // gate/up workgroups: merge tile pairs only if this many remain
 constexpr int DM_THREADS = DM_WAVES * 64;
+constexpr int DEC_RED8_BYTES = 2 * DM_WAVES * 64 * 16;  // eight waves' partials (f32x4 per lane)
 
 // Pairs routed to this workgroup's expert, derived from the ids in LDS.
 struct PairInfo {
@@ -343,17 +344,32 @@ struct DecRoute {
   int renormalize;
 };
 
-template <int WD, int UNROLL, bool XL, bool GRP, int RPER>
-__global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
+// NW: waves per workgroup.  4: the workgroup's tiles run one after the other
+// on all four waves.  8 (staged activations, two tiles): each tile runs on
+// its own four waves, side by side, so the one staged copy of the
+// activation rows serves twice the waves (NVFP4 at hidden 6144 and four
+// tokens stages 49 KB per workgroup, which caps a CU at three workgroups).
+template <int WD, int UNROLL, bool XL, bool GRP, int RPER, int NW>
+__global__ void __launch_bounds__(NW * 64) dec_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const uint32_t* __restrict__ mask, int P,
     int k, const void* __restrict__ pool, int64_t stride, const int32_t* __restrict__ slot_ids,
     const float* __restrict__ gates, uint16_t* __restrict__ hbuf, float* __restrict__ out, int T, int H, int I,
     int E, DecRoute route, int ntw, DownInfo* __restrict__ dtab) {
+  static_assert(NW == DM_WAVES || (NW == 2 * DM_WAVES && XL && GRP && RPER == 0), "eight waves: staged loop");
+  constexpr int NTH = NW * 64;
   __shared__ PairInfo pi;
-  __shared__ f32x4_t red[DM_WAVES][64];
+  // wave partials: their own array on four waves; on eight they take the
+  // place of the staged activations once every wave is done with those (the
+  // dynamic LDS is then at least RED8_BYTES), so the workgroup needs no more
+  // LDS than the staged rows and three fit on a CU at NVFP4's 49 KB
+  __shared__ f32x4_t red_s[NW == DM_WAVES ? DM_WAVES : 1][64];
+  extern __shared__ uint4 xs_dyn[];
+  f32x4_t(*red)[64] = (NW == DM_WAVES) ? red_s : reinterpret_cast<f32x4_t(*)[64]>(xs_dyn);
+  const int scr_bytes = (NW == DM_WAVES) ? (int)sizeof(red_s) : DEC_RED8_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
+  const int wl = wv & (DM_WAVES - 1), tsub = wv / DM_WAVES;  // wave within its tile's group, the group
   // out starts at zero: the down kernel adds its two halves into it
-  for (int i = blockIdx.x * DM_THREADS + tid; i < T * H / 4; i += gridDim.x * DM_THREADS)
+  for (int i = blockIdx.x * NTH + tid; i < T * H / 4; i += gridDim.x * NTH)
     reinterpret_cast<float4*>(out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   // workgroup: distinct expert d, 8-row tiles rt0 .. rt0 + ntw - 1 of I
   // (several tiles only where the activations are staged in LDS: elsewhere
@@ -368,7 +384,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
     // one token with renormalised gates: the whole workgroup ranks the
     // experts (its LDS scratch is the reduction buffer, unused until the
     // streaming loop ends); else, or where high halves tie, a wave per token
-    static_assert(sizeof(red) >= 3364, "selection scratch");
+    static_assert(sizeof(red_s) >= 3364, "selection scratch");
     ranked = (T == 1 && route.renormalize) &&
              topk_wg_one_token<RPER, DM_THREADS>(route.logits, route.sel_bias, E, k, s_ids, s_gates,
                                                  reinterpret_cast<unsigned char*>(&red[0][0]));
@@ -378,7 +394,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
                              E, k, route.renormalize, s_ids + t * k, s_gates + t * k);
     __syncthreads();
     if (blockIdx.x == 0)
-      for (int q = tid; q < P; q += DM_THREADS) {
+      for (int q = tid; q < P; q += NTH) {
         route.ids_out[q] = s_ids[q];
         route.gates_out[q] = s_gates[q];
       }
@@ -399,7 +415,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
       pi.tok[0] = 0;
     }
   } else if (wv == 0) {
-    dm_group_pairs(ids, mask, P, k, E, d, &pi, reinterpret_cast<int*>(&red[0][0]), (int)(sizeof(red) / sizeof(int)));
+    dm_group_pairs(ids, mask, P, k, E, d, &pi, reinterpret_cast<int*>(&red[0][0]), scr_bytes / (int)sizeof(int));
   }
   // the down kernel's grouping, built here beside wave 0's so that the down
   // kernel starts its weight loads after one table copy instead of a
@@ -426,22 +442,24 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
   constexpr int CK = Chunk<WD>::K, NM = Chunk<WD>::NM;
   const int nchunk = H / CK;
 
-  extern __shared__ uint4 xs_dyn[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(xs_dyn);
   const int XS = H + 8;  // LDS row stride of the staged activations (elements)
   // chunk of pass c0, step u: strided over the waves, or (GRP) a contiguous
   // quarter per wave taken four chunks at a time
   const int cpw = nchunk / DM_WAVES;
-  const int cbeg = GRP ? wv * cpw : wv, cend = GRP ? cbeg + cpw : nchunk;
+  const int cbeg = GRP ? wl * cpw : wv, cend = GRP ? cbeg + cpw : nchunk;
   const int cstep = GRP ? UNROLL : DM_WAVES * UNROLL, ustep = GRP ? 1 : DM_WAVES;
   bool staged = false;  // activation rows of the expert's distinct tokens (at most 16) in LDS, once
   for (int tg = 0; tg < np; tg += 16) {
     const bool tok_ok = tg + col < np;
     const int t = tok_ok ? pi.pair[tg + col] / k : 0;
     const int xrow = tok_ok ? pi.rank[tg + col] : 0;  // LDS row of this column's token
-    const float gate = (tok_ok && wv == 0) ? gates[pi.pair[tg + col]] : 0.f;  // issued before the stream
+    const float gate = (tok_ok && wl == 0) ? gates[pi.pair[tg + col]] : 0.f;  // issued before the stream
     const uint16_t* xr = x + (int64_t)t * H;
-    for (int rt = rt0; rt < rt0 + ntw; ++rt) {  // this workgroup's tiles, activations staged once
+    // this workgroup's tiles, activations staged once: one after the other,
+    // or (eight waves) tile rt0 + tsub on this wave's group
+    const int rt_beg = (NW == DM_WAVES) ? rt0 : rt0 + tsub, rt_end = (NW == DM_WAVES) ? rt0 + ntw : rt_beg + 1;
+    for (int rt = rt_beg; rt < rt_end; ++rt) {
       const int row = row0 + 8 * (rt - rt0);
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (!XL && !GRP) {
@@ -519,7 +537,7 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
           } else {
             if (c0 == cbeg) {
               if (!staged) {  // after the first pass's weight loads are issued: the two latencies overlap
-                for (int q = tid; q < pi.ntok * (H / 8); q += DM_THREADS) {
+                for (int q = tid; q < pi.ntok * (H / 8); q += NTH) {
                   const int r = q / (H / 8), c8 = q % (H / 8);
                   *reinterpret_cast<uint4*>(xs + r * XS + 8 * c8) =
                       *reinterpret_cast<const uint4*>(x + (int64_t)pi.tok[r] * H + 8 * c8);
@@ -546,17 +564,19 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
           c0 += cstep;
         } while (c0 < cend);
       }
+      if constexpr (NW != DM_WAVES) __syncthreads();  // every wave is done with the staged rows
       red[wv][lane] = acc;
       __syncthreads();
-      if (wv == 0) {
-        f32x4_t s = red[0][lane];
+      const int w0 = tsub * DM_WAVES;  // first wave of this tile's group
+      if (wl == 0) {
+        f32x4_t s = red[w0][lane];
   #pragma unroll
-        for (int w = 1; w < DM_WAVES; ++w) s += red[w][lane];
-        red[0][lane] = s;  // lanes 32-63 (tile rows 8-15) hold the up rows of lanes 0-31
+        for (int w = 1; w < DM_WAVES; ++w) s += red[w0 + w][lane];
+        red[w0][lane] = s;  // lanes 32-63 (tile rows 8-15) hold the up rows of lanes 0-31
       }
       __syncthreads();
-      if (wv == 0 && g < 2 && tok_ok) {
-        const f32x4_t sg = red[0][lane], su = red[0][lane + 32];
+      if (wl == 0 && g < 2 && tok_ok) {
+        const f32x4_t sg = red[w0][lane], su = red[w0][lane + 32];
         const int p = pi.pair[tg + col];
         uint16_t hi[4], lo[4];
   #pragma unroll
@@ -573,6 +593,9 @@ __global__ void __launch_bounds__(DM_THREADS) dec_gateup_kernel(
         *reinterpret_cast<uint2*>(hp + I) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
       }
       __syncthreads();
+      // eight waves: the partials overwrote the staged rows, so a further
+      // group of 16 pairs (an expert listed more than 16 times) stages again
+      if constexpr (NW != DM_WAVES) staged = false;
     }
   }
 }
@@ -723,19 +746,35 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
 #define DM_GATEUP(UN, XL_, GRP_, SH)                                                                   \
   do {                                                                                               \
     if (rper == 0)                                                                                   \
-      dec_gateup_kernel<WD, UN, XL_, GRP_, 0><<<grid, DM_THREADS, SH, st>>>(                         \
+      dec_gateup_kernel<WD, UN, XL_, GRP_, 0, DM_WAVES><<<grid, DM_THREADS, SH, st>>>(               \
           xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw, dtab); \
     else if (rper == 1)                                                                              \
-      dec_gateup_kernel<WD, UN, XL_, GRP_, 1><<<grid, DM_THREADS, SH, st>>>(                         \
+      dec_gateup_kernel<WD, UN, XL_, GRP_, 1, DM_WAVES><<<grid, DM_THREADS, SH, st>>>(               \
           xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw, dtab); \
     else                                                                                             \
-      dec_gateup_kernel<WD, UN, XL_, GRP_, 2><<<grid, DM_THREADS, SH, st>>>(                         \
+      dec_gateup_kernel<WD, UN, XL_, GRP_, 2, DM_WAVES><<<grid, DM_THREADS, SH, st>>>(               \
           xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw, dtab); \
   } while (0)
   // staged loop: four chunks per wave and pass (bf16 at H 2048: two passes
   // at 74 VGPRs, six waves per SIMD, measured 0.5-1% faster than one pass of
   // eight at 110 VGPRs, four waves per SIMD)
-  if (xl)
+  // fp4, staged activations, two tiles per workgroup, no in-kernel selection:
+  // the two tiles on eight waves side by side where four-wave workgroups
+  // would leave few waves resident, i.e. where the staged rows cap a CU at
+  // three workgroups (above 40 KB) or the grid gives each of the 256 CUs at
+  // most four.
+  // Measured against four waves, same box: NVFP4 6144/2048/256 at four
+  // tokens 213 -> 199 us per forward (49 KB staged), MXFP4 4096/2048/256 at
+  // one token 33.4 -> 32.9 us (768 workgroups); MXFP4 at four tokens (33 KB,
+  // ~2,700 workgroups) 92.2 us on four waves against 92.7 on eight.
+  const bool eight = WD != FT_BF16 && xl && ntw == 2 && rper == 0 && (xl_bytes > 40 * 1024 || grid <= 4u * 256u);
+  if (eight) {
+    if constexpr (WD != FT_BF16)
+      dec_gateup_kernel<WD, 4, true, true, 0, 2 * DM_WAVES>
+          <<<grid, 2 * DM_THREADS, xl_bytes > (size_t)DEC_RED8_BYTES ? xl_bytes : DEC_RED8_BYTES, st>>>(
+              xb, ids, mask, pl.P, k, pool, d.expert_stride, slot_ids, gates, hbuf, out, pl.T, H, I, E, route, ntw,
+              dtab);
+  } else if (xl)
     DM_GATEUP(4, true, true, xl_bytes);
   else
     DM_GATEUP((WD == FT_BF16) ? 6 : 4, false, false, 0);

@@ -212,6 +212,34 @@ def test_forward_repeated_expert_in_a_token(cfg, T):
     assert err <= tol(cfg), f"max rel err {err:.3g}"
 
 
+def test_forward_expert_listed_more_than_sixteen_times():
+    """An expert listed at 24 of the 32 pairs (NVFP4 6144/2048/256/top-8, four
+    tokens): its gate/up workgroups take the pairs in two groups of at most
+    16 columns, and on the eight-wave staged loop (49 KB of staged rows) the
+    second group stages the activation rows again after the first group's
+    partials overwrote them."""
+    cfg, T = C5, 4
+    print(f"expert listed 24 times {cfg.name} T={T}", flush=True)
+    ld = LayerData(cfg, 2, 5, T)
+    g = np.random.default_rng(91)
+    k = cfg.top_k
+    ids_np = np.stack([g.choice(cfg.n_experts, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids_np[:3, :] = ids_np[0, 0]  # tokens 0-2: one expert at every rank
+    gates_np = g.uniform(0.05, 1.0, size=(T, k)).astype(np.float32)
+    ld.build_pool(ids_np.ravel())
+    out = ld.gpu_forward(dev(ids_np), dev(gates_np)).cpu().numpy()
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = ld.experts_f64(e)
+        return cache[e]
+
+    ref = experts_forward(to_f64(ld.x, cfg.act_dtype), ids_np, gates_np.astype(np.float64), expert)
+    err = max_rel_err(out, ref)
+    assert err <= tol(cfg), f"max rel err {err:.3g}"
+
+
 # ------------------------------------------------------------ slot table --
 def _gpu_table(L, E, S):
     tb = torch.zeros(ftmoe.ft_slot_table_bytes(L, E, S), dtype=torch.uint8, device="cuda")

@@ -451,11 +451,14 @@ def test_forward_general_path_above_decode_pairs(cfg, T):
     run_layer(cfg, 3, 7, T)
 
 
-def test_forward_decode_path_slot_indirection_and_poison():
+@pytest.mark.parametrize("cfg,T", [(C2, 2), (C3, 1), (C5, 4)])
+def test_forward_decode_path_slot_indirection_and_poison(cfg, T):
     """Records placed at arbitrary pool slots through slot_ids; a negative slot
-    (failed lookup) turns that expert's outputs into NaN instead of a fault."""
-    cfg = C2
-    ld = LayerData(cfg, 4, 9, 2)
+    (failed lookup) turns that expert's outputs into NaN instead of a fault.
+    C3 at one token and C5 at four run the fp4 gate/up kernel on eight waves
+    (two tiles side by side), C2 on four."""
+    print(f"slot indirection and poison {cfg.name} T={T}", flush=True)
+    ld = LayerData(cfg, 4, 9, T)
     ids, gates, o_ids = check_route(ld)
     uniq = sorted(set(o_ids.ravel().tolist()))
     slot_of = {e: 3 + 2 * i for i, e in enumerate(uniq)}

@@ -95,8 +95,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--single-batch", action="store_true",
-                    help="bf16 decode at batch 1 only: skip the batch-2 and batch-4 figures and the 8,192-token "
-                         "prefill figures the default line also reports")
+                    help="bf16 decode at batch 1 only: skip the batch-2 and batch-4 figures, the 8,192-token "
+                         "prefill figures and the NVFP4 decode figures the default line also reports")
     ap.add_argument("--workload", default="decode_bf16_h2048_e128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -491,13 +491,16 @@ def main():
                       "forward_us": round(meas[bq]["fwd_us"], 2), "forward_bytes": round(meas[bq]["fwd_bytes"]),
                       "forward_hbm_frac": round(meas[bq]["achieved_gbs"] / HBM_PEAK_GBS, 4),
                       "distinct_experts_per_call": round(meas[bq]["distinct"], 2)} for bq in batches[1:]}
-    if not args.single_batch:  # the metric's prefill half: one 8,192-token chunk, experts resident
+    if not args.single_batch:  # the metric's prefill half (8,192-token chunks, experts resident), NVFP4 decode
         del pools
         torch.cuda.empty_cache()
         res["prefill"] = prefill_figures(torch)
         from sparse_moe_expert_softmax_amd.configs import C6, C7
         res["prefill_bf16"] = bf16_prefill_figures(torch, C6)
         res["prefill_nvfp4"] = bf16_prefill_figures(torch, C7)
+        torch.cuda.empty_cache()
+        res["decode_nvfp4"] = decode_nvfp4_figures(torch)
+        torch.cuda.empty_cache()
         res["ceilings"] = ceilings(torch)
         # the same forward rate against the streaming read this chip sustained in this run
         rd = res["ceilings"]["stream_read_gbs"]
@@ -830,6 +833,25 @@ def run_decode_resident_fp4(args, cfg, torch):
     """NVFP4-like decode, layers resident, batch 4, with the partition masks:
     every layer call also runs the forward on a random half of the experts and
     on the other half, and the two partial outputs must sum to the full one."""
+    print(json.dumps(decode_resident_fp4(args, cfg, torch)), flush=True)
+
+
+def decode_nvfp4_figures(torch):
+    """The NVFP4 decode workload for the default line: 8 resident layers of the
+    753B-like layer (6,144 / 2,048 / 256 experts / top-8) at 4 tokens, 30
+    timed eager steps after 5, partition masks checked on the last step."""
+    from sparse_moe_expert_softmax_amd.configs import C5
+    a = argparse.Namespace(layers=8, batch=4, steps=30, warmup=5)
+    r = decode_resident_fp4(a, C5, torch)
+    rf = r["roofline"]
+    return {"workload": C5.name, "batch": r["config"]["batch"], "layers": r["config"]["layers"],
+            "launch": "eager", "tokens_per_s": r["value"], "ms_per_step": r["ms_per_step"],
+            "forward_us": rf["avg_launch_us"], "forward_bytes": rf["bytes_per_launch"], "forward_hbm_frac": rf["frac"],
+            "distinct_experts_per_call": rf["distinct_experts_per_call"],
+            "partition_max_rel_err_sum_vs_full": r["partition_masks"]["max_rel_err_sum_vs_full"]}
+
+
+def decode_resident_fp4(args, cfg, torch):
     from sparse_moe_expert_softmax_amd import ftmoe, synth
     L = args.layers or cfg.n_layers
     B = cfg.batches[0] if args.batch == 1 else args.batch
@@ -908,7 +930,7 @@ def run_decode_resident_fp4(args, cfg, torch):
                        "bytes_per_launch": round(float(np.mean(fwd_bytes))),
                        "avg_launch_us": round(float(np.mean(fwd_ms)) * 1e3, 2),
                        "distinct_experts_per_call": round(float(np.mean(distinct)), 2)}
-    print(json.dumps(res), flush=True)
+    return res
 
 
 def run_decode_lru(args, cfg, torch):

@@ -411,6 +411,7 @@ def _measure_decode_bf16(args, cfg, torch, B, pools, routers, desc, calibrate):
 
     return {"ms_per_step": ms_per_step, "layer_tok_s": layer_tok_s, "graphs": len(graphs), "step_bytes": step_bytes,
             "achieved_gbs": achieved_gbs, "fwd_bytes": float(np.mean(fwd_bytes)), "fwd_us": float(np.mean(fwd_ms)) * 1e3,
+            "fwd_us_p10_p50_p90": [round(float(v) * 1e3, 2) for v in np.percentile(fwd_ms, [10, 50, 90])],
             "distinct": float(np.mean(d_meas))}
 
 
@@ -483,12 +484,14 @@ def main():
                      "frac": round(m["achieved_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": measured_decode_traffic(cfg.name, B),
                      "bytes_per_launch": round(m["fwd_bytes"]), "avg_launch_us": round(m["fwd_us"], 2),
+                     "launch_us_p10_p50_p90": m["fwd_us_p10_p50_p90"],
                      "distinct_experts_per_call": round(m["distinct"], 2)},
     }
     if len(batches) > 1:  # the metric's other decode batch sizes, same layers, same process
         res["other_batches"] = {
             str(bq): {"tokens_per_s": round(meas[bq]["layer_tok_s"], 1), "ms_per_step": round(meas[bq]["ms_per_step"], 5),
-                      "forward_us": round(meas[bq]["fwd_us"], 2), "forward_bytes": round(meas[bq]["fwd_bytes"]),
+                      "forward_us": round(meas[bq]["fwd_us"], 2), "forward_us_p10_p50_p90": meas[bq]["fwd_us_p10_p50_p90"],
+                      "forward_bytes": round(meas[bq]["fwd_bytes"]),
                       "forward_hbm_frac": round(meas[bq]["achieved_gbs"] / HBM_PEAK_GBS, 4),
                       "distinct_experts_per_call": round(meas[bq]["distinct"], 2)} for bq in batches[1:]}
     if not args.single_batch:  # the metric's prefill half (8,192-token chunks, experts resident), NVFP4 decode

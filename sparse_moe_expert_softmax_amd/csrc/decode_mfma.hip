@@ -605,7 +605,15 @@ __global__ void __launch_bounds__(NW * 64) dec_gateup_kernel(
 // 0 .. T-1 and its lo terms in columns T .. 2T-1, so one product per K slice
 // covers both (and every h load fills twice the lanes); the two column
 // groups are added once at the end.  Otherwise hi and lo take a product each.
-template <int WD, int UNROLL, bool PACK>
+// MI > 1 (packed columns; every workgroup holds at most MI items, all of
+// one half, so they share their jobs' experts, chunks and h): a wave takes
+// job (expert, chunk) for all of the workgroup's items at once, loading h
+// once for them and the weight rows of each item's tile, with an
+// accumulator per item.  The items then run side by side instead of one
+// after the other, and h, which costs a job 16 VGPRs against the weights'
+// 5, is loaded once per MI jobs.  Each accumulator adds the same jobs in
+// the same order as the item loop below, so the results are the same.
+template <int WD, int UNROLL, bool PACK, int MI>
 __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
     const uint16_t* __restrict__ hbuf, const DownInfo* __restrict__ dtab, const void* __restrict__ pool,
     int64_t stride, float* __restrict__ out, int T, int H, int I) {
@@ -621,6 +629,94 @@ __global__ void __launch_bounds__(DD_THREADS) dec_down_kernel(
   constexpr int CK = Chunk<WD>::K, NM = Chunk<WD>::NM;
   const int nchunk = I / CK;
   const RecordLayout L = record_layout(H, I, WD);
+  if constexpr (MI > 1) {
+    static_assert(PACK, "items side by side: packed columns");
+    const int n_items = (H / 16) * 2;
+    const int half = blockIdx.x & 1;  // the grid is even: every item of this workgroup has this half
+    const int ndh = (nd - half + 1) / 2;
+    const int njobs = ndh * nchunk;
+    bool ok[MI];
+    int rowi[MI];
+  #pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int item = (int)blockIdx.x + i * (int)gridDim.x;
+      ok[i] = item < n_items;
+      rowi[i] = (item >> 1) * 16 + col;
+    }
+    const bool lo = col >= T, cok = col < 2 * T;
+    const int tk = lo ? col - T : col;
+    f32x4_t acc[MI];
+  #pragma unroll
+    for (int i = 0; i < MI; ++i) acc[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    bool poisoned = false;
+    for (int j0 = wv; j0 < njobs; j0 += DD_WAVES * UNROLL) {
+      RawW<WD> rw[UNROLL][MI];
+      uint4 bh[UNROLL][NM];
+      float ts[UNROLL];
+  #pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int job = j0 + u * DD_WAVES;
+        ts[u] = 0.f;
+        if (job < njobs) {
+          const int d = half + 2 * (job / nchunk), c = job % nchunk;
+          const int slot = di.slot[d];
+          const int p = cok ? di.pair[d][tk] : -1;
+          if (slot < 0) {
+            poisoned = true;
+          } else {
+            const uint8_t* rec = reinterpret_cast<const uint8_t*>(pool) + (int64_t)slot * stride;
+            const WMat Dm = wmat<WD>(rec, L, 2, I);
+            ts[u] = Dm.tscale;
+  #pragma unroll
+            for (int i = 0; i < MI; ++i)
+              if (ok[i]) load_raw<WD>(Dm, rowi[i], c, g, rw[u][i]);
+          }
+          const uint16_t* hh = hbuf + (int64_t)(p < 0 ? 0 : p) * 2 * I + (lo ? I : 0);
+  #pragma unroll
+          for (int jj = 0; jj < NM; ++jj)
+            bh[u][jj] = p >= 0 ? *reinterpret_cast<const uint4*>(hh + kofs<WD>(c, jj, g)) : make_uint4(0, 0, 0, 0);
+        }
+      }
+  #pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        if (ts[u] != 0.f) {
+  #pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            if (!ok[i]) continue;
+            f32x4_t part = {0.f, 0.f, 0.f, 0.f};
+            const ChunkScale cs = chunk_scale<WD>(rw[u][i]);
+  #pragma unroll
+            for (int jj = 0; jj < NM; ++jj) part = mfma(decode_a<WD>(rw[u][i], jj, cs), as_bf16x8(bh[u][jj]), part);
+            if constexpr (WD == FT_NVFP4) acc[i] += part * ts[u];
+            else acc[i] += part;
+          }
+        }
+      }
+    }
+  #pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      if (!ok[i]) break;
+      red[wv][lane] = poisoned ? acc[i] * __builtin_nanf("") : acc[i];
+      __syncthreads();
+      if (wv == 0) {
+        f32x4_t s = red[0][lane];
+  #pragma unroll
+        for (int w = 1; w < DD_WAVES; ++w) s += red[w][lane];
+        const int src = (lane & ~15) | ((col + T) & 15);  // the lo column of this token
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) s[q] += __shfl(s[q], src, 64);
+        if (col < T) {
+          // exactly two addends land on each zeroed output element (one per
+          // half), and (0 + a) + b == (0 + b) + a: the sum is deterministic
+          float* o = out + (int64_t)col * H + (rowi[i] - col) + 4 * g;
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) unsafeAtomicAdd(o + q, s[q]);
+        }
+      }
+      __syncthreads();  // red is reused by the next item
+    }
+    return;
+  }
   // work items: (16-row tile rt, half) with half s taking the distinct experts
   // d = s, s+2, ...; a workgroup takes items blockIdx.x, + gridDim.x, ... (the
   // grid is capped, so the grouping above is done once per workgroup)
@@ -789,10 +885,19 @@ static hipError_t dec_forward_t(const ft_moe_desc& d, const DecPlan& pl, const v
   // 4096/2048/256 at one token, NVFP4 6144/2048/256 at four); two for fp4
   // without the packed h columns (its separate lo loads spill at three)
   constexpr int DU = 3, DUL = (WD == FT_BF16) ? 3 : 2;
-  if (pl.T <= 8)
-    dec_down_kernel<WD, DU, true><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H, I);
+#ifndef FT_DD_MI
+#define FT_DD_MI 1
+#endif
+  const int itw = ((H / 16) * 2 + (int)dgrid - 1) / (int)dgrid;  // items per workgroup
+  if (FT_DD_MI && pl.T <= 8 && itw == 2)
+    dec_down_kernel<WD, 3, true, 2><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H, I);
+  else if (FT_DD_MI && pl.T <= 8 && itw == 3)
+    dec_down_kernel<WD, 2, true, 3><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H, I);
+  else if (pl.T <= 8)
+    dec_down_kernel<WD, DU, true, 1><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H, I);
   else
-    dec_down_kernel<WD, DUL, false><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H, I);
+    dec_down_kernel<WD, DUL, false, 1><<<dgrid, DD_THREADS, 0, st>>>(hbuf, dtab, pool, d.expert_stride, out, pl.T, H,
+                                                                    I);
   return hipGetLastError();
 }
 

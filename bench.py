@@ -41,7 +41,7 @@ _CSRC = os.path.join(ROOT, "sparse_moe_expert_softmax_amd", "csrc")
 _HEADERS = [os.path.join(_CSRC, "common.hpp"), os.path.join(_CSRC, "internal.hpp"),
             os.path.join(ROOT, "include", "ft_moe.h")]
 DECODE_SRCS = [os.path.join(_CSRC, f) for f in ("decode_mfma.hip", "topk.hpp")] + _HEADERS
-DECODE_TRAFFIC = {"e96fedf5497ac298": 75947099}
+DECODE_TRAFFIC = {"fb941ebdb53fa6d6": 75968138}
 # The same for the prefill workloads (8,192-token chunks: MXFP4 H4096 E256
 # top-6 in either activation mode, bf16 H2048 E128 top-8, NVFP4 H6144 E256
 # top-8): every kernel of one ft_moe_forward call, keyed by the workload, the

@@ -17,10 +17,12 @@
 //  1. gate/up: grid = (distinct expert d) x (pair of 8-row tiles of I).
 //     Each workgroup derives the expert grouping of the <= 64 (token, rank)
 //     pairs itself (no separate permutation launch), and per tile splits K
-//     over its 4 waves, sums the wave partials in LDS in a fixed order,
-//     applies SwiGLU and stores g * h (gate of the pair folded in).
+//     over 4 waves (the two tiles in turn, or side by side on 8 waves),
+//     sums the wave partials in LDS in a fixed order, applies SwiGLU and
+//     stores g * h (gate of the pair folded in).
 //  2. down + combine: work items = 16-row tiles of H x 2 halves of the
-//     expert list, at most one workgroup per CU looping over its items.
+//     expert list, at most one workgroup per CU; a workgroup's items
+//     (several at hidden sizes above 2048) run side by side, sharing h.
 //     The gate is folded into h (h' = g_tj * h_tj), so the part of
 //     out[t] = sum over routed experts of D_e h'_t that one workgroup owns is
 //     one accumulation: every (expert, K chunk) job of the tile adds into the

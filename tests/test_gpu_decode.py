@@ -444,6 +444,29 @@ def test_fetch_copies_the_lookups_misses_on_the_device():
     assert ei.value.status == ftmoe.FT_EINVAL
 
 
+# hidden 3072 and 2176: (H / 16) x 2 = 384 and 272 down items on 256
+# workgroups, so some workgroups hold two items side by side and the rest one
+UNEVEN_MX = MoEConfig("decode_mxfp4_h3072_e16", 84, hidden=3072, inter=256, n_experts=16, top_k=4, act_dtype=BF16,
+                      router_dtype=BF16, w_dtype=2, n_layers=1)
+UNEVEN_NV = MoEConfig("decode_nvfp4_h2176_e24", 85, hidden=2176, inter=384, n_experts=24, top_k=6, act_dtype=BF16,
+                      router_dtype=BF16, w_dtype=3, n_layers=1)
+
+
+@pytest.mark.parametrize("cfg,T", [(UNEVEN_MX, 2), (UNEVEN_NV, 3), (UNEVEN_NV, 1)])
+def test_forward_decode_down_items_uneven_over_workgroups(cfg, T):
+    """The down projection runs a workgroup's items side by side; where the
+    item count is not a multiple of the grid, some workgroups hold fewer
+    items than others.  Outputs against the oracle, partition parts summing
+    to the full output."""
+    print(f"uneven down items {cfg.name} T={T}", flush=True)
+    ld, ids, gates, out, ref = run_layer(cfg, 0, 6 + T, T)
+    m = np.array([0x00A5A5A5], dtype=np.uint32)
+    comp = (~m) & np.uint32(0xFFFFFFFF)
+    a = ld.gpu_forward(ids, gates, mask=m).cpu().numpy()
+    b = ld.gpu_forward(ids, gates, mask=comp).cpu().numpy()
+    assert max_rel_err(a + b, out) <= 1e-5
+
+
 @pytest.mark.parametrize("cfg,T", [(C2, 9), (C3, 11)])
 def test_forward_general_path_above_decode_pairs(cfg, T):
     """More than 64 (token, rank) pairs: the permute + grouped GEMV path."""
